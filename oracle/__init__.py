@@ -1,0 +1,197 @@
+"""ctypes front end of the CPU oracle (``qdt_oracle.c``).
+
+TEST INFRASTRUCTURE: imported only by the test suite, the smoke check and the
+benchmark's CPU-baseline leg.  It shares nothing with the HIP path.  Arrays are
+numpy; bf16 tensors travel as uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "qdt_oracle.c")
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-pthread", "-Wall"]
+
+EPI_BIAS, EPI_SILU_GATE, EPI_HEAD_RMSNORM = 0, 1, 2
+_EPI = {"bias": EPI_BIAS, "silu_gate": EPI_SILU_GATE, "head_rmsnorm": EPI_HEAD_RMSNORM}
+
+
+def compile_oracle() -> str:
+    cmd = ["gcc", *CFLAGS, SRC_PATH, "-o", LIB_PATH, "-lm"]
+    subprocess.run(cmd, check=True)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH):
+            compile_oracle()
+        L = C.CDLL(LIB_PATH)
+        P, I64, F, I = C.c_void_p, C.c_int64, C.c_float, C.c_int
+        sig = {
+            "oracle_version": ([], I),
+            "oracle_set_threads": ([I], None),
+            "oracle_threads": ([], I),
+            "oracle_bf16_to_f32": ([C.c_uint16], F),
+            "oracle_f32_to_bf16": ([F], C.c_uint16),
+            "oracle_f32_to_bf16_array": ([P, P, I64], None),
+            "oracle_channel_absmax": ([P, I64, I64, I64, P, I], None),
+            "oracle_smooth_lambda": ([P, P, I64, F, P, P], None),
+            "oracle_quantize_rows": ([P, P, I64, I64, I64, P, P], None),
+            "oracle_smooth_prepare": ([P, P, I64, I64, F, P, P, P, P], None),
+            "oracle_gemm_i32": ([P, P, I64, I64, I64, P], None),
+            "oracle_gemm_i64": ([P, P, I64, I64, I64, P], None),
+            "oracle_epilogue": ([P, I64, I64, P, P, P, I, P, I64, F, P, I64], None),
+            "oracle_linear_rows": ([P, P, P, P, P, P, I64, I64, I64, I, P, I64, F, P, I64, P], None),
+            "oracle_bf16_gemm_rows": ([P, P, P, P, I64, I64, I64, P, P], None),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
+
+
+def threads() -> int:
+    return int(lib().oracle_threads())
+
+
+def f32_to_bf16(x) -> np.ndarray:
+    x = _c(np.atleast_1d(x), np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().oracle_f32_to_bf16_array(_p(x), _p(out), x.size)
+    return out
+
+
+def channel_absmax(X: np.ndarray, s: np.ndarray | None = None) -> np.ndarray:
+    X = _c(X, np.uint16)
+    M, K = X.shape
+    acc = s is not None
+    s = np.zeros(K, np.float32) if s is None else _c(s, np.float32).copy()
+    lib().oracle_channel_absmax(_p(X), M, K, K, _p(s), int(acc))
+    return s
+
+
+def smooth_lambda(s, w, alpha: float = 0.5):
+    s, w = _c(s, np.float32), _c(w, np.float32)
+    lam = np.empty_like(s)
+    inv = np.empty_like(s)
+    lib().oracle_smooth_lambda(_p(s), _p(w), s.size, alpha, _p(lam), _p(inv))
+    return lam, inv
+
+
+def quantize_rows(X: np.ndarray, colmul: np.ndarray | None = None):
+    X = _c(X, np.uint16)
+    M, K = X.shape
+    q = np.empty((M, K), np.int8)
+    sc = np.empty(M, np.float32)
+    lib().oracle_quantize_rows(_p(X), _p(_c(colmul, np.float32)), M, K, K, _p(q), _p(sc))
+    return q, sc
+
+
+def quantize_per_token(X: np.ndarray, inv_lambda: np.ndarray | None):
+    return quantize_rows(X, inv_lambda)
+
+
+def smooth_prepare(W: np.ndarray, s: np.ndarray | None, alpha: float = 0.5):
+    """Returns (Wq int8 [N,K], sw f32 [N], inv_lambda f32 [K], lambda f32 [K])."""
+    W = _c(W, np.uint16)
+    N, K = W.shape
+    Wq = np.empty((N, K), np.int8)
+    sw = np.empty(N, np.float32)
+    inv = np.empty(K, np.float32)
+    lam = np.empty(K, np.float32)
+    lib().oracle_smooth_prepare(_p(W), _p(_c(s, np.float32)), N, K, alpha, _p(Wq), _p(sw), _p(inv), _p(lam))
+    return Wq, sw, inv, lam
+
+
+def gemm_i32(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    A, B = _c(A, np.int8), _c(B, np.int8)
+    M, K = A.shape
+    N = B.shape[0]
+    out = np.empty((M, N), np.int32)
+    lib().oracle_gemm_i32(_p(A), _p(B), M, N, K, _p(out))
+    return out
+
+
+def gemm_i64(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    A, B = _c(A, np.int8), _c(B, np.int8)
+    M, K = A.shape
+    N = B.shape[0]
+    out = np.empty((M, N), np.int64)
+    lib().oracle_gemm_i64(_p(A), _p(B), M, N, K, _p(out))
+    return out
+
+
+def _n_out(N: int, epi: int) -> int:
+    return N // 2 if epi == EPI_SILU_GATE else N
+
+
+def epilogue(acc, sx, sw, bias=None, epi="bias", gamma=None, head_dim=256, eps=1e-6) -> np.ndarray:
+    e = _EPI[epi] if isinstance(epi, str) else int(epi)
+    acc = _c(acc, np.int32)
+    M, N = acc.shape
+    no = _n_out(N, e)
+    Y = np.empty((M, no), np.uint16)
+    lib().oracle_epilogue(_p(acc), M, N, _p(_c(sx, np.float32)), _p(_c(sw, np.float32)), _p(_c(bias, np.uint16)),
+                          e, _p(_c(gamma, np.uint16)), head_dim, eps, _p(Y), no)
+    return Y
+
+
+def linear_rows(Xq, sx, Wq, sw, bias, rows, epi="bias", gamma=None, head_dim=256, eps=1e-6, want_acc=False):
+    """GEMM + epilogue for the given rows; returns Y rows (and int32 acc rows when want_acc)."""
+    e = _EPI[epi] if isinstance(epi, str) else int(epi)
+    Xq, Wq = _c(Xq, np.int8), _c(Wq, np.int8)
+    rows = _c(rows, np.int64)
+    N, K = Wq.shape
+    no = _n_out(N, e)
+    Y = np.empty((rows.size, no), np.uint16)
+    acc = np.empty((rows.size, N), np.int32) if want_acc else None
+    lib().oracle_linear_rows(_p(Xq), _p(_c(sx, np.float32)), _p(Wq), _p(_c(sw, np.float32)),
+                             _p(_c(bias, np.uint16)), _p(rows), rows.size, N, K, e, _p(_c(gamma, np.uint16)),
+                             head_dim, eps, _p(Y), no, _p(acc))
+    return (Y, acc) if want_acc else Y
+
+
+def linear(X, W, bias=None, s=None, alpha=0.5, epi="bias", gamma=None, head_dim=256, eps=1e-6):
+    """The whole path on the CPU: prepare, quantize, GEMM, epilogue.  Returns a dict of stages."""
+    s = channel_absmax(X) if s is None else s
+    Wq, sw, inv, lam = smooth_prepare(W, s, alpha)
+    Xq, sx = quantize_per_token(X, inv)
+    acc = gemm_i32(Xq, Wq)
+    Y = epilogue(acc, sx, sw, bias, epi, gamma, head_dim, eps)
+    return dict(s=s, Wq=Wq, sw=sw, inv_lambda=inv, lam=lam, Xq=Xq, sx=sx, acc=acc, Y=Y)
+
+
+def bf16_gemm_rows(H, W, bias=None, rows=None, want_f32=False):
+    H, W = _c(H, np.uint16), _c(W, np.uint16)
+    M, K = H.shape
+    N = W.shape[0]
+    r = None if rows is None else _c(rows, np.int64)
+    nr = M if r is None else r.size
+    Z = np.empty((nr, N), np.uint16)
+    Zf = np.empty((nr, N), np.float32) if want_f32 else None
+    lib().oracle_bf16_gemm_rows(_p(H), _p(W), _p(_c(bias, np.uint16)), _p(r), nr, N, K, _p(Z), _p(Zf))
+    return (Z, Zf) if want_f32 else Z

@@ -1,0 +1,361 @@
+/*
+ * qdt_oracle.c -- plain, slow, obviously correct CPU oracle of the W8A8 DiT linear.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg load this library.  It shares no code, header, table or helper
+ * with the HIP path; its inputs come from the seeded generator module only.
+ *
+ * Pages followed (titles as published):
+ *   [PTQ]  "Quantizing a Dual-Branch Flow-Matching Diffusion Transformer for Consumer
+ *          GPUs: INT8 and GGUF Post-Training Quantization of Ideogram 4.0" --
+ *          the W8A8 recipe paragraph of its method section (per-output-row INT8
+ *          weights, per-token dynamic INT8 activations, SmoothQuant with alpha = 0.5,
+ *          lambda_j = s_j^alpha / max_i |W_ij|^(1-alpha), activations scaled down and
+ *          weights scaled up before quantization), and its related-work paragraph
+ *          (per-token dynamic activations with per-channel weights).
+ *   [FAL]  "Serving sub-second Ideogram v4 without quality loss" -- the paragraph on
+ *          fused epilogues: each large matmul is followed by a small op (RMSNorm or
+ *          a gated SiLU), and attention heads are 256 wide.
+ *   [ZC]   "Faster Ideogram 4 with Less Prompt Compute" -- section "Most of the Tensor
+ *          Was Zero": the projection has a bias, so a zero row projects to the bias,
+ *          and rows are projected independently.
+ *
+ * Readings where the pages are silent (each is also listed with the design notes):
+ *   - alpha = 0.5 is evaluated as sqrtf(s)/sqrtf(w); lambda = 1 where s or w is 0;
+ *     other alpha use powf(s, alpha) / powf(w, 1 - alpha).
+ *   - the activation side multiplies by inv_lambda = 1/lambda (computed once).
+ *   - symmetric INT8: scale = amax / 127, q = clamp(rint(v / scale), -127, 127), with a
+ *     correctly rounded fp32 division and round-half-to-even; an all-zero row has
+ *     scale 0 and q = 0.
+ *   - BIAS epilogue: y = fmaf((float)acc, sx * sw, bias), then bf16 round-half-even.
+ *   - SILU_GATE: rows [gate(0..F-1); up(F..2F-1)], Y = bf16((g / (1 + expf(-g))) * u).
+ *   - HEAD_RMSNORM: per row and per head of head_dim columns, ss = sum y^2 (fp64 here),
+ *     ms = (float)ss / head_dim, r = 1 / sqrtf(ms + eps), Y = bf16((y * r) * gamma[d]),
+ *     one gamma of head_dim entries shared by all heads.
+ *   - bf16 GEMM (the protected layer kept unquantized): exact products summed in fp64,
+ *     plus bias, rounded to fp32 and then to bf16.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math (no intrinsics, no SIMD pragmas).
+ * Floating point: every fp32 operation is IEEE round-to-nearest-even, as written.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+#define ORACLE_EPI_BIAS 0
+#define ORACLE_EPI_SILU_GATE 1
+#define ORACLE_EPI_HEAD_RMSNORM 2
+
+static int g_threads = 0;
+
+int oracle_version(void) { return 1; }
+
+void oracle_set_threads(int n) { g_threads = n; }
+
+int oracle_threads(void) {
+    if (g_threads > 0) return g_threads;
+    long n = sysconf(_SC_NPROCESSORS_ONLN);
+    return n > 0 ? (int)n : 1;
+}
+
+/* ---------------------------------------------------------------- bf16 <-> fp32 */
+float oracle_bf16_to_f32(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Round-half-to-even of an fp32 value to the 8-bit-mantissa bf16 format. */
+uint16_t oracle_f32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0) /* NaN stays NaN */
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t upper = u >> 16, lower = u & 0xFFFFu;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
+    return (uint16_t)upper;
+}
+
+void oracle_f32_to_bf16_array(const float* in, uint16_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(in[i]);
+}
+
+/* ---------------------------------------------------------------- row-parallel helper */
+typedef void (*row_fn)(void* ctx, int64_t r0, int64_t r1);
+typedef struct { row_fn fn; void* ctx; int64_t r0, r1; } row_job;
+
+static void* row_job_run(void* p) {
+    row_job* j = (row_job*)p;
+    if (j->r1 > j->r0) j->fn(j->ctx, j->r0, j->r1);
+    return NULL;
+}
+
+/* Static partition of rows [0, rows) over the oracle's threads. */
+static void parallel_rows(int64_t rows, row_fn fn, void* ctx) {
+    int nt = oracle_threads();
+    if (nt > rows) nt = (int)(rows > 0 ? rows : 1);
+    if (nt <= 1) { fn(ctx, 0, rows); return; }
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
+    row_job* jobs = (row_job*)malloc(sizeof(row_job) * (size_t)nt);
+    for (int t = 0; t < nt; ++t) {
+        jobs[t].fn = fn; jobs[t].ctx = ctx;
+        jobs[t].r0 = rows * t / nt; jobs[t].r1 = rows * (t + 1) / nt;
+        pthread_create(&th[t], NULL, row_job_run, &jobs[t]);
+    }
+    for (int t = 0; t < nt; ++t) pthread_join(th[t], NULL);
+    free(th); free(jobs);
+}
+
+/* ---------------------------------------------------------------- O1: calibration max-abs */
+/* s_j = max over rows m of |X_mj|  ([PTQ] W8A8 recipe: per-channel activation scale s). */
+void oracle_channel_absmax(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, float* s, int accumulate) {
+    if (!accumulate)
+        for (int64_t j = 0; j < K; ++j) s[j] = 0.0f;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < K; ++j) {
+            float v = fabsf(oracle_bf16_to_f32(X[m * ldx + j]));
+            if (v > s[j]) s[j] = v;
+        }
+}
+
+/* ---------------------------------------------------------------- O2: smoothing vector */
+/* lambda_j = s_j^alpha / w_j^(1-alpha) with w_j = max_i |W_ij|  ([PTQ] W8A8 recipe). */
+void oracle_smooth_lambda(const float* s, const float* w, int64_t K, float alpha, float* lambda,
+                          float* inv_lambda) {
+    for (int64_t j = 0; j < K; ++j) {
+        float l;
+        if (s[j] == 0.0f || w[j] == 0.0f)
+            l = 1.0f;
+        else if (alpha == 0.5f)
+            l = sqrtf(s[j]) / sqrtf(w[j]);
+        else
+            l = powf(s[j], alpha) / powf(w[j], 1.0f - alpha);
+        lambda[j] = l;
+        inv_lambda[j] = 1.0f / l;
+    }
+}
+
+/* ---------------------------------------------------------------- O3/O4: per-row INT8 */
+typedef struct {
+    const uint16_t* X; const float* colmul; int64_t K, ldx; int8_t* q; float* scale;
+} quant_ctx;
+
+static void quant_rows(void* p, int64_t r0, int64_t r1) {
+    quant_ctx* c = (quant_ctx*)p;
+    float* v = (float*)malloc(sizeof(float) * (size_t)c->K);
+    for (int64_t m = r0; m < r1; ++m) {
+        const uint16_t* x = c->X + m * c->ldx;
+        float amax = 0.0f;
+        for (int64_t j = 0; j < c->K; ++j) {
+            float f = oracle_bf16_to_f32(x[j]);
+            v[j] = c->colmul ? f * c->colmul[j] : f;
+            float a = fabsf(v[j]);
+            if (a > amax) amax = a;
+        }
+        int8_t* q = c->q + m * c->K;
+        if (amax == 0.0f) {
+            c->scale[m] = 0.0f;
+            for (int64_t j = 0; j < c->K; ++j) q[j] = 0;
+            continue;
+        }
+        float sc = amax / 127.0f;
+        c->scale[m] = sc;
+        for (int64_t j = 0; j < c->K; ++j) {
+            float t = rintf(v[j] / sc); /* default rounding mode: half to even */
+            if (t > 127.0f) t = 127.0f;
+            if (t < -127.0f) t = -127.0f;
+            q[j] = (int8_t)t;
+        }
+    }
+    free(v);
+}
+
+/* Row m: v = X_m * colmul (elementwise, colmul may be NULL), scale_m = max|v| / 127,
+ * q = clamp(rint(v / scale_m), -127, 127).  Used with colmul = inv_lambda for the
+ * activations (per token) and colmul = lambda for the weights (per output row). */
+void oracle_quantize_rows(const uint16_t* X, const float* colmul, int64_t M, int64_t K, int64_t ldx,
+                          int8_t* q, float* scale) {
+    quant_ctx c = {X, colmul, K, ldx, q, scale};
+    parallel_rows(M, quant_rows, &c);
+}
+
+/* Offline weight preparation: w_j, lambda, inv_lambda, then Wq/sw from W * diag(lambda).
+ * s == NULL means no smoothing (lambda = 1). */
+void oracle_smooth_prepare(const uint16_t* W, const float* s, int64_t N, int64_t K, float alpha,
+                           int8_t* Wq, float* sw, float* inv_lambda, float* lambda) {
+    float* w = (float*)malloc(sizeof(float) * (size_t)K);
+    float* lam = lambda ? lambda : (float*)malloc(sizeof(float) * (size_t)K);
+    float* inv = inv_lambda ? inv_lambda : (float*)malloc(sizeof(float) * (size_t)K);
+    if (s) {
+        oracle_channel_absmax(W, N, K, K, w, 0);
+        oracle_smooth_lambda(s, w, K, alpha, lam, inv);
+    } else {
+        for (int64_t j = 0; j < K; ++j) { lam[j] = 1.0f; inv[j] = 1.0f; }
+    }
+    oracle_quantize_rows(W, s ? lam : NULL, N, K, K, Wq, sw);
+    free(w);
+    if (!lambda) free(lam);
+    if (!inv_lambda) free(inv);
+}
+
+/* ---------------------------------------------------------------- O5: integer GEMM */
+typedef struct {
+    const int8_t* A; const int8_t* B; int64_t N, K; int32_t* C32; int64_t* C64;
+} gemm_ctx;
+
+static void gemm_rows(void* p, int64_t r0, int64_t r1) {
+    gemm_ctx* c = (gemm_ctx*)p;
+    for (int64_t m = r0; m < r1; ++m) {
+        const int8_t* a = c->A + m * c->K;
+        for (int64_t n = 0; n < c->N; ++n) {
+            const int8_t* b = c->B + n * c->K;
+            if (c->C32) {
+                uint32_t acc = 0; /* int32 two's-complement accumulation without UB */
+                for (int64_t k = 0; k < c->K; ++k) acc += (uint32_t)((int32_t)a[k] * (int32_t)b[k]);
+                c->C32[m * c->N + n] = (int32_t)acc;
+            } else {
+                int64_t acc = 0;
+                for (int64_t k = 0; k < c->K; ++k) acc += (int64_t)a[k] * (int64_t)b[k];
+                c->C64[m * c->N + n] = acc;
+            }
+        }
+    }
+}
+
+/* C[m][n] = sum_k A[m][k] * B[n][k]: activations [M,K] times weights [N,K] transposed. */
+void oracle_gemm_i32(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, int32_t* C) {
+    gemm_ctx c = {A, B, N, K, C, NULL};
+    parallel_rows(M, gemm_rows, &c);
+}
+
+void oracle_gemm_i64(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, int64_t* C) {
+    gemm_ctx c = {A, B, N, K, NULL, C};
+    parallel_rows(M, gemm_rows, &c);
+}
+
+/* ---------------------------------------------------------------- O6: epilogues */
+static float dequant_bias(int32_t acc, float sx, float sw, const uint16_t* bias, int64_t n) {
+    float b = bias ? oracle_bf16_to_f32(bias[n]) : 0.0f;
+    float d = sx * sw;
+    return fmaf((float)acc, d, b);
+}
+
+/* One output row.  acc: [N] (N = 2F for SILU_GATE), Y: [N_out]. */
+static void epilogue_row(const int32_t* acc, int64_t N, float sx, const float* sw, const uint16_t* bias,
+                         int epi, const uint16_t* gamma, int64_t head_dim, float eps, uint16_t* Y,
+                         float* ybuf) {
+    if (epi == ORACLE_EPI_BIAS) {
+        for (int64_t n = 0; n < N; ++n) Y[n] = oracle_f32_to_bf16(dequant_bias(acc[n], sx, sw[n], bias, n));
+    } else if (epi == ORACLE_EPI_SILU_GATE) {
+        int64_t F = N / 2;
+        for (int64_t f = 0; f < F; ++f) {
+            float g = dequant_bias(acc[f], sx, sw[f], bias, f);
+            float u = dequant_bias(acc[F + f], sx, sw[F + f], bias, F + f);
+            float silu = g / (1.0f + expf(-g));
+            Y[f] = oracle_f32_to_bf16(silu * u);
+        }
+    } else { /* ORACLE_EPI_HEAD_RMSNORM */
+        for (int64_t n = 0; n < N; ++n) ybuf[n] = dequant_bias(acc[n], sx, sw[n], bias, n);
+        for (int64_t h0 = 0; h0 < N; h0 += head_dim) {
+            double ss = 0.0;
+            for (int64_t d = 0; d < head_dim; ++d) ss += (double)ybuf[h0 + d] * (double)ybuf[h0 + d];
+            float ms = (float)ss / (float)head_dim;
+            float r = 1.0f / sqrtf(ms + eps);
+            for (int64_t d = 0; d < head_dim; ++d) {
+                float g = oracle_bf16_to_f32(gamma[d]);
+                Y[h0 + d] = oracle_f32_to_bf16((ybuf[h0 + d] * r) * g);
+            }
+        }
+    }
+}
+
+typedef struct {
+    const int32_t* acc; int64_t N; const float* sx; const float* sw; const uint16_t* bias; int epi;
+    const uint16_t* gamma; int64_t head_dim; float eps; uint16_t* Y; int64_t ldy;
+} epi_ctx;
+
+static void epi_rows(void* p, int64_t r0, int64_t r1) {
+    epi_ctx* c = (epi_ctx*)p;
+    float* ybuf = (float*)malloc(sizeof(float) * (size_t)c->N);
+    for (int64_t m = r0; m < r1; ++m)
+        epilogue_row(c->acc + m * c->N, c->N, c->sx[m], c->sw, c->bias, c->epi, c->gamma, c->head_dim, c->eps,
+                     c->Y + m * c->ldy, ybuf);
+    free(ybuf);
+}
+
+/* Y[m][:] = epilogue(acc[m][:]) for all M rows; acc is [M, N] int32 row-major. */
+void oracle_epilogue(const int32_t* acc, int64_t M, int64_t N, const float* sx, const float* sw,
+                     const uint16_t* bias, int epi, const uint16_t* gamma, int64_t head_dim, float eps,
+                     uint16_t* Y, int64_t ldy) {
+    epi_ctx c = {acc, N, sx, sw, bias, epi, gamma, head_dim, eps, Y, ldy};
+    parallel_rows(M, epi_rows, &c);
+}
+
+/* ---------------------------------------------------------------- sampled rows */
+typedef struct {
+    const int8_t* Xq; const float* sx; const int8_t* Wq; const float* sw; const uint16_t* bias;
+    const int64_t* rows; int64_t N, K; int epi; const uint16_t* gamma; int64_t head_dim; float eps;
+    uint16_t* Y; int64_t ldy; int32_t* acc_out;
+} rows_ctx;
+
+static void linear_rows_run(void* p, int64_t i0, int64_t i1) {
+    rows_ctx* c = (rows_ctx*)p;
+    int32_t* acc = (int32_t*)malloc(sizeof(int32_t) * (size_t)c->N);
+    float* ybuf = (float*)malloc(sizeof(float) * (size_t)c->N);
+    for (int64_t i = i0; i < i1; ++i) {
+        int64_t m = c->rows[i];
+        gemm_ctx g = {c->Xq + m * c->K, c->Wq, c->N, c->K, acc, NULL};
+        gemm_rows(&g, 0, 1);
+        if (c->acc_out) memcpy(c->acc_out + i * c->N, acc, sizeof(int32_t) * (size_t)c->N);
+        if (c->Y)
+            epilogue_row(acc, c->N, c->sx[m], c->sw, c->bias, c->epi, c->gamma, c->head_dim, c->eps,
+                         c->Y + i * c->ldy, ybuf);
+    }
+    free(acc); free(ybuf);
+}
+
+/* GEMM + epilogue for the listed rows only (rows are independent): output row i of
+ * Y / acc_out belongs to input row rows[i].  Y or acc_out may be NULL. */
+void oracle_linear_rows(const int8_t* Xq, const float* sx, const int8_t* Wq, const float* sw,
+                        const uint16_t* bias, const int64_t* rows, int64_t nrows, int64_t N, int64_t K, int epi,
+                        const uint16_t* gamma, int64_t head_dim, float eps, uint16_t* Y, int64_t ldy,
+                        int32_t* acc_out) {
+    rows_ctx c = {Xq, sx, Wq, sw, bias, rows, N, K, epi, gamma, head_dim, eps, Y, ldy, acc_out};
+    parallel_rows(nrows, linear_rows_run, &c);
+}
+
+/* ---------------------------------------------------------------- O7: bf16 GEMM */
+typedef struct {
+    const uint16_t* H; const uint16_t* W; const uint16_t* bias; const int64_t* rows; int64_t N, K;
+    uint16_t* Z; float* Zf;
+} bgemm_ctx;
+
+static void bgemm_rows(void* p, int64_t i0, int64_t i1) {
+    bgemm_ctx* c = (bgemm_ctx*)p;
+    for (int64_t i = i0; i < i1; ++i) {
+        int64_t m = c->rows ? c->rows[i] : i;
+        const uint16_t* h = c->H + m * c->K;
+        for (int64_t n = 0; n < c->N; ++n) {
+            const uint16_t* w = c->W + n * c->K;
+            double acc = 0.0; /* bf16 x bf16 products are exact in fp64 */
+            for (int64_t k = 0; k < c->K; ++k)
+                acc += (double)oracle_bf16_to_f32(h[k]) * (double)oracle_bf16_to_f32(w[k]);
+            if (c->bias) acc += (double)oracle_bf16_to_f32(c->bias[n]);
+            float f = (float)acc;
+            if (c->Zf) c->Zf[i * c->N + n] = f;
+            c->Z[i * c->N + n] = oracle_f32_to_bf16(f);
+        }
+    }
+}
+
+/* Z = H * W^T (+ bias): H [M,K], W [N,K] bf16; Z [nrows, N] bf16 and optional fp32 Zf.
+ * rows == NULL computes every row (nrows = M). */
+void oracle_bf16_gemm_rows(const uint16_t* H, const uint16_t* W, const uint16_t* bias, const int64_t* rows,
+                           int64_t nrows, int64_t N, int64_t K, uint16_t* Z, float* Zf) {
+    bgemm_ctx c = {H, W, bias, rows, N, K, Z, Zf};
+    parallel_rows(nrows, bgemm_rows, &c);
+}

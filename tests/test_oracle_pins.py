@@ -1,0 +1,408 @@
+"""Pins of the CPU oracle against facts other than itself (no GPU).
+
+Each test checks the oracle against a closed form, an invariant of the method, a
+special case that reduces to a library routine, brute force on tiny inputs, or a
+number printed on the pages -- chosen so that a plausible mistake (a dropped term,
+a wrong sign or index, a transposed operand, a wrong rounding rule) fails one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import qdt_workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf(x):
+    return W.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def f32(b):
+    return W.bf16_bits_to_f32(b)
+
+
+def ulp_dist_bf16(a, b):
+    """Distance in bf16 ulps between bit patterns, via the order-preserving integer map."""
+    def key(u):
+        u = np.asarray(u, np.int32)
+        return np.where(u & 0x8000, 0x8000 - (u & 0x7FFF), 0x8000 + (u & 0x7FFF))
+    return np.abs(key(a) - key(b))
+
+
+# ----------------------------------------------------------------------------- bf16 rounding
+def test_bf16_round_half_even_ties():
+    one = 1.0
+    cases = {
+        one + 2.0 ** -8: one,                          # tie, even neighbour is 1.0
+        one + 2.0 ** -7 + 2.0 ** -8: one + 2.0 ** -6,  # tie, odd below -> rounds up to even
+        one + 2.0 ** -8 + 2.0 ** -20: one + 2.0 ** -7,  # just above the tie
+        -(one + 2.0 ** -8): -one,
+        3.0 * 2.0 ** -132: 3.0 * 2.0 ** -132,          # bf16 subnormal (multiple of 2^-133), exact
+        2.0 ** -135: 0.0,                              # below half the smallest bf16 subnormal
+    }
+    for x, want in cases.items():
+        got = f32(oracle.f32_to_bf16(np.float32(x)))[0]
+        assert got == np.float32(want), (x, got, want)
+
+
+def test_bf16_rounding_matches_torch_cpu():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10.0 ** rng.integers(-30, 30, 100000),
+                        (rng.integers(0, 2 ** 32, 100000, dtype=np.uint64).astype(np.uint32)
+                         & np.uint32(0x7F7FFFFF)).view(np.float32)])
+    ours = oracle.f32_to_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+# ----------------------------------------------------------------------------- integer GEMM
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (3, 5, 64), (7, 2, 128), (8, 8, 256), (17, 33, 320)])
+def test_gemm_equals_int64_matmul(M, N, K):
+    rng = np.random.default_rng(M * 1000 + N * 10 + K)
+    A = rng.integers(-127, 128, (M, K), dtype=np.int64).astype(np.int8)
+    B = rng.integers(-127, 128, (N, K), dtype=np.int64).astype(np.int8)
+    A[0, :] = 127
+    B[-1, :] = -127
+    ref = A.astype(np.int64) @ B.astype(np.int64).T
+    assert np.array_equal(oracle.gemm_i64(A, B), ref)
+    assert np.array_equal(oracle.gemm_i32(A, B).astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("K", [4608, 53248])
+def test_gemm_int32_extremes_no_overflow(K):
+    # |acc| <= 127^2 K stays below 2^31 up to K = 133144; the extreme is reached here
+    A = np.full((2, K), 127, np.int8)
+    A[1] = -127
+    B = np.full((3, K), 127, np.int8)
+    B[2, ::2] = -127
+    c32 = oracle.gemm_i32(A, B)
+    c64 = oracle.gemm_i64(A, B)
+    assert np.array_equal(c32.astype(np.int64), c64)
+    assert c64[0, 0] == 127 * 127 * K and c64[1, 0] == -127 * 127 * K
+    assert c64[0, 2] == 0
+
+
+# ----------------------------------------------------------------------------- quantization
+def test_quantize_round_half_even_on_exact_scale():
+    # with no smoothing and a row maximum of 127 (exact in bf16) the scale is exactly 1.0,
+    # so v / scale = v and the ties expose the rounding rule
+    row = np.array([127.0, 2.5, 3.5, -2.5, -3.5, 0.5, 1.5, 126.5, -0.5, 0.25, -1.5, 5.5] + [0.0] * 52, np.float32)
+    q, s = oracle.quantize_rows(bf(row[None, :]))
+    assert s[0] == np.float32(1.0)
+    want = [127, 2, 4, -2, -4, 0, 2, 126, 0, 0, -2, 6]
+    assert q[0, :12].tolist() == want
+
+
+def _quant_bounds(X, colmul, q, s):
+    x = f32(X).astype(np.float32)
+    v = (x * colmul[None, :]).astype(np.float32) if colmul is not None else x
+    v64 = v.astype(np.float64)
+    amax = np.abs(v64).max(axis=1)
+    nz = amax > 0
+    # zero rows: zero scale and codes
+    assert np.all(s[~nz] == 0) and np.all(q[~nz] == 0)
+    # scale is amax/127 to within one fp32 rounding
+    assert np.all(np.abs(s[nz].astype(np.float64) * 127.0 - amax[nz]) <= amax[nz] * 2.0 ** -23)
+    # every nonzero row uses the full symmetric range, never -128
+    assert np.all(np.abs(q[nz].astype(np.int32)).max(axis=1) == 127)
+    assert q.min() >= -127
+    # reconstruction error of round-to-nearest: |v - q s| <= s/2 (1 + 2^-15)
+    err = np.abs(v64 - q.astype(np.float64) * s[:, None].astype(np.float64))
+    assert np.all(err <= s[:, None].astype(np.float64) * 0.5 * (1.0 + 2.0 ** -15))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_quantize_brute_force_tiny(seed):
+    rng = np.random.default_rng(seed)
+    M = int(rng.integers(1, 9))
+    K = int(rng.choice([64, 128, 256]))
+    X = bf(rng.standard_normal((M, K)).astype(np.float32) * np.float32(10.0 ** rng.uniform(-3, 3)))
+    X[rng.integers(0, M)] = 0  # one all-zero row
+    colmul = (2.0 ** rng.uniform(-4, 4, K)).astype(np.float32)
+    for cm in (None, colmul):
+        q, s = oracle.quantize_rows(X, cm)
+        _quant_bounds(X, cm, q, s)
+        # every code is the nearest integer to v/s computed in fp64 except at (near-)ties
+        x = f32(X)
+        v = (x * cm[None, :]).astype(np.float32) if cm is not None else x
+        nz = s > 0
+        t = v[nz].astype(np.float64) / s[nz, None].astype(np.float64)
+        near_tie = np.abs(np.abs(t - np.floor(t)) - 0.5) < 1e-4
+        assert np.all((q[nz] == np.round(t)) | near_tie)
+
+
+@pytest.mark.parametrize("k", [-3, 1, 5])
+def test_quantize_power_of_two_invariance(k):
+    d = W.make_linear(16, 8, 256, seed=7, x_kind="four20")
+    q0, s0 = oracle.quantize_rows(d["X"])
+    Xs = bf(f32(d["X"]) * np.float32(2.0 ** k))  # exact scaling by 2^k
+    q1, s1 = oracle.quantize_rows(Xs)
+    assert np.array_equal(q0, q1)
+    assert np.array_equal(s1, (s0 * np.float32(2.0 ** k)).astype(np.float32))
+
+
+def test_per_token_scales_are_per_row():
+    # rows of very different magnitude each get their own scale (a per-tensor scale fails)
+    X = bf(np.outer(10.0 ** np.arange(-4, 4), np.linspace(-1, 1, 64)).astype(np.float32))
+    q, s = oracle.quantize_rows(X)
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    assert np.all(np.diff(np.log10(s)) > 0.9)
+
+
+# ----------------------------------------------------------------------------- smoothing
+def test_lambda_closed_form_on_powers_of_four():
+    a = np.arange(-6, 7)
+    b = np.arange(6, -7, -1)
+    s = (4.0 ** a).astype(np.float32)
+    w = (4.0 ** b).astype(np.float32)
+    lam, inv = oracle.smooth_lambda(s, w, 0.5)
+    assert np.array_equal(lam, (2.0 ** (a - b)).astype(np.float32))
+    assert np.array_equal(inv, (2.0 ** (b - a)).astype(np.float32))
+
+
+def test_lambda_zero_channels_and_other_alpha():
+    s = np.array([0.0, 3.0, 0.0, 2.0], np.float32)
+    w = np.array([1.0, 0.0, 0.0, 0.5], np.float32)
+    lam, inv = oracle.smooth_lambda(s, w, 0.5)
+    assert lam[:3].tolist() == [1.0, 1.0, 1.0] and inv[:3].tolist() == [1.0, 1.0, 1.0]
+    assert lam[3] == np.float32(2.0)
+    # alpha = 1 moves everything into the weights: lambda = s; alpha = 0: lambda = 1/w
+    lam1, _ = oracle.smooth_lambda(s[3:], w[3:], 1.0)
+    lam0, _ = oracle.smooth_lambda(s[3:], w[3:], 0.0)
+    assert lam1[0] == np.float32(2.0) and lam0[0] == np.float32(2.0)
+    lamq, _ = oracle.smooth_lambda(np.float32([16.0]), np.float32([81.0]), 0.25)
+    assert abs(float(lamq[0]) - 2.0 / 27.0) < 1e-6
+
+
+def test_smoothing_balances_channel_ranges():
+    # with alpha = 0.5 the smoothed activation and the smoothed weight of channel j
+    # share the same max-abs, sqrt(s_j w_j)
+    d = W.make_linear(64, 96, 256, seed=11, x_kind="four20")
+    s = oracle.channel_absmax(d["X"])
+    Wq, sw, inv, lam = oracle.smooth_prepare(d["W"], s, 0.5)
+    x = f32(d["X"]).astype(np.float64)
+    w = f32(d["W"]).astype(np.float64)
+    xs = np.abs(x * inv[None, :]).max(axis=0)
+    ws = np.abs(w * lam[None, :]).max(axis=0)
+    target = np.sqrt(s.astype(np.float64) * np.abs(w).max(axis=0))
+    assert np.allclose(xs, target, rtol=4e-7) and np.allclose(ws, target, rtol=4e-7)
+    assert np.all(np.abs(inv.astype(np.float64) * lam.astype(np.float64) - 1.0) <= 2.0 ** -23)
+
+
+def test_channel_absmax_accumulates():
+    d = W.make_linear(40, 8, 128, seed=3, x_kind="four20")
+    full = oracle.channel_absmax(d["X"])
+    part = oracle.channel_absmax(d["X"][:13])
+    acc = oracle.channel_absmax(d["X"][13:], part)
+    assert np.array_equal(full, acc)
+    assert np.array_equal(full, np.abs(f32(d["X"])).max(axis=0))
+
+
+def _reconstruction_bound_check(r, X, Wt):
+    """sum_j (qx sx)(qw sw) reproduces X W^T within the quantization and rounding bound."""
+    x = f32(X).astype(np.float64)
+    w = f32(Wt).astype(np.float64)
+    sx = r["sx"].astype(np.float64)
+    sw = r["sw"].astype(np.float64)
+    xh = r["Xq"].astype(np.float64) * sx[:, None]
+    wh = r["Wq"].astype(np.float64) * sw[:, None]
+    approx = xh @ wh.T
+    exact = x @ w.T
+    xs = np.abs(x * r["inv_lambda"][None, :].astype(np.float64))
+    ws = np.abs(w * r["lam"][None, :].astype(np.float64))
+    h = 0.5 * (1.0 + 2.0 ** -15)
+    bound = (h * xs @ np.ones_like(ws).T * sw[None, :] + h * np.ones_like(xs) @ ws.T * sx[:, None]
+             + h * h * X.shape[1] * sx[:, None] * sw[None, :] + 4 * 2.0 ** -24 * (np.abs(x) @ np.abs(w).T))
+    assert np.all(np.abs(approx - exact) <= bound)
+    return approx, exact
+
+
+def test_smoothquant_invariant_through_quantization():
+    # X diag(lambda)^-1 diag(lambda) W = X W: the dequantized product must approximate the
+    # unsmoothed product; applying lambda on the wrong side (or twice) breaks the bound.
+    d = W.make_linear(24, 40, 512, seed=21, x_kind="four20", w_sigma=0.02)
+    r = oracle.linear(d["X"], d["W"], d["bias"])
+    _reconstruction_bound_check(r, d["X"], d["W"])
+    # planted mistake: lambda applied to the activations instead of its inverse
+    bad = dict(r)
+    bad["Xq"], bad["sx"] = oracle.quantize_rows(d["X"], r["lam"])
+    with pytest.raises(AssertionError):
+        _reconstruction_bound_check(bad, d["X"], d["W"])
+
+
+def test_smoothquant_exact_with_power_of_two_lambda():
+    # columns whose calibration max and weight max are powers of 4 give lambda = 2^k:
+    # then x_hat * w_hat == x * w exactly for every product, so X_hat W_hat^T == X W^T in fp64
+    rng = np.random.default_rng(4)
+    M, N, K = 6, 5, 64
+    x = (0.5 * rng.standard_normal((M, K))).astype(np.float32)   # |x| < 4 in practice
+    w = (0.01 * rng.standard_normal((N, K))).astype(np.float32)  # |w| < 0.25 in practice
+    X = bf(x); Wt = bf(w)
+    xa = np.abs(f32(X)); wa = np.abs(f32(Wt))
+    ia = xa.argmax(axis=0); iw = wa.argmax(axis=0)
+    X[ia, np.arange(K)] = bf(np.sign(f32(X[ia, np.arange(K)])) * 4.0 ** rng.integers(1, 3, K))
+    Wt[iw, np.arange(K)] = bf(np.sign(f32(Wt[iw, np.arange(K)])) * 4.0 ** rng.integers(-1, 1, K))
+    s = oracle.channel_absmax(X)
+    assert np.all(np.log2(s) % 2 == 0)
+    _, _, inv, lam = oracle.smooth_prepare(Wt, s, 0.5)
+    assert np.all(np.log2(lam) == np.round(np.log2(lam)))
+    xh = (f32(X) * inv[None, :]).astype(np.float64)
+    wh = (f32(Wt) * lam[None, :]).astype(np.float64)
+    assert np.array_equal(xh @ wh.T, f32(X).astype(np.float64) @ f32(Wt).astype(np.float64).T)
+
+
+# ----------------------------------------------------------------------------- epilogues
+def test_bias_epilogue_matches_fp64_dequant():
+    rng = np.random.default_rng(9)
+    M, N = 7, 19
+    acc = rng.integers(-2 ** 24, 2 ** 24, (M, N)).astype(np.int32)
+    acc[0, :5] = [0, 1, -1, 2 ** 30, -(2 ** 30)]
+    sx = (rng.uniform(0.5, 2.0, M) * 1e-3).astype(np.float32)
+    sw = (rng.uniform(0.5, 2.0, N) * 1e-4).astype(np.float32)
+    bias = bf(rng.standard_normal(N) * 0.01)
+    Y = oracle.epilogue(acc, sx, sw, bias, "bias")
+    ref = acc.astype(np.float64) * sx[:, None].astype(np.float64) * sw[None, :].astype(np.float64) \
+        + f32(bias).astype(np.float64)[None, :]
+    refb = oracle.f32_to_bf16(ref.astype(np.float32).ravel()).reshape(M, N)
+    assert ulp_dist_bf16(Y, refb).max() <= 1
+    # transposed scales (sw per row) or a dropped bias is caught
+    assert ulp_dist_bf16(oracle.epilogue(acc, sx, sw, None, "bias"), refb).max() > 1
+
+
+def test_zero_rows_project_to_bias_exactly():
+    # a zero row projects to the bias vector; rows are independent
+    # (Faster Ideogram 4 with Less Prompt Compute, "Most of the Tensor Was Zero")
+    d = W.make_linear(32, 48, 256, seed=5, x_kind="pareto", zero_rows_after=20)
+    r = oracle.linear(d["X"], d["W"], d["bias"])
+    assert np.all(r["sx"][20:] == 0) and np.all(r["Xq"][20:] == 0)
+    assert np.array_equal(f32(r["Y"][20:]), np.broadcast_to(f32(d["bias"]), (12, 48)))
+
+
+def test_rows_are_independent():
+    d = W.make_linear(40, 64, 256, seed=6, x_kind="four20")
+    r = oracle.linear(d["X"], d["W"], d["bias"])
+    rows = np.array([39, 0, 17, 17, 5])
+    Y = oracle.linear_rows(r["Xq"], r["sx"], r["Wq"], r["sw"], d["bias"], rows)
+    assert np.array_equal(Y, r["Y"][rows])
+    # padding with repeated rows (no new column maxima) leaves the real rows unchanged
+    Xp = np.concatenate([d["X"], d["X"][::-1]], axis=0)
+    rp = oracle.linear(Xp, d["W"], d["bias"], s=r["s"])
+    assert np.array_equal(rp["Y"][:40], r["Y"])
+
+
+def test_silu_gate_epilogue():
+    from scipy.special import expit
+    rng = np.random.default_rng(12)
+    M, F = 5, 33
+    acc = rng.integers(-3000, 3000, (M, 2 * F)).astype(np.int32)
+    acc[:, 0] = 0          # g = 0 (with zero bias) -> 0
+    acc[:, F + 1] = 0      # u = 0 -> 0
+    sx = np.full(M, 1e-2, np.float32)
+    sw = np.full(2 * F, 1e-2, np.float32)
+    Y = f32(oracle.epilogue(acc, sx, sw, None, "silu_gate"))
+    assert Y.shape == (M, F)
+    assert np.all(Y[:, 0] == 0) and np.all(Y[:, 1] == 0)
+    g = acc[:, :F].astype(np.float64) * 1e-4
+    u = acc[:, F:].astype(np.float64) * 1e-4
+    ref = g * expit(g) * u
+    refb = f32(oracle.f32_to_bf16(ref.astype(np.float32).ravel()).reshape(M, F))
+    assert ulp_dist_bf16(bf(Y), bf(refb)).max() <= 1
+    # the gate/up roles are not symmetric: swapping them is caught
+    swapped = u * expit(u) * g
+    assert np.abs(swapped - Y).max() > 1e-3
+
+
+def test_head_rmsnorm_closed_forms():
+    hd = 256
+    M, H = 4, 3
+    N = hd * H
+    rng = np.random.default_rng(13)
+    gamma = bf(1.0 + 0.1 * rng.standard_normal(hd))
+    g = f32(gamma).astype(np.float64)
+    sx = np.ones(M, np.float32)
+    sw = np.ones(N, np.float32)
+    # head 0 constant c per row, head 1 random, head 2 random at 1000x the scale
+    acc = np.zeros((M, N), np.int32)
+    c = np.array([3, -7, 1, 100])
+    acc[:, :hd] = c[:, None]
+    acc[:, hd:2 * hd] = rng.integers(-50, 50, (M, hd))
+    acc[:, 2 * hd:] = rng.integers(-50000, 50000, (M, hd))
+    for eps in (1e-6, 1e-2):
+        Y = f32(oracle.epilogue(acc, sx, sw, None, "head_rmsnorm", bf(f32(gamma)), hd, eps)).astype(np.float64)
+        # constant head: y r gamma = gamma c / sqrt(c^2 + eps)
+        want = g[None, :] * c[:, None] / np.sqrt(c[:, None].astype(np.float64) ** 2 + eps)
+        assert np.all(np.abs(Y[:, :hd] - want) <= np.abs(want) * 2.0 ** -7)
+        # each head is normalised on its own: sum (Y/gamma)^2 = hd * ms / (ms + eps)
+        for h in (1, 2):
+            y = acc[:, h * hd:(h + 1) * hd].astype(np.float64)
+            ms = (y ** 2).mean(axis=1)
+            lhs = ((Y[:, h * hd:(h + 1) * hd] / g[None, :]) ** 2).sum(axis=1)
+            assert np.allclose(lhs, hd * ms / (ms + eps), rtol=2e-2)
+    # tiny values: eps dominates, Y = y gamma / sqrt(eps)
+    acc2 = np.ones((1, hd), np.int32)
+    Y2 = f32(oracle.epilogue(acc2, np.float32([1e-6]), np.ones(hd, np.float32), None, "head_rmsnorm",
+                             gamma, hd, 1e-2)).astype(np.float64)
+    assert np.allclose(Y2[0], g * 1e-6 / np.sqrt(1e-2 + 1e-12), rtol=2 ** -7)
+
+
+def test_bf16_gemm_within_fp64_bound():
+    rng = np.random.default_rng(14)
+    M, N, K = 9, 13, 512
+    H = bf(rng.standard_normal((M, K)))
+    Wd = bf(0.01 * rng.standard_normal((N, K)))
+    bias = bf(0.01 * rng.standard_normal(N))
+    Z, Zf = oracle.bf16_gemm_rows(H, Wd, bias, want_f32=True)
+    ref = f32(H).astype(np.float64) @ f32(Wd).astype(np.float64).T + f32(bias).astype(np.float64)
+    assert np.all(np.abs(Zf - ref) <= np.abs(ref) * 2.0 ** -24 + 1e-30)
+    assert ulp_dist_bf16(Z, bf(ref.astype(np.float32))).max() <= 1
+    rows = np.array([8, 0, 3])
+    assert np.array_equal(oracle.bf16_gemm_rows(H, Wd, bias, rows), Z[rows])
+
+
+# ----------------------------------------------------------------------------- page facts
+def test_workload_shapes_match_page_facts():
+    f = json.load(open(os.path.join(GOLDEN, "page_facts.json")))
+    w = W.WORKLOADS
+    hidden = f["hidden_width"]["value"]
+    assert w["dit_attn_proj_4608x4608x4608"]["K"] == hidden == w["dit_attn_proj_4608x4608x4608"]["N"]
+    assert w["dit_attn_proj_4608x4608x4608"]["M"] == f["packed_rows_1024"]["value"] \
+        == f["text_rows_main_profile"]["value"] + f["image_rows_1024"]["value"]
+    tc = w["text_cond_proj_512x4608x53248"]
+    assert (tc["M"], tc["K"], tc["N"]) == (f["text_rows_main_profile"]["value"], f["qwen_feature_width"]["value"],
+                                           hidden)
+    assert [1, tc["padded_M"], tc["K"]] == f["conditioning_tensor_shape"]["value"]
+    assert w["qk_proj_headnorm_6037x4608x4608"]["M"] == f["packed_rows_long_prompt"]["value"] \
+        == f["packed_rows_long_prompt"]["prompt_tokens"] + f["image_rows_1024"]["value"]
+    qk = w["qk_proj_headnorm_16896x4608x4608"]
+    assert qk["M"] == f["predicted_zero_row_savings_gib"]["image_rows"][2] + f["text_rows_main_profile"]["value"]
+    assert qk["head_dim"] == f["head_dim"]["value"] and qk["N"] % qk["head_dim"] == 0
+    # byte counts printed on the page follow from these shapes
+    c = f["cached_text_projection_mib"]
+    assert math.prod(c["shape"]) * c["dtype_bytes"] / 2 ** 20 == c["value"]
+    z = f["predicted_zero_row_savings_gib"]
+    for rows, gib in zip(z["image_rows"], z["value"]):
+        assert rows * tc["K"] * z["dtype_bytes"] * z["branches"] / 2 ** 30 == gib
+    fc = f["fp32_construction_gib"]
+    assert abs(sum(fc["rows"]) * fc["width"] * fc["dtype_bytes"] / 2 ** 30 - fc["value"]) < 5e-4
+    assert W.BASE_SEED == f["seed"]["value"]
+
+
+def test_generator_is_deterministic_and_prefix_stable():
+    a = W.make_workload("tiny_w8a8_64x128x256")
+    b = W.make_workload("tiny_w8a8_64x128x256")
+    for k in ("X", "W", "bias"):
+        assert np.array_equal(a[k], b[k])
+    full = W.make_linear(70, 8, 256, seed=99, x_kind="pct1")
+    pre = W.make_linear(30, 8, 256, seed=99, x_kind="pct1")
+    assert np.array_equal(full["X"][:30], pre["X"])
+    pad = W.make_linear(70, 8, 256, seed=99, x_kind="pct1", zero_rows_after=30)
+    assert np.array_equal(pad["X"][:30], pre["X"]) and not pad["X"][30:].any()
+    # outlier channels: 4 channels x20 in the tiny case
+    fac = W.outlier_factors(256, 1000, "four20")
+    assert sorted(np.unique(fac).tolist()) == [1.0, 20.0] and (fac == 20).sum() == 4

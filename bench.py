@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of the W8A8 DiT linear on one MI355X.
+
+A step is one pass of the hot path over one batch: per-token INT8 quantization of X
+(qdt_quantize_per_token) followed by the INT8 MFMA GEMM with the fused dequant + bias
+epilogue (qdt_w8a8_linear), on the 4608 x 4608 x 4608 attention projection (4096 image +
+512 text tokens at hidden width 4608).  Weight preparation (calibration max-abs, smoothing,
+weight quantization) is offline and untimed.  Inputs are seeded synthetic tensors resident
+in HBM; R rotating buffer sets (each with its own X, Xq, Wq and Y) keep every step's
+operands out of the 256 MB Infinity Cache.
+
+Prints one JSON line: effective TOPS = 2 M N K / wall time per step, the GEMM's MFMA
+roofline fraction (HIP events on the launch stream), the quantize pass's HBM fraction, the
+CPU oracle timed on the host on the same workload, and the other workloads' timings.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W8A8 DiT linear effective TOPS at 4608³ (quant+GEMM+epilogue), % INT8 peak"
+PEAK_INT8_TOPS = 5000.0    # MI355X dense INT8 MFMA
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=6, help="rotating buffer sets (cold Infinity Cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--only", default=None, help="run only this workload's timing loop (profiling)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def to_dev(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def time_loop(fn_step, sets, steps, warmup):
+    """Wall time of `steps` steps (sync on both sides) + per-phase HIP event times."""
+    import torch
+    st = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn_step(sets[i % len(sets)], None)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn_step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ph1 = [e[0].elapsed_time(e[1]) for e in evs]
+    ph2 = [e[1].elapsed_time(e[2]) for e in evs]
+    del st
+    return (t1 - t0) * 1e3 / steps, ph1, ph2
+
+
+def stats(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return dict(mean=float(a.mean()), median=float(np.median(a)), p10=float(np.percentile(a, 10)),
+                p90=float(np.percentile(a, 90)))
+
+
+def traffic_record(name):
+    """HBM bytes per launch measured with rocprofv3 counters, valid only for the kernel source it
+    was taken on (null once the source changed)."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "quantized_diffusion_transformer_amd", "csrc", rec["source"]), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec
+
+
+def headline(args):
+    import numpy as np
+    import torch
+
+    import qdt_workloads as W
+    import quantized_diffusion_transformer_amd as qdt
+
+    name = W.HEADLINE
+    log(f"generating {name}")
+    d = W.make_workload(name)
+    M, N, K = d["M"], d["N"], d["K"]
+    X0, W0, b = to_dev(d["X"]), to_dev(d["W"]), to_dev(d["bias"])
+    s = qdt.channel_absmax(X0)
+    Wq0, sw, inv, lam = qdt.smooth_prepare(W0, s)
+    torch.cuda.synchronize()
+    plan = qdt.linear_plan(M, N, K, "bias")
+    R = max(1, args.rotate)
+    sets = []
+    for r in range(R):
+        X = X0 if r == 0 else X0.clone()
+        Wq = Wq0 if r == 0 else Wq0.clone()
+        sets.append(dict(X=X, Wq=Wq, Xq=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                         sx=torch.empty(M, dtype=torch.float32, device="cuda"),
+                         Y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+    del W0
+    torch.cuda.synchronize()
+
+    def step(S, ev):
+        if ev is not None:
+            ev[0].record()
+        qdt.quantize_per_token(S["X"], inv, S["Xq"], S["sx"])
+        if ev is not None:
+            ev[1].record()
+        qdt.w8a8_linear(S["Xq"], S["sx"], S["Wq"], sw, b, "bias", out=S["Y"])
+        if ev is not None:
+            ev[2].record()
+
+    log(f"timing {args.steps} steps (warmup {args.warmup}, {R} rotating sets), plan {plan}")
+    ms, tq, tg = time_loop(step, sets, args.steps, args.warmup)
+    ops = 2.0 * M * N * K
+    tops = ops / (ms * 1e-3) / 1e12
+    q = stats(tq)
+    g = stats(tg)
+    qbytes = 2 * M * K + M * K + 4 * M + 4 * K
+    gbytes = M * K + N * K + 4 * M + 4 * N + 2 * N + 2 * M * N
+    gemm_tops = ops / (g["mean"] * 1e-3) / 1e12
+    traffic = traffic_record("w8a8_gemm_bias_4608")
+    out = {
+        "metric": METRIC,
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": name, "M": M, "N": N, "K": K, "epilogue": "bias", "smoothquant_alpha": 0.5,
+                   "plan": plan, "rotating_sets": R},
+        "pct_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel (qdt_w8a8_linear, BIAS)",
+                     "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+                     "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                     "algorithmic_ops_per_launch": ops, "avg_launch_ms": round(g["mean"], 5),
+                     "launch_ms": {k: round(v, 5) for k, v in g.items()}},
+        "roofline_quantize": {"bound": "hbm", "kernel": "quant_rows_kernel (qdt_quantize_per_token)",
+                              "achieved": round(qbytes / (q["mean"] * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                              "unit": "GB/s", "frac": round(qbytes / (q["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                              "algorithmic_bytes_per_launch": qbytes, "avg_launch_ms": round(q["mean"], 5),
+                              "launch_ms": {k: round(v, 5) for k, v in q.items()},
+                              "traffic": None if traffic_record("quantize_4608") is None
+                              else traffic_record("quantize_4608")["bytes_per_launch"]},
+        "gemm_algorithmic_bytes": gbytes,
+        "device": torch.cuda.get_device_name(0),
+    }
+    return out, d
+
+
+def cpu_baseline(d):
+    import numpy as np
+
+    import oracle
+    n = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    oracle.set_threads(min(n, os.cpu_count() or n))
+    s = oracle.channel_absmax(d["X"])
+    Wq, sw, inv, _ = oracle.smooth_prepare(d["W"], s)
+    M, N, K = d["M"], d["N"], d["K"]
+    # warm-up on a few rows, then the whole workload once: quantize + int32 GEMM + epilogue
+    oracle.linear_rows(*oracle.quantize_per_token(d["X"][:8], inv), Wq, sw, d["bias"], np.arange(8), "bias")
+    t0 = time.perf_counter()
+    Xq, sx = oracle.quantize_per_token(d["X"], inv)
+    acc = oracle.gemm_i32(Xq, Wq)
+    oracle.epilogue(acc, sx, sw, d["bias"], "bias")
+    dt = time.perf_counter() - t0
+    return {"value": round(2.0 * M * N * K / dt / 1e12, 4), "unit": "TOPS", "cores": oracle.threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the whole {M}x{N}x{K} linear once (quantize + int32 GEMM + BIAS epilogue), after a warm-up"}
+
+
+def extra_workloads(args):
+    """Timings of the other workloads (one rotating set; context for the other epilogues)."""
+    import torch
+
+    import qdt_workloads as W
+    import quantized_diffusion_transformer_amd as qdt
+    res = {}
+    steps, warm = max(5, args.steps // 5), 3
+
+    def prep(name, padded=False):
+        d = W.make_workload(name, padded=padded)
+        X, Wt = to_dev(d["X"]), to_dev(d["W"])
+        s = qdt.channel_absmax(X)
+        Wq, sw, inv, _ = qdt.smooth_prepare(Wt, s)
+        torch.cuda.synchronize()
+        return d, X, Wq, sw, inv
+
+    def run(name, d, X, Wq, sw, inv, epi, extra=None, **kw):
+        M, N, K = d["M"], d["N"], d["K"]
+        Xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        sx = torch.empty(M, dtype=torch.float32, device="cuda")
+        b = None if d.get("bias") is None else to_dev(d["bias"])
+        plan = qdt.linear_plan(M, N, K, epi)
+        ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device="cuda") if plan["workspace_bytes"] else None
+        nout = N // 2 if epi == "silu_gate" else N
+        Y = torch.empty((M, nout), dtype=torch.bfloat16, device="cuda")
+
+        def step(_, ev):
+            if ev is not None:
+                ev[0].record()
+            qdt.quantize_per_token(X, inv, Xq, sx)
+            if ev is not None:
+                ev[1].record()
+            qdt.w8a8_linear(Xq, sx, Wq, sw, b, epi, out=Y, workspace=ws, **kw)
+            if ev is not None:
+                ev[2].record()
+        ms, tq, tg = time_loop(step, [None], steps, warm)
+        ops = 2.0 * M * N * K
+        g = stats(tg)["mean"]
+        r = {"M": M, "N": N, "K": K, "epilogue": epi, "plan": plan, "ms_per_step": round(ms, 4),
+             "eff_tops": round(ops / (ms * 1e-3) / 1e12, 1), "gemm_ms": round(g, 4),
+             "gemm_tops": round(ops / (g * 1e-3) / 1e12, 1),
+             "gemm_frac_int8_peak": round(ops / (g * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+             "quantize_ms": round(stats(tq)["mean"], 4)}
+        if extra:
+            r.update(extra(Y))
+        res[name] = r
+        log(f"{name}: {r['ms_per_step']} ms/step, GEMM {r['gemm_tops']} TOPS")
+
+    d, X, Wq, sw, inv = prep("dit_ffn_gate_up_4608x24576x4608")
+    Wd = to_dev(d["W_down"])
+
+    def down(H):
+        Z = torch.empty((H.shape[0], Wd.shape[0]), dtype=torch.bfloat16, device="cuda")
+
+        def step(_, ev):
+            if ev is not None:
+                ev[0].record()
+                ev[1].record()
+            qdt.bf16_linear(H, Wd, out=Z)
+            if ev is not None:
+                ev[2].record()
+        _, _, tg = time_loop(step, [None], steps, warm)
+        g = stats(tg)["mean"]
+        fl = 2.0 * H.shape[0] * Wd.shape[0] * H.shape[1]
+        return {"bf16_down_proj": {"M": H.shape[0], "N": Wd.shape[0], "K": H.shape[1], "ms": round(g, 4),
+                                   "tflops": round(fl / (g * 1e-3) / 1e12, 1),
+                                   "frac_bf16_peak": round(fl / (g * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
+    run("dit_ffn_gate_up_4608x24576x4608", d, X, Wq, sw, inv, "silu_gate", extra=down)
+    del d, X, Wq, Wd
+    d, X, Wq, sw, inv = prep("text_cond_proj_512x4608x53248")
+    run("text_cond_proj_512x4608x53248", d, X, Wq, sw, inv, "bias")
+    dp = W.make_workload("text_cond_proj_512x4608x53248", padded=True)
+    run("text_cond_proj_padded_4608x4608x53248", dp, to_dev(dp["X"]), Wq, sw, inv, "bias")
+    del d, dp, X, Wq
+    for name in ("qk_proj_headnorm_16896x4608x4608", "qk_proj_headnorm_6037x4608x4608"):
+        d, X, Wq, sw, inv = prep(name)
+        run(name, d, X, Wq, sw, inv, "head_rmsnorm", gamma=to_dev(d["gamma"]), eps=d["eps"])
+        del d, X, Wq
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the W8A8 linear is measured on one "
+                                   "MI355X; multi-GPU sharding is a design note, not a measured path",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    out, d = headline(args)
+    log(f"headline: {out['value']} TOPS ({out['pct_int8_peak']}% of INT8 peak), {out['ms_per_step']} ms/step")
+    if args.only is None and not args.no_extra:
+        try:
+            out["other_workloads"] = extra_workloads(args)
+        except Exception as e:  # the headline line is still reported
+            out["other_workloads"] = {"error": repr(e)}
+    if not args.no_cpu_baseline and args.only is None:
+        log("cpu baseline (oracle on the host)")
+        out["cpu_baseline"] = cpu_baseline(d)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

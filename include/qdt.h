@@ -1,0 +1,198 @@
+/*
+ * qdt.h -- C ABI of the W8A8 quantized linear of a flow-matching diffusion transformer,
+ * implemented in hand-written HIP for AMD CDNA4 (gfx950, MI355X).
+ *
+ * The layer (pages, by title):
+ *   [PTQ]  "Quantizing a Dual-Branch Flow-Matching Diffusion Transformer for Consumer GPUs:
+ *          INT8 and GGUF Post-Training Quantization of Ideogram 4.0", W8A8 recipe paragraph:
+ *          per-output-row INT8 weights, per-token dynamic INT8 activations, SmoothQuant
+ *          smoothing lambda_j = s_j^alpha / max_i |W_ij|^(1-alpha) with alpha = 0.5 that
+ *          scales activations down and weights up before quantization; the FFN
+ *          down-projections are kept in bf16 (fragility paragraph).
+ *   [FAL]  "Serving sub-second Ideogram v4 without quality loss", paragraph on fused
+ *          epilogues: the small op after each big matmul (RMSNorm over 256-wide heads,
+ *          gated SiLU) is fused into the GEMM.
+ *   [ZC]   "Faster Ideogram 4 with Less Prompt Compute", section "Most of the Tensor Was
+ *          Zero": a linear with bias, rows projected independently, zero rows give the bias.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers into memory of the current HIP device; the caller
+ *     owns every buffer.  The library allocates no device memory.
+ *   - bf16 tensors are passed as uint16_t bit patterns.  Matrices are row-major; W is
+ *     [out_features = N, in_features = K] (nn.Linear layout), X is [M tokens, K].
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call
+ *     enqueues its kernels on `stream` and returns without synchronizing.
+ *   - Errors: argument errors are detected on the host before anything is launched and
+ *     returned synchronously (nothing is enqueued then).  A launch failure returns
+ *     QDT_EHIP.  Faults inside a kernel surface at the caller's next synchronization.
+ *   - Alignment: every pointer 16-byte aligned; row strides (ld*) in elements with
+ *     (ld * element size) a multiple of 16 bytes.
+ *   - K must be a positive multiple of 64 and at most QDT_MAX_K (the int32 accumulator
+ *     bound 127^2 * K < 2^31 holds up to K = 133144).
+ *   - Floating point follows IEEE fp32 round-to-nearest-even with no contraction except
+ *     the explicit fused multiply-add named below; integer stages are exact.
+ */
+#ifndef QDT_H
+#define QDT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QDT_MAX_K 131072
+
+typedef enum qdt_status {
+    QDT_OK = 0,
+    QDT_EINVAL = 1,       /* null pointer, bad enum or parameter value */
+    QDT_ESHAPE = 2,       /* dimension not supported (K % 64, N % 16, head_dim, ...) */
+    QDT_EALIGN = 3,       /* pointer or row stride misaligned */
+    QDT_EWORKSPACE = 4,   /* workspace missing or smaller than required */
+    QDT_EALIAS = 5,       /* output overlaps an input */
+    QDT_EHIP = 6,         /* the HIP runtime reported an error at launch */
+    QDT_EUNSUPPORTED = 7  /* valid request this build cannot serve (e.g. plan/epilogue pair) */
+} qdt_status;
+
+typedef enum qdt_epilogue {
+    /* Y[m][n] = bf16_rne(fmaf((float)acc[m][n], x_scale[m] * w_scale[n], bias[n]))
+     * (bias term +0.0f when bias is NULL).  [PTQ] dequantization; [ZC] linear with bias. */
+    QDT_EPI_BIAS = 0,
+    /* W rows are [gate(0..F-1); up(F..2F-1)], N = 2F, Y is [M, F]:
+     * g, u as in BIAS on rows f and F+f; Y[m][f] = bf16_rne((g / (1 + expf(-g))) * u).
+     * [FAL] gated-SiLU epilogue. */
+    QDT_EPI_SILU_GATE = 1,
+    /* y as in BIAS; per row and per head of head_dim columns: r = 1/sqrtf(mean(y^2) + eps),
+     * Y = bf16_rne((y * r) * gamma[n mod head_dim]).  [FAL] RMSNorm over 256-wide heads. */
+    QDT_EPI_HEAD_RMSNORM = 2,
+    /* Y is int32 [M, N]: the raw accumulators sum_k Xq[m][k] * Wq[n][k] (for testing). */
+    QDT_EPI_ACC_I32 = 3
+} qdt_epilogue;
+
+/* Parameters of QDT_EPI_HEAD_RMSNORM.  gamma: device bf16 [head_dim], shared by all heads. */
+typedef struct qdt_rmsnorm_params {
+    const uint16_t* gamma;
+    int32_t head_dim; /* must be 256 */
+    float eps;        /* added to the mean square inside the square root */
+} qdt_rmsnorm_params;
+
+/* Workgroup tile shapes of the MFMA GEMM. */
+typedef enum qdt_tile {
+    QDT_TILE_AUTO = -1,
+    QDT_TILE_256 = 0, /* 256 token rows x 256 weight rows per workgroup */
+    QDT_TILE_288 = 1  /* 288 x 288: 16 x 16 = 256 tiles at 4608 x 4608, one per compute unit */
+} qdt_tile;
+
+/* Launch plan of qdt_w8a8_linear.  The planner fills every field; callers of
+ * qdt_w8a8_linear_planned set `tile` and `split_k` (others are recomputed). */
+typedef struct qdt_linear_plan {
+    int32_t tile;            /* qdt_tile */
+    int32_t split_k;         /* number of K slices; 1 = no split (epilogue fused in the GEMM) */
+    int32_t tile_m, tile_n;  /* token rows and weight rows per workgroup */
+    int32_t tiles_m, tiles_n;
+    int32_t k_tiles;         /* K / 128 rounded up: K steps of the main loop */
+    int32_t grid;            /* workgroups launched by the GEMM kernel */
+    int64_t workspace_bytes; /* int32 partial sums for split_k > 1, else 0 */
+} qdt_linear_plan;
+
+/* Human-readable name of a status code (static storage). */
+const char* qdt_status_string(qdt_status status);
+
+/* Library version string (static storage). */
+const char* qdt_version(void);
+
+/*
+ * Calibration max-abs: s[j] = max over rows m of |X[m][j]|  ([PTQ]: the per-channel
+ * activation scale s of the smoothing rule; here taken from the given activations).
+ *   X: bf16 [M, ldx], first K columns used.  s: fp32 [K], output.
+ *   accumulate = 0: s is overwritten; accumulate != 0: s = max(s, new) (several batches).
+ * Exact (max of exact values).  M = 0 with accumulate = 0 gives s = 0.
+ */
+qdt_status qdt_channel_absmax(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, float* s,
+                              int accumulate, void* stream);
+
+/*
+ * Offline weight preparation ([PTQ] W8A8 recipe):
+ *   w_j = max_n |W[n][j]|
+ *   lambda_j = sqrtf(s_j) / sqrtf(w_j) for alpha = 0.5 (powf(s_j, alpha) / powf(w_j, 1 - alpha)
+ *     otherwise); lambda_j = 1 where s_j or w_j is 0;  inv_lambda_j = 1.0f / lambda_j
+ *   What_nj = (float)W[n][j] * lambda_j
+ *   w_scale[n] = max_j |What_nj| / 127;  Wq[n][j] = clamp(rint(What_nj / w_scale[n]), -127, 127)
+ *   (an all-zero row gets w_scale 0 and Wq 0).
+ *   W: bf16 [N, K].  s: fp32 [K] calibration max-abs, or NULL for no smoothing (lambda = 1).
+ *   Outputs: Wq int8 [N, K], w_scale fp32 [N], inv_lambda fp32 [K], lambda fp32 [K]
+ *   (inv_lambda and lambda are always written; the lambda buffer also serves as scratch).
+ *   alpha in [0, 1].  Bit-exact with the CPU definition for alpha = 0.5; other alpha use the
+ *   device powf.
+ */
+qdt_status qdt_smooth_prepare(const uint16_t* W, const float* s, int64_t N, int64_t K, float alpha,
+                              int8_t* Wq, float* w_scale, float* inv_lambda, float* lambda, void* stream);
+
+/*
+ * Per-token dynamic INT8 quantization of the activations ([PTQ] W8A8 recipe):
+ *   v = (float)X[m][j] * inv_lambda[j]   (v = (float)X[m][j] when inv_lambda is NULL)
+ *   x_scale[m] = max_j |v| / 127;  Xq[m][j] = clamp(rint(v / x_scale[m]), -127, 127)
+ *   with a correctly rounded fp32 division and round-half-to-even; an all-zero row gets
+ *   x_scale 0 and Xq 0.
+ *   X: bf16 [M, ldx] (first K columns).  Xq: int8 [M, K].  x_scale: fp32 [M].
+ *   Bit-exact.  M = 0 is a no-op.
+ */
+qdt_status qdt_quantize_per_token(const uint16_t* X, const float* inv_lambda, int64_t M, int64_t K,
+                                  int64_t ldx, int8_t* Xq, float* x_scale, void* stream);
+
+/* The plan qdt_w8a8_linear uses for this problem (pure host computation, no device call). */
+qdt_status qdt_w8a8_linear_plan(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, qdt_linear_plan* plan);
+
+/* The plan qdt_w8a8_linear_planned uses for a requested tile (qdt_tile, QDT_TILE_AUTO = planner's
+ * choice) and K split (0 = planner's choice; a request is rounded down so no slice is empty).
+ * Pure host computation. */
+qdt_status qdt_w8a8_linear_plan_for(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, int32_t tile, int32_t split_k,
+                                    qdt_linear_plan* plan);
+
+/* Bytes of workspace qdt_w8a8_linear needs for this problem (0 when it needs none). */
+qdt_status qdt_w8a8_linear_workspace_size(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, size_t* bytes);
+
+/*
+ * W8A8 linear: acc[m][n] = sum_k Xq[m][k] * Wq[n][k] in exact int32 on INT8 MFMA, followed by
+ * the epilogue `epi` (see qdt_epilogue), all in one kernel unless the plan splits K.
+ *   Xq int8 [M, K], x_scale fp32 [M] (from qdt_quantize_per_token); Wq int8 [N, K],
+ *   w_scale fp32 [N] (from qdt_smooth_prepare); bias bf16 [N] or NULL.
+ *   epi_params: qdt_rmsnorm_params* for QDT_EPI_HEAD_RMSNORM, else ignored (may be NULL).
+ *   Y: bf16 [M, ldy] with ldy >= N_out (N_out = N/2 for SILU_GATE, N otherwise), or int32
+ *   [M, ldy] for ACC_I32.  Y must not overlap any input.
+ *   workspace: device buffer of at least qdt_w8a8_linear_workspace_size() bytes (may be NULL
+ *   when that size is 0).
+ * Shapes: M >= 0 (rows are masked, any M), K % 64 == 0, N % 16 == 0 (N % 32 == 0 for
+ * SILU_GATE, N % 256 == 0 for HEAD_RMSNORM).  Results do not depend on M, the tile or the
+ * K split: the integer sum is exact and every output element is computed by the same
+ * fp32 operation sequence.
+ */
+qdt_status qdt_w8a8_linear(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
+                           const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi,
+                           const void* epi_params, void* Y, int64_t ldy, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* As qdt_w8a8_linear with an explicit tile and K split (plan->tile, plan->split_k; the other
+ * fields are recomputed and written back).  Used to show that results are plan-independent. */
+qdt_status qdt_w8a8_linear_planned(const int8_t* Xq, const float* x_scale, const int8_t* Wq,
+                                   const float* w_scale, const uint16_t* bias, int64_t M, int64_t N,
+                                   int64_t K, qdt_epilogue epi, const void* epi_params, void* Y, int64_t ldy,
+                                   void* workspace, size_t workspace_bytes, qdt_linear_plan* plan,
+                                   void* stream);
+
+/*
+ * bf16 linear of a protected (unquantized) layer ([PTQ] fragility paragraph: the FFN
+ * down-projections stay in bf16): Y[m][n] = bf16_rne(sum_k X[m][k] * W[n][k] + bias[n]),
+ * products exact, accumulated in fp32 on bf16 MFMA (summation order differs from a serial
+ * sum; error within the fp32 forward-error bound of a K-term sum).
+ *   X bf16 [M, K], W bf16 [N, K], bias bf16 [N] or NULL, Y bf16 [M, ldy].
+ * Shapes: K % 64 == 0, N % 16 == 0, any M >= 0.
+ */
+qdt_status qdt_bf16_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, int64_t M, int64_t N,
+                           int64_t K, uint16_t* Y, int64_t ldy, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QDT_H */

@@ -1,0 +1,237 @@
+"""Python binding of libqdt.so, the HIP (gfx950) W8A8 quantized linear of a flow-matching DiT.
+
+Argument marshalling only: every step runs in the library's kernels.  torch supplies the
+device memory and the current stream.  The ctypes entry points keep the C names
+(``qdt_quantize_per_token`` ...); the torch-facing helpers drop the prefix
+(``quantize_per_token`` ...), allocate outputs with torch and raise on any non-OK status.
+
+Importing this module loads the library and fails loudly if it has not been built
+(``python -c "import __graft_entry__ as g; g.build()"``).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqdt.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libqdt.so not found at {LIB_PATH}: build the HIP library first "
+                      "(quantized_diffusion_transformer_amd/_build.py)")
+
+_lib = C.CDLL(LIB_PATH)
+
+# ------------------------------------------------------------------------------- C types
+QDT_OK, QDT_EINVAL, QDT_ESHAPE, QDT_EALIGN, QDT_EWORKSPACE, QDT_EALIAS, QDT_EHIP, QDT_EUNSUPPORTED = range(8)
+QDT_EPI_BIAS, QDT_EPI_SILU_GATE, QDT_EPI_HEAD_RMSNORM, QDT_EPI_ACC_I32 = range(4)
+QDT_TILE_AUTO, QDT_TILE_256, QDT_TILE_288 = -1, 0, 1
+QDT_MAX_K = 131072
+
+EPILOGUES = {"bias": QDT_EPI_BIAS, "silu_gate": QDT_EPI_SILU_GATE, "head_rmsnorm": QDT_EPI_HEAD_RMSNORM,
+             "acc_i32": QDT_EPI_ACC_I32}
+
+
+class qdt_rmsnorm_params(C.Structure):
+    _fields_ = [("gamma", C.c_void_p), ("head_dim", C.c_int32), ("eps", C.c_float)]
+
+
+class qdt_linear_plan(C.Structure):
+    _fields_ = [("tile", C.c_int32), ("split_k", C.c_int32), ("tile_m", C.c_int32), ("tile_n", C.c_int32),
+                ("tiles_m", C.c_int32), ("tiles_n", C.c_int32), ("k_tiles", C.c_int32), ("grid", C.c_int32),
+                ("workspace_bytes", C.c_int64)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+_P, _I64, _F, _I, _SZ = C.c_void_p, C.c_int64, C.c_float, C.c_int, C.c_size_t
+_SIGS = {
+    "qdt_status_string": ([_I], C.c_char_p),
+    "qdt_version": ([], C.c_char_p),
+    "qdt_channel_absmax": ([_P, _I64, _I64, _I64, _P, _I, _P], _I),
+    "qdt_smooth_prepare": ([_P, _P, _I64, _I64, _F, _P, _P, _P, _P, _P], _I),
+    "qdt_quantize_per_token": ([_P, _P, _I64, _I64, _I64, _P, _P, _P], _I),
+    "qdt_w8a8_linear_plan": ([_I64, _I64, _I64, _I, C.POINTER(qdt_linear_plan)], _I),
+    "qdt_w8a8_linear_plan_for": ([_I64, _I64, _I64, _I, C.c_int32, C.c_int32, C.POINTER(qdt_linear_plan)], _I),
+    "qdt_w8a8_linear_workspace_size": ([_I64, _I64, _I64, _I, C.POINTER(_SZ)], _I),
+    "qdt_w8a8_linear": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P, _SZ, _P], _I),
+    "qdt_w8a8_linear_planned": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P, _SZ,
+                                 C.POINTER(qdt_linear_plan), _P], _I),
+    "qdt_bf16_linear": ([_P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+    globals()[_name] = _fn
+
+EXPORTED = tuple(_SIGS)
+
+
+class QdtError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {qdt_status_string(status).decode()}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != QDT_OK:
+        raise QdtError(status, where)
+
+
+def version() -> str:
+    return qdt_version().decode()
+
+
+# ------------------------------------------------------------------------------- helpers
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _rows(t, name):
+    """(tensor, row stride) of a 2-D tensor with unit column stride."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    return t, t.stride(0)
+
+
+# ------------------------------------------------------------------------------- torch API
+def channel_absmax(X: torch.Tensor, s: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Calibration max-abs per column of bf16 X [M, K]; accumulates into ``s`` when given."""
+    _dev(X, torch.bfloat16, "X")
+    X, ldx = _rows(X, "X")
+    M, K = X.shape
+    acc = s is not None
+    if s is None:
+        s = torch.empty(K, dtype=torch.float32, device=X.device)
+    _check(qdt_channel_absmax(_ptr(X), M, K, ldx, _ptr(s), int(acc), _stream(stream)), "qdt_channel_absmax")
+    return s
+
+
+def smooth_prepare(W: torch.Tensor, s: torch.Tensor | None, alpha: float = 0.5, stream=None):
+    """Offline weight preparation.  Returns (Wq int8 [N,K], w_scale [N], inv_lambda [K], lambda [K])."""
+    _dev(W, torch.bfloat16, "W")
+    if not W.is_contiguous():
+        raise ValueError("W must be contiguous")
+    N, K = W.shape
+    dev = W.device
+    Wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    sw = torch.empty(N, dtype=torch.float32, device=dev)
+    inv = torch.empty(K, dtype=torch.float32, device=dev)
+    lam = torch.empty(K, dtype=torch.float32, device=dev)
+    if s is not None:
+        _dev(s, torch.float32, "s")
+    _check(qdt_smooth_prepare(_ptr(W), _ptr(s), N, K, alpha, _ptr(Wq), _ptr(sw), _ptr(inv), _ptr(lam),
+                              _stream(stream)), "qdt_smooth_prepare")
+    return Wq, sw, inv, lam
+
+
+def quantize_per_token(X: torch.Tensor, inv_lambda: torch.Tensor | None, Xq=None, x_scale=None, stream=None):
+    """Per-token INT8 of bf16 X [M, K] (row stride may exceed K).  Returns (Xq int8 [M,K], x_scale [M])."""
+    _dev(X, torch.bfloat16, "X")
+    X, ldx = _rows(X, "X")
+    M, K = X.shape
+    if Xq is None:
+        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(M, dtype=torch.float32, device=X.device)
+    _check(qdt_quantize_per_token(_ptr(X), _ptr(inv_lambda), M, K, ldx, _ptr(Xq), _ptr(x_scale), _stream(stream)),
+           "qdt_quantize_per_token")
+    return Xq, x_scale
+
+
+def linear_plan(M: int, N: int, K: int, epilogue: str = "bias", tile: int | None = None,
+                split_k: int | None = None) -> dict:
+    p = qdt_linear_plan()
+    if tile is None and split_k is None:
+        _check(qdt_w8a8_linear_plan(M, N, K, EPILOGUES[epilogue], C.byref(p)), "qdt_w8a8_linear_plan")
+    else:
+        _check(qdt_w8a8_linear_plan_for(M, N, K, EPILOGUES[epilogue], QDT_TILE_AUTO if tile is None else tile,
+                                        0 if split_k is None else split_k, C.byref(p)), "qdt_w8a8_linear_plan_for")
+    return p.as_dict()
+
+
+def workspace_size(M: int, N: int, K: int, epilogue: str = "bias") -> int:
+    b = C.c_size_t(0)
+    _check(qdt_w8a8_linear_workspace_size(M, N, K, EPILOGUES[epilogue], C.byref(b)), "qdt_w8a8_linear_workspace_size")
+    return int(b.value)
+
+
+def w8a8_linear(Xq, x_scale, Wq, w_scale, bias=None, epilogue: str = "bias", gamma=None, head_dim: int = 256,
+                eps: float = 1e-6, out=None, workspace=None, tile: int | None = None, split_k: int | None = None,
+                stream=None):
+    """W8A8 linear with a fused epilogue.  Returns bf16 [M, N_out] (int32 [M, N] for "acc_i32").
+
+    ``tile`` / ``split_k`` force a plan (results are plan-independent); by default the
+    library plans.  ``workspace`` is allocated here when the plan needs one and none is given.
+    """
+    epi = EPILOGUES[epilogue]
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    nout = N // 2 if epi == QDT_EPI_SILU_GATE else N
+    dev = Xq.device
+    if out is None:
+        out = torch.empty((M, nout), dtype=torch.int32 if epi == QDT_EPI_ACC_I32 else torch.bfloat16, device=dev)
+    params = None
+    if epi == QDT_EPI_HEAD_RMSNORM:
+        params = qdt_rmsnorm_params(gamma.data_ptr(), head_dim, eps)
+    planned = tile is not None or split_k is not None
+    if planned:
+        plan = qdt_linear_plan()
+        plan.tile = QDT_TILE_AUTO if tile is None else tile
+        plan.split_k = 0 if split_k is None else split_k
+        need = linear_plan(M, N, K, epilogue, tile, split_k)["workspace_bytes"]
+    else:
+        need = workspace_size(M, N, K, epilogue)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), _ptr(bias), M, N, K, epi,
+            None if params is None else C.cast(C.byref(params), C.c_void_p), _ptr(out), out.stride(0),
+            _ptr(workspace), wsb]
+    if planned:
+        _check(qdt_w8a8_linear_planned(*args, C.byref(plan), _stream(stream)), "qdt_w8a8_linear_planned")
+    else:
+        _check(qdt_w8a8_linear(*args, _stream(stream)), "qdt_w8a8_linear")
+    return out
+
+
+def bf16_linear(X, W, bias=None, out=None, stream=None):
+    """bf16 linear of a protected layer: Y = X W^T + bias, fp32 accumulation on bf16 MFMA."""
+    _dev(X, torch.bfloat16, "X")
+    _dev(W, torch.bfloat16, "W")
+    M, K = X.shape
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    _check(qdt_bf16_linear(_ptr(X), _ptr(W), _ptr(bias), M, N, K, _ptr(out), out.stride(0), _stream(stream)),
+           "qdt_bf16_linear")
+    return out
+
+
+class PreparedLinear:
+    """A W8A8 linear with its weights prepared once (offline) on the device."""
+
+    def __init__(self, W: torch.Tensor, s: torch.Tensor | None, bias: torch.Tensor | None = None, alpha: float = 0.5):
+        self.N, self.K = W.shape
+        self.Wq, self.w_scale, self.inv_lambda, self.lam = smooth_prepare(W, s, alpha)
+        self.bias = bias
+
+    def __call__(self, X: torch.Tensor, epilogue: str = "bias", **kw) -> torch.Tensor:
+        Xq, sx = quantize_per_token(X, self.inv_lambda)
+        return w8a8_linear(Xq, sx, self.Wq, self.w_scale, self.bias, epilogue, **kw)

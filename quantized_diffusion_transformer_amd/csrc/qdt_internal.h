@@ -1,0 +1,55 @@
+// Internal declarations of the HIP path (kernels, launchers, planner).  Not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qdt.h"
+
+namespace qdt {
+
+constexpr int kNumCU = 256;  // MI355X compute units (8 XCDs x 32); the planner sizes grids for it
+constexpr int kNumXCD = 8;
+
+// ------------------------------------------------------------------ elementwise / row kernels
+hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t st);
+hipError_t launch_colmax(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, float* s, hipStream_t st);
+hipError_t launch_lambda(const float* s, float* lam_inout, float* inv, int64_t K, float alpha, hipStream_t st);
+// Per-row symmetric INT8 of X[m][:K] * colmul (colmul may be null).
+hipError_t launch_quant_rows(const uint16_t* X, int64_t ldx, const float* colmul, int64_t M, int64_t K, int8_t* Q,
+                             float* scale, hipStream_t st);
+
+// ------------------------------------------------------------------ GEMM
+enum EpiKind { EPI_BIAS = 0, EPI_SILU = 1, EPI_RMSNORM = 2, EPI_ACC = 3, EPI_PARTIAL = 4, EPI_F32BIAS = 5 };
+
+struct Plan {
+    int tile;       // qdt_tile
+    int bm, bn;     // token rows, weight rows per tile
+    int tiles_m, tiles_n, split_k, kt_total, kt_per_split, grid, group_m;
+    int64_t ws_bytes;
+};
+
+// Planner: pure host computation.  esize = operand bytes (1 int8, 2 bf16).
+// tile_req / split_req: QDT_TILE_AUTO / 0 for automatic.
+qdt_status make_plan(int64_t M, int64_t N, int64_t K, int epi, int esize, int tile_req, int split_req, Plan* p);
+
+struct GemmArgs {
+    const void* X;       // token operand [M][K] (int8 or bf16)
+    const void* W;       // weight operand [N][K]
+    const float* sx;     // [M] (int8 path)
+    const float* sw;     // [N] (int8 path)
+    const uint16_t* bias;
+    const uint16_t* gamma;
+    float eps;
+    void* Y;
+    int64_t ldy;
+    int32_t* ws;         // split-K partials [S][M][N]
+    int M, N, K;         // K in elements
+    int epi;             // EpiKind for the fused epilogue (EPI_PARTIAL when split)
+};
+
+hipError_t launch_gemm_i8(const GemmArgs& a, const Plan& p, hipStream_t st);
+hipError_t launch_gemm_bf16(const GemmArgs& a, const Plan& p, hipStream_t st);
+// Sum of the S int32 partial slices followed by epilogue `epi` (BIAS, SILU, RMSNORM, ACC).
+hipError_t launch_splitk_epilogue(const GemmArgs& a, int split_k, int epi, hipStream_t st);
+
+}  // namespace qdt

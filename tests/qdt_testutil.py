@@ -1,0 +1,52 @@
+"""Helpers shared by the tests: host/device transfer of bf16 bit patterns and ulp distances."""
+from __future__ import annotations
+
+import numpy as np
+
+
+def bf16_key(u) -> np.ndarray:
+    """Order-preserving integer of a bf16 bit pattern (+0 and -0 map to the same key)."""
+    u = np.asarray(u).astype(np.int64)
+    return np.where(u & 0x8000, 0x8000 - (u & 0x7FFF), 0x8000 + (u & 0x7FFF))
+
+
+def ulp_bf16(a, b) -> np.ndarray:
+    return np.abs(bf16_key(a) - bf16_key(b))
+
+
+def is_nan_bf16(u) -> np.ndarray:
+    u = np.asarray(u).astype(np.int64)
+    return ((u & 0x7F80) == 0x7F80) & ((u & 0x7F) != 0)
+
+
+def to_dev(a: np.ndarray, dev="cuda"):
+    """numpy array -> torch device tensor; uint16 arrays become bfloat16 (same bits)."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev)
+
+
+def to_host(t) -> np.ndarray:
+    """torch tensor -> numpy; bfloat16 becomes uint16 bit patterns."""
+    import torch
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def bits_equal(a: np.ndarray, b: np.ndarray) -> bool:
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def sample_rows(M: int, n: int, seed: int = 0) -> np.ndarray:
+    """First, last and tail rows plus a seeded sample, sorted and unique."""
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, M - 1, M - 2, M // 2]
+    tail = list(range(max(0, M - (M % 256 or 256)), M))[:8]
+    rows = np.unique(np.clip(np.concatenate([fixed, tail, rng.integers(0, M, n)]), 0, M - 1))
+    return rows.astype(np.int64)

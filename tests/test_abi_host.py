@@ -1,0 +1,137 @@
+"""Host-side tests of the C ABI (no GPU): exported symbols, validation errors, planner.
+
+Every call here fails validation or is a pure host computation, so nothing reaches HIP.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+qdt = pytest.importorskip("quantized_diffusion_transformer_amd")
+
+P = C.c_void_p
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "qdt.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qdt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    declared = header_functions()
+    assert len(declared) >= 10
+    lib = C.CDLL(qdt.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in qdt.h but not exported"
+    assert sorted(qdt.EXPORTED) == declared
+
+
+def test_status_strings_and_version():
+    for s in range(8):
+        assert qdt.qdt_status_string(s).decode().startswith("QDT_")
+    assert "gfx950" in qdt.version()
+
+
+def A(addr=0x10000):
+    return P(addr)
+
+
+def test_quantize_validation():
+    f = qdt.qdt_quantize_per_token
+    assert f(A(), None, 4, 100, 100, A(0x20000), A(0x30000), None) == qdt.QDT_ESHAPE  # K % 64
+    assert f(A(), None, 4, 128, 64, A(0x20000), A(0x30000), None) == qdt.QDT_ESHAPE   # ldx < K
+    assert f(A(), None, -1, 128, 128, A(0x20000), A(0x30000), None) == qdt.QDT_ESHAPE
+    assert f(None, None, 4, 128, 128, A(0x20000), A(0x30000), None) == qdt.QDT_EINVAL
+    assert f(A(0x10008), None, 4, 128, 128, A(0x20000), A(0x30000), None) == qdt.QDT_EALIGN
+    assert f(A(), None, 4, 128, 132, A(0x20000), A(0x30000), None) == qdt.QDT_EALIGN   # row stride
+    assert f(A(), None, 4, 128, 128, A(0x10100), A(0x30000), None) == qdt.QDT_EALIAS   # Xq inside X
+    assert f(A(), None, 4, qdt.QDT_MAX_K + 64, qdt.QDT_MAX_K + 64, A(0x2000000), A(0x3000000), None) == qdt.QDT_ESHAPE
+    assert f(A(), None, 0, 128, 128, A(0x20000), A(0x30000), None) == qdt.QDT_OK        # M = 0: no-op
+
+
+def test_smooth_prepare_validation():
+    f = qdt.qdt_smooth_prepare
+    outs = (A(0x100000), A(0x200000), A(0x300000), A(0x400000))
+    assert f(A(), None, 8, 100, 0.5, *outs, None) == qdt.QDT_ESHAPE
+    assert f(A(), None, 8, 128, 1.5, *outs, None) == qdt.QDT_EINVAL
+    assert f(A(), None, 8, 128, float("nan"), *outs, None) == qdt.QDT_EINVAL
+    assert f(A(), None, 8, 128, 0.5, A(0x100000), A(0x200000), None, A(0x400000), None) == qdt.QDT_EINVAL
+    assert f(A(), None, 8, 128, 0.5, A(0x10010), A(0x200000), A(0x300000), A(0x400000), None) == qdt.QDT_EALIAS
+    assert f(A(), None, 8, 128, 0.5, A(0x100000), A(0x100000), A(0x300000), A(0x400000), None) == qdt.QDT_EALIAS
+
+
+def _lin(M=64, N=128, K=256, epi=0, params=None, Y=0x900000, ldy=None, ws=None, wsb=0, bias=None,
+         xq=0x100000, sx=0x200000, wq=0x300000, sw=0x400000):
+    ldy = (N // 2 if epi == 1 else N) if ldy is None else ldy
+    return qdt.qdt_w8a8_linear(A(xq), A(sx), A(wq), A(sw), None if bias is None else A(bias), M, N, K, epi, params,
+                               A(Y), ldy, None if ws is None else A(ws), wsb, None)
+
+
+def test_linear_validation():
+    assert _lin(K=100) == qdt.QDT_ESHAPE
+    assert _lin(N=120) == qdt.QDT_ESHAPE
+    assert _lin(N=48, epi=1) == qdt.QDT_ESHAPE                     # SILU needs N % 32
+    assert _lin(N=384, epi=2, params=None) == qdt.QDT_ESHAPE        # heads need N % 256
+    assert _lin(N=512, epi=2, params=None) == qdt.QDT_EINVAL        # missing gamma
+    bad = qdt.qdt_rmsnorm_params(0x500000, 128, 1e-6)
+    assert _lin(N=512, epi=2, params=C.cast(C.byref(bad), P)) == qdt.QDT_ESHAPE
+    neg = qdt.qdt_rmsnorm_params(0x500000, 256, -1.0)
+    assert _lin(N=512, epi=2, params=C.cast(C.byref(neg), P)) == qdt.QDT_EINVAL
+    assert _lin(epi=7) == qdt.QDT_EINVAL
+    assert _lin(ldy=64) == qdt.QDT_ESHAPE
+    assert _lin(ldy=132) == qdt.QDT_EALIGN
+    assert _lin(Y=0x900008) == qdt.QDT_EALIGN
+    assert _lin(Y=0x300000 + 1024) == qdt.QDT_EALIAS                # Y over Wq
+    assert _lin(M=0) == qdt.QDT_OK                                   # empty: nothing to do
+
+
+def test_linear_workspace_checks():
+    M, N, K = 512, 4608, 53248
+    need = qdt.workspace_size(M, N, K)
+    plan = qdt.linear_plan(M, N, K)
+    assert plan["split_k"] > 1 and need == plan["split_k"] * M * N * 4
+    big = 0x10000000000
+    args = dict(M=M, N=N, K=K, xq=big, sx=2 * big, wq=3 * big, sw=4 * big, Y=5 * big)
+    assert _lin(**args) == qdt.QDT_EWORKSPACE
+    assert _lin(ws=6 * big, wsb=need - 16, **args) == qdt.QDT_EWORKSPACE
+    assert _lin(ws=5 * big + 64, wsb=need, **args) == qdt.QDT_EALIAS  # workspace over Y
+
+
+def test_bf16_linear_validation():
+    f = qdt.qdt_bf16_linear
+    assert f(A(), A(0x200000), None, 4, 100, 128, A(0x900000), 100, None) == qdt.QDT_ESHAPE
+    assert f(A(), A(0x200000), None, 4, 128, 96, A(0x900000), 128, None) == qdt.QDT_ESHAPE
+    assert f(A(), A(0x200000), None, 4, 128, 128, A(0x10000), 128, None) == qdt.QDT_EALIAS
+    assert f(A(), A(0x200000), None, 0, 128, 128, A(0x900000), 128, None) == qdt.QDT_OK
+
+
+@pytest.mark.parametrize("M,N,K,epi,tile,split", [
+    (4608, 4608, 4608, "bias", 288, 1),          # attention projection: 256 tiles of 288 x 288
+    (512, 4608, 53248, "bias", 256, 7),          # deep-K text projection: split K over 7 slices
+    (4608, 4608, 53248, "bias", 288, 1),         # its zero-padded variant fills the GPU without a split
+    (16896, 4608, 4608, "head_rmsnorm", 256, 1),  # heads need 256-wide tiles
+    (6037, 4608, 4608, "head_rmsnorm", 256, 1),
+    (4608, 24576, 4608, "silu_gate", 256, 1),
+    (64, 128, 256, "bias", 256, 1),
+])
+def test_planner_choices(M, N, K, epi, tile, split):
+    p = qdt.linear_plan(M, N, K, epi)
+    assert p["tile_m"] == tile and p["split_k"] == split
+    nout_tiles = -(-(N // 2) // (tile // 2)) if epi == "silu_gate" else -(-N // tile)
+    assert p["tiles_m"] == -(-M // tile) and p["tiles_n"] == nout_tiles
+    assert p["grid"] == p["tiles_m"] * p["tiles_n"] * p["split_k"]
+    assert p["workspace_bytes"] == (split * M * N * 4 if split > 1 else 0)
+
+
+def test_plan_for_honours_requests():
+    p = qdt.linear_plan(600, 1024, 4096, "bias", tile=qdt.QDT_TILE_288, split_k=5)
+    assert p["tile_m"] == 288 and p["split_k"] == 5 and p["k_tiles"] == 32
+    # a request that would leave an empty slice is rounded down
+    p = qdt.linear_plan(600, 1024, 256, "bias", split_k=3)
+    assert p["split_k"] == 2
+    with pytest.raises(qdt.QdtError):
+        qdt.linear_plan(600, 1024, 4096, "head_rmsnorm", tile=qdt.QDT_TILE_288)

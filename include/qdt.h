@@ -27,8 +27,9 @@
  *     QDT_EHIP.  Faults inside a kernel surface at the caller's next synchronization.
  *   - Alignment: every pointer 16-byte aligned; row strides (ld*) in elements with
  *     (ld * element size) a multiple of 16 bytes.
- *   - K must be a positive multiple of 64 and at most QDT_MAX_K (the int32 accumulator
- *     bound 127^2 * K < 2^31 holds up to K = 133144).
+ *   - K must be a positive multiple of 64 (of 128 for qdt_w8a8_linear, whose main loop
+ *     moves whole 128-byte cache lines per row and stage) and at most QDT_MAX_K (the int32
+ *     accumulator bound 127^2 * K < 2^31 holds up to K = 133144).
  *   - Floating point follows IEEE fp32 round-to-nearest-even with no contraction except
  *     the explicit fused multiply-add named below; integer stages are exact.
  */
@@ -47,7 +48,7 @@ extern "C" {
 typedef enum qdt_status {
     QDT_OK = 0,
     QDT_EINVAL = 1,       /* null pointer, bad enum or parameter value */
-    QDT_ESHAPE = 2,       /* dimension not supported (K % 64, N % 16, head_dim, ...) */
+    QDT_ESHAPE = 2,       /* dimension not supported (K % 64 or % 128, N % 16, head_dim, ...) */
     QDT_EALIGN = 3,       /* pointer or row stride misaligned */
     QDT_EWORKSPACE = 4,   /* workspace missing or smaller than required */
     QDT_EALIAS = 5,       /* output overlaps an input */
@@ -91,7 +92,7 @@ typedef struct qdt_linear_plan {
     int32_t split_k;         /* number of K slices; 1 = no split (epilogue fused in the GEMM) */
     int32_t tile_m, tile_n;  /* token rows and weight rows per workgroup */
     int32_t tiles_m, tiles_n;
-    int32_t k_tiles;         /* K / 128 rounded up: K steps of the main loop */
+    int32_t k_tiles;         /* K stages of the main loop (64 bytes of K each) */
     int32_t grid;            /* workgroups launched by the GEMM kernel */
     int64_t workspace_bytes; /* int32 partial sums for split_k > 1, else 0 */
 } qdt_linear_plan;
@@ -163,7 +164,7 @@ qdt_status qdt_w8a8_linear_workspace_size(int64_t M, int64_t N, int64_t K, qdt_e
  *   [M, ldy] for ACC_I32.  Y must not overlap any input.
  *   workspace: device buffer of at least qdt_w8a8_linear_workspace_size() bytes (may be NULL
  *   when that size is 0).
- * Shapes: M >= 0 (rows are masked, any M), K % 64 == 0, N % 16 == 0 (N % 32 == 0 for
+ * Shapes: M >= 0 (rows are masked, any M), K % 128 == 0, N % 16 == 0 (N % 32 == 0 for
  * SILU_GATE, N % 256 == 0 for HEAD_RMSNORM).  Results do not depend on M, the tile or the
  * K split: the integer sum is exact and every output element is computed by the same
  * fp32 operation sequence.

@@ -25,22 +25,23 @@ static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // round that is only 68/256 full.
 qdt_status make_plan(int64_t M, int64_t N, int64_t K, int epi, int esize, int tile_req, int split_req, Plan* p) {
     const bool silu = epi == EPI_SILU, rms = epi == EPI_RMSNORM;
-    const int64_t kt_total = cdiv(K * esize, 128);
     Plan best{};
     double best_cost = -1.0;
     for (int tile = QDT_TILE_256; tile <= QDT_TILE_288; ++tile) {
         if (tile_req != QDT_TILE_AUTO && tile != tile_req) continue;
         if (tile == QDT_TILE_288 && (silu || rms)) continue;  // heads / gate-up halves need 256-wide tiles
         const int bm = tile == QDT_TILE_288 ? 288 : 256, bn = bm;
+        const int64_t kstage = 128;  // bytes of K per main-loop stage (whole cache lines)
+        const int64_t kt_total = cdiv(K * esize, kstage);
         const int64_t tiles_m = cdiv(M > 0 ? M : 1, bm);
         const int64_t tiles_n = silu ? cdiv(N / 2, bn / 2) : cdiv(N, bn);
         const int64_t tiles = tiles_m * tiles_n;
         int64_t split = 1;
         if (split_req > 0) {
             split = split_req;
-        } else if (esize == 1 && tiles < kNumCU / 2 && kt_total >= 32) {
+        } else if (esize == 1 && tiles < kNumCU / 2 && kt_total * kstage >= 8192) {
             split = kNumCU / tiles;
-            if (split > kt_total / 16) split = kt_total / 16;
+            if (split > kt_total * kstage / 4096) split = kt_total * kstage / 4096;
             if (split > 16) split = 16;
             if (split < 1) split = 1;
         }
@@ -49,7 +50,7 @@ qdt_status make_plan(int64_t M, int64_t N, int64_t K, int epi, int esize, int ti
         split = cdiv(kt_total, kps);  // no empty slices
         const int64_t grid = tiles * split;
         const int64_t rounds = cdiv(grid, kNumCU);
-        double cost = (double)rounds * bm * bn * kps * 128.0 / 8192.0;  // ~cycles of MFMA per CU
+        double cost = (double)rounds * bm * bn * kps * kstage / 8192.0;  // ~cycles of MFMA per CU
         if (split > 1) cost += (double)split * M * N * 4 * 2 / (8e12 / 2.4e9 / kNumCU) / kNumCU;
         if (best_cost < 0 || cost < best_cost) {
             best_cost = cost;
@@ -168,7 +169,7 @@ static int epi_kind(qdt_epilogue e) {
 static qdt_status check_shape(int64_t M, int64_t N, int64_t K, qdt_epilogue epi) {
     if (epi_kind(epi) < 0) return QDT_EINVAL;
     if (M < 0 || M > INT32_MAX / 2 || N <= 0 || N > INT32_MAX / 2 || N % 16 != 0) return QDT_ESHAPE;
-    if (K <= 0 || K % 64 != 0 || K > QDT_MAX_K) return QDT_ESHAPE;
+    if (K <= 0 || K % 128 != 0 || K > QDT_MAX_K) return QDT_ESHAPE;
     if (epi == QDT_EPI_SILU_GATE && N % 32 != 0) return QDT_ESHAPE;
     if (epi == QDT_EPI_HEAD_RMSNORM && N % 256 != 0) return QDT_ESHAPE;
     return QDT_OK;

@@ -13,15 +13,18 @@
 //     (v_mfma_f32_16x16x32_bf16 for bf16).  The MFMA A operand is the weight fragment and
 //     the B operand the token fragment, so lane l holds 4 consecutive output columns of one
 //     output row: the epilogue stores 8 bytes per lane straight from registers.
-//   * K advances 128 bytes per stage.  Global -> VGPR prefetch of stage k+1 overlaps the
-//     MFMAs of stage k; LDS is double buffered (one barrier per stage).  Rows are 128 bytes
-//     in LDS with the 16-byte chunks XOR-swizzled by (row & 7) so that the 16 rows read by
-//     one ds_read_b128 fall in distinct banks.
+//   * K advances 128 bytes (two MFMA K steps; 64 bytes for the 288 tile) per stage through two
+//     LDS buffers: the global loads of stage k+1 are in flight (register staged) while the
+//     MFMAs of stage k run, then written to the other buffer -- one barrier per stage.  LDS
+//     rows are XOR-swizzled so that the 16 rows read by one ds_read_b128 fall in distinct
+//     banks.
 //   * Tile order is XCD-aware: workgroup ids are dealt round-robin to the 8 XCDs, so ids are
 //     remapped to give each XCD a contiguous run of tiles, walked in groups of `group_m` tile
 //     rows, which keeps the operands of neighbouring tiles in that XCD's L2.
-//   * Rows beyond M (or N) load zeros and are not stored; the integer sum is exact, so the
-//     result is independent of the tile shape and of the K split.
+//   * Rows beyond M (or N) are clamped loads whose outputs are not stored; the integer sum is
+//     exact, so the result is independent of the tile shape and of the K split.
+#include <type_traits>
+
 #include "qdt_device.h"
 #include "qdt_internal.h"
 
@@ -30,6 +33,9 @@ namespace qdt {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+// 16-byte chunk as a native vector (HIP's uint4 is a struct whose copies become memcpy,
+// which keeps arrays of it out of registers)
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 struct KArgs {
     const uint8_t* X;
@@ -53,37 +59,71 @@ struct AccT<false> { typedef v4i type; };
 template <>
 struct AccT<true> { typedef v4f type; };
 
-template <bool BF16>
-__device__ __forceinline__ typename AccT<BF16>::type mfma(const uint4& a, const uint4& b, typename AccT<BF16>::type c) {
+// MFMA with the accumulator tied in place (dst == srcC).  Issued from inline asm: the
+// compiler's own MFMA selection may pick the untied form, whose early-clobber destination
+// forces accumulators to rotate through a spare register tuple on every iteration once all
+// 256 accumulation registers are in use.  ACC_AGPR selects where the tuple lives (AGPR, or a
+// VGPR tuple for tiles with more than 64 accumulator tuples per wave).  Being asm, these are
+// invisible to the hazard recognizer: the kernel waits explicitly before reading accumulators.
+template <bool BF16, bool ACC_AGPR>
+__device__ __forceinline__ void mfma(typename AccT<BF16>::type& c, const v4u& a, const v4u& b) {
     if constexpr (BF16) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0,
-                                                      0);
+        if constexpr (ACC_AGPR)
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+        else
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
     } else {
-        return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a), __builtin_bit_cast(v4i, b), c, 0, 0, 0);
+        if constexpr (ACC_AGPR)
+            asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+        else
+            asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
     }
 }
 
-// WM x WN waves, FM x FN fragments of 16x16 per wave.  PHASED: prefetch the weight half of
-// the next stage before the first K sub-step and the token half before the second one
-// (halves the prefetch registers of the large tile).
-template <int WM, int WN, int FM, int FN, bool BF16, int EPI, bool PHASED>
+// Wait for the MFMA pipeline to drain before accumulators are read by other instructions.
+__device__ __forceinline__ void mfma_drain() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+// LDS-DMA (gfx950 global_load_lds_dwordx4): lane l of the wave copies 16 bytes from its global
+// address to LDS at m0 + 16 l, i.e. one wave instruction fills 1 KiB of LDS without passing
+// through registers.  Issued from inline asm so that the compiler does not wait for it before
+// every LDS read; completion is tracked by explicit vmcnt waits before the barrier that
+// publishes a stage.  M0 is set in the same statement (the compiler sets M0 itself before
+// each of its own uses).
+__device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* gptr) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(gptr)
+                 : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// WM x WN waves, FM x FN fragments of 16x16 per wave.
+template <int WM, int WN, int FM, int FN, bool BF16, int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64), amdgpu_waves_per_eu(1, 1))) void
 gemm_kernel(KArgs p) {
-    constexpr int NT = WM * WN * 64;
+    constexpr int NW = WM * WN;            // waves
     constexpr int BM = WM * FM * 16;
     constexpr int BN = WN * FN * 16;
-    constexpr int BKC = 8;  // 16-byte chunks per row per stage
-    constexpr int BK = BKC * 16;
-    constexpr int ROWS = BN + BM;  // LDS rows per stage: weight rows, then token rows
+    constexpr int BK = 128;                // K bytes per stage: two MFMA K steps, whole cache lines
+    constexpr int NB = 2;                  // LDS stages (double buffer)
+    constexpr int ROWS = BN + BM;          // LDS rows per stage: weight rows, then token rows
     constexpr int STAGE = ROWS * BK;
-    constexpr int RSTEP = NT / BKC;
-    constexpr int CW = BN / RSTEP, CX = BM / RSTEP;
+    constexpr int NBLK = ROWS / 8;         // 1 KiB LDS blocks (8 rows) per stage
+    constexpr int NI = NBLK / NW;          // LDS-DMA instructions per wave per stage
+    constexpr int NACC_A = 64;             // accumulator tuples held in AGPRs (the rest in VGPRs)
     constexpr bool SILU = EPI == EPI_SILU;
-    static_assert(BN % RSTEP == 0 && BM % RSTEP == 0, "tile rows must be a multiple of the load row step");
-    static_assert(!SILU || ((BN / 2) % RSTEP == 0 && FN % 2 == 0), "gate/up halves must align");
+    static_assert(NBLK % NW == 0, "whole LDS blocks per wave");
+    static_assert(BN % 8 == 0 && (!SILU || ((BN / 2) % 8 == 0 && FN % 2 == 0)), "blocks never straddle");
+    static_assert(FM <= FN && NI <= 2 * FN, "reads and LDS-DMAs fit in the fragment groups");
     using Acc = typename AccT<BF16>::type;
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * STAGE];
     __shared__ float red[EPI == EPI_RMSNORM ? WN * BM : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -104,56 +144,44 @@ gemm_kernel(KArgs p) {
     const int n0 = tn * (SILU ? BN / 2 : BN);  // first output column (SILU) / weight row
     const int kt0 = split * p.kt_per_split;
     const int kt1 = min(p.kt_total, kt0 + p.kt_per_split);
+    const int nk = kt1 - kt0;
 
-    // ---- global load assignment: chunk kc of rows rb + i * RSTEP
-    const int kc = tid % BKC, rb = tid / BKC;
+    // LDS rows are 128 bytes; chunk c of row g sits in slot c ^ (g & 7), which keeps the 16 rows
+    // of a fragment read by one ds_read_b128 free of bank conflicts on gfx950 (measured with the
+    // SQ_LDS_BANK_CONFLICT counter).
+
+    // ---- LDS-DMA assignment: instruction i of wave w fills LDS block b = w * NI + i = tile rows
+    // 8 b .. 8 b + 7 (weight rows first, then token rows); lane l moves row 8 b + l / 8, slot l % 8,
+    // which holds global chunk (l % 8) ^ (row & 7).  A whole 128-byte line per row and stage:
+    // half-line stages measured at 14 TB/s of L2 -> LDS traffic, whole lines at 21 TB/s.
+    // Rows past the matrix end are clamped to its last row: their products only reach outputs
+    // that are not stored.
     const int64_t Kb = p.Kb;
     const int nlim = SILU ? p.F : p.N;
-    const uint8_t* pw = p.W + (int64_t)(n0 + rb) * Kb + kc * 16;
-    const uint8_t* pwu = SILU ? p.W + (int64_t)(p.F + n0 + rb) * Kb + kc * 16 : pw;
-    const uint8_t* px = p.X + (int64_t)(m0 + rb) * Kb + kc * 16;
-    const int w_rows_left = nlim - n0 - rb;  // chunk i valid iff i * RSTEP < rows_left
-    const int x_rows_left = p.M - m0 - rb;
-    const int64_t rstride = (int64_t)RSTEP * Kb;
-    const int st_off = rb * BK + ((kc ^ (rb & 7)) << 4);  // swizzled LDS offset of this thread's chunk
-
-    uint4 rw[CW], rx[CX];
-    auto load_w = [&](int kt) {
-        const int64_t ko = (int64_t)kt * BK;
-        const bool kok = ko + kc * 16 < Kb;
+    const int wlast = nlim - n0 - 1, xlast = p.M - m0 - 1;
+    const int lchunk = (lane & 7) ^ ((lane >> 3) & 7);
+    const uint8_t* gptr[NI];
 #pragma unroll
-        for (int i = 0; i < CW; ++i) {
-            const int ii = SILU && i >= CW / 2 ? i - CW / 2 : i;
-            const uint8_t* base = SILU && i >= CW / 2 ? pwu : pw;
-            if (kok && ii * RSTEP < w_rows_left)
-                rw[i] = *reinterpret_cast<const uint4*>(base + ii * rstride + ko);
-            else
-                rw[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < NI; ++i) {
+        const int r = (wave * NI + i) * 8 + (lane >> 3);
+        const uint8_t* base;
+        int grow;
+        if (r < BN) {
+            const bool up = SILU && r >= BN / 2;
+            base = up ? p.W + (int64_t)(p.F + n0) * Kb : p.W + (int64_t)n0 * Kb;
+            grow = min(up ? r - BN / 2 : r, wlast);
+        } else {
+            base = p.X + (int64_t)m0 * Kb;
+            grow = min(r - BN, xlast);
         }
-    };
-    auto load_x = [&](int kt) {
-        const int64_t ko = (int64_t)kt * BK;
-        const bool kok = ko + kc * 16 < Kb;
-#pragma unroll
-        for (int i = 0; i < CX; ++i) {
-            if (kok && i * RSTEP < x_rows_left)
-                rx[i] = *reinterpret_cast<const uint4*>(px + i * rstride + ko);
-            else
-                rx[i] = make_uint4(0u, 0u, 0u, 0u);
-        }
-    };
-    auto store_w = [&](int buf) {
-        uint8_t* s = smem + buf * STAGE + st_off;
-#pragma unroll
-        for (int i = 0; i < CW; ++i) *reinterpret_cast<uint4*>(s + i * RSTEP * BK) = rw[i];
-    };
-    auto store_x = [&](int buf) {
-        uint8_t* s = smem + buf * STAGE + BN * BK + st_off;
-#pragma unroll
-        for (int i = 0; i < CX; ++i) *reinterpret_cast<uint4*>(s + i * RSTEP * BK) = rx[i];
+        gptr[i] = base + (int64_t)grow * Kb + (int64_t)kt0 * BK + lchunk * 16;
+    }
+    const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds_offset(smem) + wave * NI * 1024);
+    auto dma = [&](int stage, int i) __attribute__((always_inline)) {
+        lds_dma16(ldsw + (uint32_t)((stage % NB) * STAGE + i * 1024), gptr[i] + (int64_t)stage * BK);
     };
 
-    // ---- fragment read offsets: row (lane & 15) of a 16-row fragment, chunk 4*ks + (lane >> 4)
+    // ---- fragment reads: row (lane & 15) of a 16-row fragment, chunk 4 * ks + (lane >> 4)
     int wrow[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
@@ -164,8 +192,8 @@ gemm_kernel(KArgs p) {
     }
     const int xrow0 = BN + wm * FM * 16;
     const int lrow = (lane & 15) * BK;
-    const int lck0 = (((lane >> 4) + 0) ^ (lane & 7)) << 4;
-    const int lck1 = (((lane >> 4) + 4) ^ (lane & 7)) << 4;
+    const int lck0 = ((0 + (lane >> 4)) ^ (lane & 7)) << 4;
+    const int lck1 = ((4 + (lane >> 4)) ^ (lane & 7)) << 4;
 
     Acc acc[FN][FM];
 #pragma unroll
@@ -173,41 +201,56 @@ gemm_kernel(KArgs p) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = Acc{0, 0, 0, 0};
 
-    auto compute = [&](int buf, int ks) {
-        const uint8_t* s = smem + buf * STAGE + lrow + (ks ? lck1 : lck0);
-        uint4 a[FN], b[FM];
+    auto mma_group = [&](int g, const v4u& a, const v4u (&b)[FM]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) a[fn] = *reinterpret_cast<const uint4*>(s + wrow[fn] * BK);
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) b[fm] = *reinterpret_cast<const uint4*>(s + (xrow0 + fm * 16) * BK);
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma<BF16>(a[fn], b[fm], acc[fn][fm]);
+        for (int fm = 0; fm < FM; ++fm) {
+            if (g * FM + fm < NACC_A)
+                mfma<BF16, true>(acc[g][fm], a, b[fm]);
+            else
+                mfma<BF16, false>(acc[g][fm], a, b[fm]);
+        }
     };
 
-    if (kt0 < kt1) {
-        load_w(kt0);
-        load_x(kt0);
-        store_w(0);
-        store_x(0);
-        __syncthreads();
-        for (int kt = kt0; kt < kt1; ++kt) {
-            const int cur = (kt - kt0) & 1;
-            const bool more = kt + 1 < kt1;
-            if (more) {
-                load_w(kt + 1);
-                if constexpr (!PHASED) load_x(kt + 1);
-            }
-            compute(cur, 0);
-            if (more) {
-                store_w(cur ^ 1);
-                if constexpr (PHASED) load_x(kt + 1);
-            }
-            compute(cur, 1);
-            if (more) store_x(cur ^ 1);
+    // ---- main loop over stages j = 0 .. nk-1 (stage j in LDS buffer j % 2).
+    // Step j: wait for the LDS-DMA of stage j, barrier (publishes it; every wave is done with the
+    // other buffer), read the sub-step 0 fragments, then 2 x FN fenced groups of FM MFMAs: during
+    // sub-step 0 each group also reads one weight and one token fragment of sub-step 1 and issues
+    // LDS-DMAs of stage j+1 into the other buffer; sub-step 1 issues the remaining LDS-DMAs.
+    // Only accumulators are carried around the loop.
+    if (nk > 0) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) dma(0, i);
+        for (int j = 0; j < nk; ++j) {
+            wait_vmcnt<0>();
             __syncthreads();
+            const uint8_t* s = smem + (j % NB) * STAGE + lrow;
+            const bool more = j + 1 < nk;
+            v4u a0[FN], b0[FM], a1[FN], b1[FM];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) b0[fm] = *reinterpret_cast<const v4u*>(s + (xrow0 + fm * 16) * BK + lck0);
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) a0[fn] = *reinterpret_cast<const v4u*>(s + wrow[fn] * BK + lck0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int g = 0; g < FN; ++g) {
+                a1[g] = *reinterpret_cast<const v4u*>(s + wrow[g] * BK + lck1);
+                if (g < FM) b1[g] = *reinterpret_cast<const v4u*>(s + (xrow0 + g * 16) * BK + lck1);
+                if (more) {
+                    if (2 * g < NI) dma(j + 1, 2 * g);
+                    if (2 * g + 1 < NI) dma(j + 1, 2 * g + 1);
+                }
+                mma_group(g, a0[g], b0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int g = 0; g < FN; ++g) {
+                if (more && 2 * FN + g < NI) dma(j + 1, 2 * FN + g);
+                mma_group(g, a1[g], b1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
+        wait_vmcnt<0>();
+        mfma_drain();
     }
 
     // ---------------------------------------------------------------- epilogues
@@ -501,9 +544,9 @@ static KArgs make_kargs(const GemmArgs& a, const Plan& pl, int esize) {
     return k;
 }
 
-template <int FMN, bool BF16, int EPI, bool PHASED>
+template <int FMN, bool BF16, int EPI>
 static hipError_t go(const KArgs& k, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_kernel<2, 2, FMN, FMN, BF16, EPI, PHASED>), dim3(grid), dim3(256), 0, st, k);
+    hipLaunchKernelGGL((gemm_kernel<2, 2, FMN, FMN, BF16, EPI>), dim3(grid), dim3(256), 0, st, k);
     return hipGetLastError();
 }
 
@@ -512,26 +555,26 @@ hipError_t launch_gemm_i8(const GemmArgs& a, const Plan& pl, hipStream_t st) {
     const int epi = pl.split_k > 1 ? EPI_PARTIAL : a.epi;
     if (pl.tile == QDT_TILE_288) {
         switch (epi) {
-            case EPI_BIAS: return go<9, false, EPI_BIAS, true>(k, pl.grid, st);
-            case EPI_ACC: return go<9, false, EPI_ACC, true>(k, pl.grid, st);
-            case EPI_PARTIAL: return go<9, false, EPI_PARTIAL, true>(k, pl.grid, st);
+            case EPI_BIAS: return go<9, false, EPI_BIAS>(k, pl.grid, st);
+            case EPI_ACC: return go<9, false, EPI_ACC>(k, pl.grid, st);
+            case EPI_PARTIAL: return go<9, false, EPI_PARTIAL>(k, pl.grid, st);
             default: return hipErrorInvalidValue;
         }
     }
     switch (epi) {
-        case EPI_BIAS: return go<8, false, EPI_BIAS, false>(k, pl.grid, st);
-        case EPI_SILU: return go<8, false, EPI_SILU, false>(k, pl.grid, st);
-        case EPI_RMSNORM: return go<8, false, EPI_RMSNORM, false>(k, pl.grid, st);
-        case EPI_ACC: return go<8, false, EPI_ACC, false>(k, pl.grid, st);
-        case EPI_PARTIAL: return go<8, false, EPI_PARTIAL, false>(k, pl.grid, st);
+        case EPI_BIAS: return go<8, false, EPI_BIAS>(k, pl.grid, st);
+        case EPI_SILU: return go<8, false, EPI_SILU>(k, pl.grid, st);
+        case EPI_RMSNORM: return go<8, false, EPI_RMSNORM>(k, pl.grid, st);
+        case EPI_ACC: return go<8, false, EPI_ACC>(k, pl.grid, st);
+        case EPI_PARTIAL: return go<8, false, EPI_PARTIAL>(k, pl.grid, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, const Plan& pl, hipStream_t st) {
     KArgs k = make_kargs(a, pl, 2);
-    if (pl.tile == QDT_TILE_288) return go<9, true, EPI_F32BIAS, true>(k, pl.grid, st);
-    return go<8, true, EPI_F32BIAS, false>(k, pl.grid, st);
+    if (pl.tile == QDT_TILE_288) return go<9, true, EPI_F32BIAS>(k, pl.grid, st);
+    return go<8, true, EPI_F32BIAS>(k, pl.grid, st);
 }
 
 hipError_t launch_splitk_epilogue(const GemmArgs& a, int split_k, int epi, hipStream_t st) {

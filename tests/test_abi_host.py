@@ -73,6 +73,7 @@ def _lin(M=64, N=128, K=256, epi=0, params=None, Y=0x900000, ldy=None, ws=None, 
 
 def test_linear_validation():
     assert _lin(K=100) == qdt.QDT_ESHAPE
+    assert _lin(K=192) == qdt.QDT_ESHAPE                           # INT8 GEMM stages are 128 bytes of K
     assert _lin(N=120) == qdt.QDT_ESHAPE
     assert _lin(N=48, epi=1) == qdt.QDT_ESHAPE                     # SILU needs N % 32
     assert _lin(N=384, epi=2, params=None) == qdt.QDT_ESHAPE        # heads need N % 256
@@ -129,7 +130,7 @@ def test_planner_choices(M, N, K, epi, tile, split):
 
 def test_plan_for_honours_requests():
     p = qdt.linear_plan(600, 1024, 4096, "bias", tile=qdt.QDT_TILE_288, split_k=5)
-    assert p["tile_m"] == 288 and p["split_k"] == 5 and p["k_tiles"] == 32
+    assert p["tile_m"] == 288 and p["split_k"] == 5 and p["k_tiles"] == 32  # 128-byte K stages
     # a request that would leave an empty slice is rounded down
     p = qdt.linear_plan(600, 1024, 256, "bias", split_k=3)
     assert p["split_k"] == 2

@@ -15,8 +15,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, b);
 }
 
+// Two round-half-to-even conversions in one v_cvt_pk_bf16_f32; lo in bits 0..15.
+typedef float qdt_v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 qdt_v2bf __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    const qdt_v2bf r = __builtin_convertvector((qdt_v2f){lo, hi}, qdt_v2bf);
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 // Dequantization + bias of one accumulator: fmaf((float)acc, sx * sw, b).

@@ -95,6 +95,30 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* gptr) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(gptr)
                  : "memory", "m0");
 }
+// LDS-DMA of one dword per lane (global_load_lds_dword): lane l writes LDS m0 + 4 l.
+__device__ __forceinline__ void lds_dma4(uint32_t lds_addr, const void* gptr) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr), "v"(gptr)
+                 : "memory", "m0");
+}
+// Same, addressed as a 64-bit scalar base plus a 32-bit per-lane offset, with M0 already set;
+// sets M0 to the LDS address of the next LDS-DMA afterwards, so the MFMAs issued in between
+// cover the M0 -> LDS-DMA hazard.  The compiler does not use M0 on gfx950 (LDS instructions do
+// not read it), so keeping it live between statements is safe.
+__device__ __forceinline__ void lds_dma16_next(uint32_t voff, const void* sbase, uint32_t next_lds) {
+    asm volatile("global_load_lds_dwordx4 %0, %1\n\ts_mov_b32 m0, %2" ::"v"(voff), "s"(sbase), "s"(next_lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void set_m0(uint32_t lds_addr) { asm volatile("s_mov_b32 m0, %0" ::"s"(lds_addr) : "m0"); }
+__device__ __forceinline__ void lds_dma16_s(uint32_t lds_addr, uint32_t voff, const void* sbase) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<T*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -120,13 +144,25 @@ gemm_kernel(KArgs p) {
     constexpr bool SILU = EPI == EPI_SILU;
     static_assert(NBLK % NW == 0, "whole LDS blocks per wave");
     static_assert(BN % 8 == 0 && (!SILU || ((BN / 2) % 8 == 0 && FN % 2 == 0)), "blocks never straddle");
-    static_assert(FM <= FN && NI <= 2 * FN, "reads and LDS-DMAs fit in the fragment groups");
+    constexpr int SP = 4;                  // MFMA slots between consecutive LDS-DMAs / reads
+    static_assert(NI * SP <= FN * FM && (FN + FM) * SP <= FN * FM, "LDS-DMAs and reads fit between the MFMAs of a sub-step");
     using Acc = typename AccT<BF16>::type;
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * STAGE];
     __shared__ float red[EPI == EPI_RMSNORM ? WN * BM : 1];
+    // Epilogue parameters staged in LDS (dwords, each array padded to whole 64-lane DMA chunks):
+    // w_scale per tile weight row, x_scale per tile token row, bias per weight row (bf16 pairs),
+    // gamma per head column (bf16 pairs).
+    constexpr bool HAS_SCALE = EPI == EPI_BIAS || EPI == EPI_SILU || EPI == EPI_RMSNORM;
+    constexpr bool HAS_BIAS = HAS_SCALE || EPI == EPI_F32BIAS;
+    constexpr int P_SW = 0, N_SW = HAS_SCALE ? (BN + 63) / 64 * 64 : 0;
+    constexpr int P_SX = P_SW + N_SW, N_SX = HAS_SCALE ? (BM + 63) / 64 * 64 : 0;
+    constexpr int P_B = P_SX + N_SX, N_B = HAS_BIAS ? (BN / 2 + 63) / 64 * 64 : 0;
+    constexpr int P_G = P_B + N_B, N_G = EPI == EPI_RMSNORM ? 128 : 0;
+    constexpr int NPRM = P_G + N_G;
+    __shared__ __attribute__((aligned(16))) uint32_t prm[NPRM > 0 ? NPRM : 1];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave % WN, wm = wave / WN;
 
     // ---- workgroup id -> (tile, K slice), contiguous per XCD
@@ -160,25 +196,64 @@ gemm_kernel(KArgs p) {
     const int nlim = SILU ? p.F : p.N;
     const int wlast = nlim - n0 - 1, xlast = p.M - m0 - 1;
     const int lchunk = (lane & 7) ^ ((lane >> 3) & 7);
-    const uint8_t* gptr[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int r = (wave * NI + i) * 8 + (lane >> 3);
-        const uint8_t* base;
-        int grow;
-        if (r < BN) {
-            const bool up = SILU && r >= BN / 2;
-            base = up ? p.W + (int64_t)(p.F + n0) * Kb : p.W + (int64_t)n0 * Kb;
-            grow = min(up ? r - BN / 2 : r, wlast);
-        } else {
-            base = p.X + (int64_t)m0 * Kb;
-            grow = min(r - BN, xlast);
-        }
-        gptr[i] = base + (int64_t)grow * Kb + (int64_t)kt0 * BK + lchunk * 16;
+    // The NI blocks of a wave lie in one operand region (weight rows; gate or up rows for SILU;
+    // token rows): one scalar base per wave, a 32-bit offset per lane and instruction.
+    static_assert(BN % (NI * 8) == 0 && (!SILU || (BN / 2) % (NI * 8) == 0), "one operand region per wave");
+    const int rw0 = wave * NI * 8;  // first tile row of the wave's blocks
+    const uint8_t* wbase;
+    int rlocal0, rlast;
+    if (rw0 < BN) {
+        const bool up = SILU && rw0 >= BN / 2;
+        wbase = p.W + (int64_t)((up ? p.F : 0) + n0) * Kb;
+        rlocal0 = up ? rw0 - BN / 2 : rw0;
+        rlast = wlast;
+    } else {
+        wbase = p.X + (int64_t)m0 * Kb;
+        rlocal0 = rw0 - BN;
+        rlast = xlast;
     }
+    wbase = uniform_ptr(wbase + (int64_t)kt0 * BK);
+    uint32_t voff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) voff[i] = (uint32_t)(min(rlocal0 + i * 8 + (lane >> 3), rlast) * Kb) + lchunk * 16;
     const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds_offset(smem) + wave * NI * 1024);
-    auto dma = [&](int stage, int i) __attribute__((always_inline)) {
-        lds_dma16(ldsw + (uint32_t)((stage % NB) * STAGE + i * 1024), gptr[i] + (int64_t)stage * BK);
+    // LDS-DMA instruction i of `stage` into LDS buffer `buf` (sets M0 itself)
+    auto dma = [&](int buf, int stage, int i) __attribute__((always_inline)) {
+        lds_dma16_s(ldsw + (uint32_t)(buf * STAGE + i * 1024), voff[i], wbase + (int64_t)stage * BK);
+    };
+
+    // Global weight row of tile weight row r (clamped like the operand rows).
+    auto wglobal = [&](int r) __attribute__((always_inline)) {
+        if constexpr (SILU) {
+            const bool up = r >= BN / 2;
+            return (up ? p.F : 0) + n0 + min(up ? r - BN / 2 : r, wlast);
+        } else {
+            return n0 + min(r, wlast);
+        }
+    };
+    // Parameter DMA chunk c (64 dwords of prm), issued by wave c % NW.
+    auto prm_dma = [&](int c) __attribute__((always_inline)) {
+        const int e = c * 64 + lane;
+        const void* src;
+        if (e < P_SX) {
+            src = p.sw + wglobal(min(e - P_SW, BN - 1));
+        } else if (e < P_B) {
+            src = p.sx + m0 + min(e - P_SX, min(BM - 1, xlast));
+        } else if (e < P_G) {
+            // pair of weight rows 2 q, 2 q + 1 (same half for SILU); clamping keeps pairs even
+            const int r = 2 * min(e - P_B, BN / 2 - 1);
+            int g;
+            if constexpr (SILU) {
+                const bool up = r >= BN / 2;
+                g = (up ? p.F : 0) + n0 + min(up ? r - BN / 2 : r, wlast - 1);
+            } else {
+                g = n0 + min(r, wlast - 1);
+            }
+            src = p.bias + g;
+        } else {
+            src = p.gamma + 2 * min(e - P_G, 127);
+        }
+        lds_dma4(__builtin_amdgcn_readfirstlane(lds_offset(prm) + c * 256), src);
     };
 
     // ---- fragment reads: row (lane & 15) of a 16-row fragment, chunk 4 * ks + (lane >> 4)
@@ -201,159 +276,222 @@ gemm_kernel(KArgs p) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = Acc{0, 0, 0, 0};
 
-    auto mma_group = [&](int g, const v4u& a, const v4u (&b)[FM]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            if (g * FM + fm < NACC_A)
-                mfma<BF16, true>(acc[g][fm], a, b[fm]);
-            else
-                mfma<BF16, false>(acc[g][fm], a, b[fm]);
-        }
+    // One MFMA of the group for weight fragment g, token fragment fm.
+    auto mma = [&](int g, int fm, const v4u& a, const v4u& b) __attribute__((always_inline)) {
+        if (g * FM + fm < NACC_A)
+            mfma<BF16, true>(acc[g][fm], a, b);
+        else
+            mfma<BF16, false>(acc[g][fm], a, b);
+    };
+    auto frag = [&](const uint8_t* s, int row, int lck) __attribute__((always_inline)) {
+        return *reinterpret_cast<const v4u*>(s + row * BK + lck);
     };
 
-    // ---- main loop over stages j = 0 .. nk-1 (stage j in LDS buffer j % 2).
-    // Step j: wait for the LDS-DMA of stage j, barrier (publishes it; every wave is done with the
-    // other buffer), read the sub-step 0 fragments, then 2 x FN fenced groups of FM MFMAs: during
-    // sub-step 0 each group also reads one weight and one token fragment of sub-step 1 and issues
-    // LDS-DMAs of stage j+1 into the other buffer; sub-step 1 issues the remaining LDS-DMAs.
-    // Only accumulators are carried around the loop.
-    if (nk > 0) {
+    // ---- main loop over stages j = 0 .. nk-1 (stage j in LDS buffer j % 2), two MFMA K steps
+    // (sub-steps) per stage.  The barrier sits between the sub-steps: when a wave reaches it, its
+    // own LDS-DMAs of stage j+1 have landed (vmcnt 0) and its reads of stage j are complete (the
+    // sub-step 1 fragments are in registers).  After it, stage j+1 is readable and buffer j % 2
+    // is free, so sub-step 1 issues the LDS-DMAs of stage j+2 into buffer j % 2 and reads the
+    // sub-step 0 fragments of stage j+1, while sub-step 0 reads the sub-step 1 fragments of its
+    // own stage.  Every LDS read and LDS-DMA is issued between two MFMAs, so a wave never waits
+    // on LDS latency after a barrier.  Past the last stage, loads are clamped to stage nk-1 (their
+    // data is never used), which keeps the loop free of branches.
+    // Parameter chunks go first, so the prologue's wait for stage 0 covers them.
 #pragma unroll
-        for (int i = 0; i < NI; ++i) dma(0, i);
+    for (int c = 0; c < NPRM / 64; ++c) {
+        const bool is_bias = c * 64 >= P_B && c * 64 < P_G;
+        if (c % NW == wave && (!is_bias || p.bias != nullptr)) prm_dma(c);
+    }
+    if (nk > 0) {
+        v4u a0[FN], b0[FM], a1[FN], b1[FM];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) dma(0, 0, i);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) dma(1, min(1, nk - 1), i);
+        wait_vmcnt<NI>();
+        __syncthreads();
+        {
+            const uint8_t* s = smem + lrow;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) a0[fn] = frag(s, wrow[fn], lck0);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) b0[fm] = frag(s, xrow0 + fm * 16, lck0);
+        }
         for (int j = 0; j < nk; ++j) {
+            const uint8_t* s = smem + (j % NB) * STAGE + lrow;
+            const uint8_t* sn = smem + ((j + 1) % NB) * STAGE + lrow;
+            const int jd = min(j + 2, nk - 1);
+            // sub-step 0: every SP-th slot reads b1[0..FM-1], then a1[0..FN-1]
+#pragma unroll
+            for (int g = 0; g < FN; ++g) {
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    mma(g, fm, a0[g], b0[fm]);
+                    const int k = g * FM + fm, q = k / SP;
+                    if (k % SP == 0 && q < FM)
+                        b1[q] = frag(s, xrow0 + q * 16, lck1);
+                    else if (k % SP == 0 && q < FM + FN)
+                        a1[q - FM] = frag(s, wrow[q - FM], lck1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
             wait_vmcnt<0>();
             __syncthreads();
-            const uint8_t* s = smem + (j % NB) * STAGE + lrow;
-            const bool more = j + 1 < nk;
-            v4u a0[FN], b0[FM], a1[FN], b1[FM];
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) b0[fm] = *reinterpret_cast<const v4u*>(s + (xrow0 + fm * 16) * BK + lck0);
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) a0[fn] = *reinterpret_cast<const v4u*>(s + wrow[fn] * BK + lck0);
-            __builtin_amdgcn_sched_barrier(0);
+            // sub-step 1: slot SP q issues LDS-DMA q of stage j+2 (and points M0 at LDS-DMA q+1);
+            // slot SP q + SP/2 reads b0[q] / a0[q - FM] of stage j+1
+            const uint32_t ldsd = ldsw + (uint32_t)((j % NB) * STAGE);
+            const uint8_t* sbase = wbase + (int64_t)jd * BK;
+            set_m0(ldsd);
 #pragma unroll
             for (int g = 0; g < FN; ++g) {
-                a1[g] = *reinterpret_cast<const v4u*>(s + wrow[g] * BK + lck1);
-                if (g < FM) b1[g] = *reinterpret_cast<const v4u*>(s + (xrow0 + g * 16) * BK + lck1);
-                if (more) {
-                    if (2 * g < NI) dma(j + 1, 2 * g);
-                    if (2 * g + 1 < NI) dma(j + 1, 2 * g + 1);
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    mma(g, fm, a1[g], b1[fm]);
+                    const int k = g * FM + fm, q = k / SP;
+                    if (k % SP == 0 && q < NI)
+                        lds_dma16_next(voff[q], sbase, ldsd + (uint32_t)((q + 1) * 1024));
+                    else if (k % SP == SP / 2 && q < FM)
+                        b0[q] = frag(sn, xrow0 + q * 16, lck0);
+                    else if (k % SP == SP / 2 && q < FM + FN)
+                        a0[q - FM] = frag(sn, wrow[q - FM], lck0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                mma_group(g, a0[g], b0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int g = 0; g < FN; ++g) {
-                if (more && 2 * FN + g < NI) dma(j + 1, 2 * FN + g);
-                mma_group(g, a1[g], b1);
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
         wait_vmcnt<0>();
         mfma_drain();
+    } else {
+        wait_vmcnt<0>();
+        __syncthreads();
     }
 
     // ---------------------------------------------------------------- epilogues
-    const int mrow0 = m0 + wm * FM * 16 + (lane & 15);  // + fm * 16
-    const int ncol0 = wn * (SILU ? FN / 2 : FN) * 16 + 4 * (lane >> 4);  // + n0 + fn * 16
+    // Staged parameters of tile weight rows rl .. rl+3 and tile token row.
+    auto prm_sw4 = [&](int rl) __attribute__((always_inline)) { return *reinterpret_cast<const float4*>(&prm[P_SW + rl]); };
+    auto prm_b4 = [&](int rl, float (&b)[4]) __attribute__((always_inline)) {
+        if (p.bias) {
+            const uint2 bb = *reinterpret_cast<const uint2*>(&prm[P_B + rl / 2]);
+            b[0] = bf16_to_f32(bb.x & 0xFFFFu); b[1] = bf16_to_f32(bb.x >> 16);
+            b[2] = bf16_to_f32(bb.y & 0xFFFFu); b[3] = bf16_to_f32(bb.y >> 16);
+        } else {
+            b[0] = b[1] = b[2] = b[3] = 0.0f;
+        }
+    };
+    auto prm_sx = [&](int rt) __attribute__((always_inline)) { return __uint_as_float(prm[P_SX + rt]); };
+    const int ncol0 = wn * (SILU ? FN / 2 : FN) * 16 + 4 * (lane >> 4);  // + fn * 16: tile weight row
+
+    // ---- output through LDS.  Per 16-row strip (one fm) a wave writes its fragments to a private
+    // LDS strip in row-major order and reads them back 16 bytes per lane, so each global store
+    // writes whole row segments instead of 16 rows x 32 bytes.  The stage buffers are reused
+    // (after a barrier: other waves may still read the last stage); two strips per wave alternate.
+    constexpr int NF = SILU ? FN / 2 : FN;                               // output fragments per row
+    constexpr int ES = (EPI == EPI_ACC || EPI == EPI_PARTIAL) ? 4 : 2;   // output element bytes
+    constexpr int CW = NF * 16 * ES, RS = CW + 16, CPR = CW / 16, NCH = 16 * CPR;
+    static_assert(NW * 2 * 16 * RS <= NB * STAGE, "output strips fit in the stage buffers");
+    __syncthreads();
+    uint8_t* Yb;
+    int64_t ldb;
+    int ncols;
+    if constexpr (EPI == EPI_PARTIAL) {
+        Yb = reinterpret_cast<uint8_t*>(p.ws + (int64_t)split * p.M * p.N);
+        ldb = (int64_t)p.N * 4;
+        ncols = p.N;
+    } else {
+        Yb = reinterpret_cast<uint8_t*>(p.Y);
+        ldb = p.ldy * ES;
+        ncols = SILU ? p.F : p.N;
+    }
+    const int colw = n0 + wn * NF * 16;  // first output column of the wave
+    // Read-back chunk it of a lane: strip row r_it, 16-byte column chunk cc_it (the same in every
+    // strip, so the offsets are computed once).
+    constexpr int NIT = (NCH + 63) / 64;
+    int rr[NIT], lofs[NIT];
+    int64_t gofs[NIT];
+    bool ok[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int c = it * 64 + lane, r = c / CPR, cc = c % CPR, n = colw + cc * (16 / ES);
+        rr[it] = r;
+        lofs[it] = r * RS + cc * 16;
+        gofs[it] = (int64_t)r * ldb + (int64_t)n * ES;
+        ok[it] = (NCH % 64 == 0 || c < NCH) && n < ncols;
+    }
+    // frag_out(fn) gives the lane's 4 outputs of fragment (fn, fm): row lane & 15 of the strip,
+    // columns fn * 16 + 4 * (lane >> 4) .. + 3.
+    auto put_strip = [&](int fm, auto&& frag_out) __attribute__((always_inline)) {
+        uint8_t* st = smem + (wave * 2 + (fm & 1)) * 16 * RS;
+#pragma unroll
+        for (int fn = 0; fn < NF; ++fn) {
+            const auto v = frag_out(fn);
+            *reinterpret_cast<std::remove_const_t<decltype(v)>*>(st + (lane & 15) * RS + (fn * 16 + 4 * (lane >> 4)) * ES) = v;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int r0 = m0 + wm * FM * 16 + fm * 16;
+        uint8_t* yrow = Yb + (int64_t)r0 * ldb;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const v4u v = *reinterpret_cast<const v4u*>(st + lofs[it]);
+            if (ok[it] && r0 + rr[it] < p.M) *reinterpret_cast<v4u*>(yrow + gofs[it]) = v;
+        }
+    };
+    auto prm_sxf = [&](int fm) __attribute__((always_inline)) { return prm_sx(wm * FM * 16 + fm * 16 + (lane & 15)); };
 
     if constexpr (EPI == EPI_ACC || EPI == EPI_PARTIAL) {
-        int32_t* out = EPI == EPI_ACC ? reinterpret_cast<int32_t*>(p.Y) : p.ws + (int64_t)split * p.M * p.N;
-        const int64_t ld = EPI == EPI_ACC ? p.ldy : p.N;
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int n = n0 + ncol0 + fn * 16;
-            if (n >= p.N) continue;
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int m = mrow0 + fm * 16;
-                if (m < p.M) *reinterpret_cast<v4i*>(out + (int64_t)m * ld + n) = acc[fn][fm];
-            }
-        }
+        for (int fm = 0; fm < FM; ++fm) put_strip(fm, [&](int fn) { return acc[fn][fm]; });
     } else if constexpr (EPI == EPI_F32BIAS) {
-        uint16_t* Y = reinterpret_cast<uint16_t*>(p.Y);
+        float b[FN][4];
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int n = n0 + ncol0 + fn * 16;
-            if (n >= p.N) continue;
-            float b[4] = {0.f, 0.f, 0.f, 0.f};
-            if (p.bias) {
-                uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
-                b[0] = bf16_to_f32(bb.x & 0xFFFFu); b[1] = bf16_to_f32(bb.x >> 16);
-                b[2] = bf16_to_f32(bb.y & 0xFFFFu); b[3] = bf16_to_f32(bb.y >> 16);
-            }
+        for (int fn = 0; fn < FN; ++fn) prm_b4(ncol0 + fn * 16, b[fn]);
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int m = mrow0 + fm * 16;
-                if (m >= p.M) continue;
-                float y[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) y[r] = p.bias ? (float)acc[fn][fm][r] + b[r] : (float)acc[fn][fm][r];
-                *reinterpret_cast<uint2*>(Y + (int64_t)m * p.ldy + n) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-            }
-        }
+        for (int fm = 0; fm < FM; ++fm)
+            put_strip(fm, [&](int fn) {
+                const Acc& a = acc[fn][fm];
+                return make_uint2(pack_bf16x2((float)a[0] + b[fn][0], (float)a[1] + b[fn][1]),
+                                  pack_bf16x2((float)a[2] + b[fn][2], (float)a[3] + b[fn][3]));
+            });
     } else if constexpr (EPI == EPI_BIAS) {
-        uint16_t* Y = reinterpret_cast<uint16_t*>(p.Y);
-        float sxv[FM];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) sxv[fm] = mrow0 + fm * 16 < p.M ? p.sx[mrow0 + fm * 16] : 0.0f;
+        float4 sw[FN];
+        float b[FN][4];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            const int n = n0 + ncol0 + fn * 16;
-            if (n >= p.N) continue;
-            const float4 sw = *reinterpret_cast<const float4*>(p.sw + n);
-            float b[4] = {0.f, 0.f, 0.f, 0.f};
-            if (p.bias) {
-                uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
-                b[0] = bf16_to_f32(bb.x & 0xFFFFu); b[1] = bf16_to_f32(bb.x >> 16);
-                b[2] = bf16_to_f32(bb.y & 0xFFFFu); b[3] = bf16_to_f32(bb.y >> 16);
-            }
+            sw[fn] = prm_sw4(ncol0 + fn * 16);
+            prm_b4(ncol0 + fn * 16, b[fn]);
+        }
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int m = mrow0 + fm * 16;
-                if (m >= p.M) continue;
-                const float y0 = dequant(acc[fn][fm][0], sxv[fm], sw.x, b[0]);
-                const float y1 = dequant(acc[fn][fm][1], sxv[fm], sw.y, b[1]);
-                const float y2 = dequant(acc[fn][fm][2], sxv[fm], sw.z, b[2]);
-                const float y3 = dequant(acc[fn][fm][3], sxv[fm], sw.w, b[3]);
-                *reinterpret_cast<uint2*>(Y + (int64_t)m * p.ldy + n) = make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
-            }
+        for (int fm = 0; fm < FM; ++fm) {
+            const float sx = prm_sxf(fm);
+            put_strip(fm, [&](int fn) {
+                const Acc& a = acc[fn][fm];
+                return make_uint2(pack_bf16x2(dequant(a[0], sx, sw[fn].x, b[fn][0]), dequant(a[1], sx, sw[fn].y, b[fn][1])),
+                                  pack_bf16x2(dequant(a[2], sx, sw[fn].z, b[fn][2]), dequant(a[3], sx, sw[fn].w, b[fn][3])));
+            });
         }
     } else if constexpr (EPI == EPI_SILU) {
-        uint16_t* Y = reinterpret_cast<uint16_t*>(p.Y);
-        float sxv[FM];
+        // gate fragment fn pairs with up fragment fn + FN / 2 (tile weight rows BN / 2 further)
+        float swg[NF][4], swu[NF][4], bg[NF][4], bu[NF][4];
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) sxv[fm] = mrow0 + fm * 16 < p.M ? p.sx[mrow0 + fm * 16] : 0.0f;
+        for (int fn = 0; fn < NF; ++fn) {
+            const int rl = ncol0 + fn * 16;
+            const float4 g4 = prm_sw4(rl), u4 = prm_sw4(BN / 2 + rl);
+            swg[fn][0] = g4.x; swg[fn][1] = g4.y; swg[fn][2] = g4.z; swg[fn][3] = g4.w;
+            swu[fn][0] = u4.x; swu[fn][1] = u4.y; swu[fn][2] = u4.z; swu[fn][3] = u4.w;
+            prm_b4(rl, bg[fn]);
+            prm_b4(BN / 2 + rl, bu[fn]);
+        }
 #pragma unroll
-        for (int fn = 0; fn < FN / 2; ++fn) {
-            const int f = n0 + ncol0 + fn * 16;
-            if (f >= p.F) continue;
-            const float4 swg = *reinterpret_cast<const float4*>(p.sw + f);
-            const float4 swu = *reinterpret_cast<const float4*>(p.sw + p.F + f);
-            float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
-            if (p.bias) {
-                uint2 g2 = *reinterpret_cast<const uint2*>(p.bias + f);
-                uint2 u2 = *reinterpret_cast<const uint2*>(p.bias + p.F + f);
-                bg[0] = bf16_to_f32(g2.x & 0xFFFFu); bg[1] = bf16_to_f32(g2.x >> 16);
-                bg[2] = bf16_to_f32(g2.y & 0xFFFFu); bg[3] = bf16_to_f32(g2.y >> 16);
-                bu[0] = bf16_to_f32(u2.x & 0xFFFFu); bu[1] = bf16_to_f32(u2.x >> 16);
-                bu[2] = bf16_to_f32(u2.y & 0xFFFFu); bu[3] = bf16_to_f32(u2.y >> 16);
-            }
-            const float swgv[4] = {swg.x, swg.y, swg.z, swg.w};
-            const float swuv[4] = {swu.x, swu.y, swu.z, swu.w};
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int m = mrow0 + fm * 16;
-                if (m >= p.M) continue;
+        for (int fm = 0; fm < FM; ++fm) {
+            const float sx = prm_sxf(fm);
+            put_strip(fm, [&](int fn) {
                 float y[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float g = dequant(acc[fn][fm][r], sxv[fm], swgv[r], bg[r]);
-                    const float u = dequant(acc[fn + FN / 2][fm][r], sxv[fm], swuv[r], bu[r]);
+                    const float g = dequant(acc[fn][fm][r], sx, swg[fn][r], bg[fn][r]);
+                    const float u = dequant(acc[fn + NF][fm][r], sx, swu[fn][r], bu[fn][r]);
                     y[r] = silu_gate(g, u);
                 }
-                *reinterpret_cast<uint2*>(Y + (int64_t)m * p.ldy + f) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-            }
+                return make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+            });
         }
     } else if constexpr (EPI == EPI_RMSNORM) {
         // The workgroup's BN = 256 columns are exactly one head; each wave holds FN*16 of
@@ -361,26 +499,18 @@ gemm_kernel(KArgs p) {
         // fragments, across the 4 lane groups with shuffles, across waves through LDS, in a
         // fixed order.
         static_assert(BN == 256, "one head per tile");
-        uint16_t* Y = reinterpret_cast<uint16_t*>(p.Y);
         float sxv[FM], ss[FM];
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-            sxv[fm] = mrow0 + fm * 16 < p.M ? p.sx[mrow0 + fm * 16] : 0.0f;
+            sxv[fm] = prm_sxf(fm);
             ss[fm] = 0.0f;
         }
         float swv[FN][4], bv[FN][4];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            const int n = n0 + ncol0 + fn * 16;
-            const float4 sw = *reinterpret_cast<const float4*>(p.sw + n);
+            const float4 sw = prm_sw4(ncol0 + fn * 16);
             swv[fn][0] = sw.x; swv[fn][1] = sw.y; swv[fn][2] = sw.z; swv[fn][3] = sw.w;
-            if (p.bias) {
-                uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
-                bv[fn][0] = bf16_to_f32(bb.x & 0xFFFFu); bv[fn][1] = bf16_to_f32(bb.x >> 16);
-                bv[fn][2] = bf16_to_f32(bb.y & 0xFFFFu); bv[fn][3] = bf16_to_f32(bb.y >> 16);
-            } else {
-                bv[fn][0] = bv[fn][1] = bv[fn][2] = bv[fn][3] = 0.0f;
-            }
+            prm_b4(ncol0 + fn * 16, bv[fn]);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -406,26 +536,24 @@ gemm_kernel(KArgs p) {
             const float ms = tot / (float)p.head_dim;
             rinv[fm] = 1.0f / sqrtf(ms + p.eps);
         }
+        float g[FN][4];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            const int d = ncol0 + fn * 16;  // column within the head
-            const int n = n0 + d;
-            uint2 gg = *reinterpret_cast<const uint2*>(p.gamma + d);
-            const float g[4] = {bf16_to_f32(gg.x & 0xFFFFu), bf16_to_f32(gg.x >> 16), bf16_to_f32(gg.y & 0xFFFFu),
-                                bf16_to_f32(gg.y >> 16)};
+            const uint2 gg = *reinterpret_cast<const uint2*>(&prm[P_G + (ncol0 + fn * 16) / 2]);  // column within the head
+            g[fn][0] = bf16_to_f32(gg.x & 0xFFFFu); g[fn][1] = bf16_to_f32(gg.x >> 16);
+            g[fn][2] = bf16_to_f32(gg.y & 0xFFFFu); g[fn][3] = bf16_to_f32(gg.y >> 16);
+        }
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int m = mrow0 + fm * 16;
-                if (m >= p.M) continue;
+        for (int fm = 0; fm < FM; ++fm)
+            put_strip(fm, [&](int fn) {
                 float o[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float y = dequant(acc[fn][fm][r], sxv[fm], swv[fn][r], bv[fn][r]);
-                    o[r] = (y * rinv[fm]) * g[r];
+                    o[r] = (y * rinv[fm]) * g[fn][r];
                 }
-                *reinterpret_cast<uint2*>(Y + (int64_t)m * p.ldy + n) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-            }
-        }
+                return make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+            });
     }
 }
 

@@ -100,107 +100,183 @@ hipError_t launch_lambda(const float* s, float* lam, float* inv, int64_t K, floa
 }
 
 // ---------------------------------------------------------------------------- per-row INT8
-// Exact rint(v / scale) from a reciprocal: with rcp = RN(1/scale) and t = RN(v * rcp),
-// |t - v/scale| < 2^-16 whenever |v/scale| <= 127 (two roundings of relative size 2^-24).
-// If t is farther than 2^-15 from every half-integer, v/scale and its correctly rounded fp32
-// quotient lie on the same side of the same half-integers as t, so rint(t) equals
-// rint(RN(v / scale)).  Otherwise (probability about 6e-5 per element) the element takes the
-// correctly rounded division.  Rows whose scale is below FLT_MIN (1/scale would overflow)
-// always take the division.
-__device__ __forceinline__ int quant_one(float v, float sc, float rcp, bool fast) {
-    float q;
-    float t = v * rcp;
-    float r = rintf(t);
-    if (fast && fabsf(t - r) < 0.5f - 3.0517578125e-05f) {
-        q = r;
-    } else {
-        q = rintf(v / sc);
-    }
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
+// q = clamp(rint(v / scale), -127, 127) with scale = max|v| / 127, bit-exact, without a
+// division per element:
+//   * rcp = RN(1 / scale), t = RN(v * rcp).  For |v / scale| <= 127 the two roundings keep
+//     |t - v / scale| < 2^-16.
+//   * m = RN(t + 1.5 * 2^23) rounds t to the nearest integer (ties to even): for |t| < 2^22 the
+//     sum's ulp is 1, and the integer sits in the low mantissa bits, so the low byte of m is the
+//     two's-complement int8 of rint(t) (|t| <= 127.001 here, so no clamp is needed).
+//   * If t is at least 2^-15 away from every half-integer, v / scale and RN(v / scale) lie on the
+//     same side of the same half-integers as t, so rint(t) == rint(RN(v / scale)).  The test is
+//     |t - rint(t)| < 0.5 - 2^-15.  Chunks where some element fails it (probability about 6e-5
+//     per element) are redone with the correctly rounded division, as are rows whose scale is
+//     below FLT_MIN (1 / scale overflows).
+constexpr float kRoundMagic = 12582912.0f;          // 1.5 * 2^23
+constexpr float kNearTie = 0.5f - 3.0517578125e-05f;  // 0.5 - 2^-15
+
+__device__ __forceinline__ int quant_exact(float v, float sc) {
+    const float q = fminf(fmaxf(rintf(v / sc), -127.0f), 127.0f);
     return (int)q;
 }
 
-__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
-    return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
-           ((uint32_t)(d & 0xFF) << 24);
+// bytes 0 of a, b, c, d -> one dword (a in byte 0)
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
-// WPR waves per row, C chunks of 8 elements per lane.  WPR == 1: 4 rows per 256-thread block.
+// One row per wave (WPR == 1, 4 waves per block) or per block of WPR waves; C chunks of 8
+// consecutive elements per lane (chunk index lane + 64 c within the row, or thread + 64 WPR c).
+// Rows are grid-strided.  With WPR == 1 (K <= 8192) the column multipliers are staged in LDS
+// once per block and shared by the rows of its 4 waves; larger K reads them per row (L2 hits).
+constexpr int kQuantMaxLdsK = 8192;
+
 template <int WPR, int C>
 __global__ __launch_bounds__(WPR == 1 ? 256 : WPR * 64) void quant_rows_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, const float* __restrict__ colmul, int64_t M, int64_t K,
     int8_t* __restrict__ Q, float* __restrict__ scale) {
     constexpr int NT = WPR * 64;
-    __shared__ float red[WPR > 1 ? WPR : 1];
+    constexpr bool LDSMUL = WPR == 1;
+    __shared__ float red[2][WPR > 1 ? WPR : 1];
+    extern __shared__ __attribute__((aligned(16))) float smul[];  // K floats when LDSMUL and colmul
     const int lane = threadIdx.x & 63;
-    const int64_t row = WPR == 1 ? (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6) : (int64_t)blockIdx.x;
     const int t = WPR == 1 ? lane : (int)threadIdx.x;
-    if (WPR == 1 && row >= M) return;
-    const uint16_t* x = X + row * ldx;
+    // the row is uniform per wave (WPR == 1) or per block
+    const int64_t row0 = WPR == 1 ? (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)
+                                  : (int64_t)blockIdx.x;
+    const int64_t rstep = WPR == 1 ? (int64_t)gridDim.x * 4 : (int64_t)gridDim.x;
     const int64_t nch = K >> 3;
+    if (LDSMUL && colmul) {
+        for (int64_t j = threadIdx.x; j < nch * 2; j += blockDim.x)
+            *reinterpret_cast<float4*>(smul + j * 4) = *reinterpret_cast<const float4*>(colmul + j * 4);
+        __syncthreads();
+    }
+    // multipliers of chunk j (8 columns)
+    auto load_mul = [&](int64_t j, float (&mm)[8]) __attribute__((always_inline)) {
+        const float* src = LDSMUL ? smul + j * 8 : colmul + j * 8;
+        const float4 m0 = *reinterpret_cast<const float4*>(src);
+        const float4 m1 = *reinterpret_cast<const float4*>(src + 4);
+        mm[0] = m0.x; mm[1] = m0.y; mm[2] = m0.z; mm[3] = m0.w;
+        mm[4] = m1.x; mm[5] = m1.y; mm[6] = m1.z; mm[7] = m1.w;
+    };
 
-    float v[C][8];
-    float amax = 0.0f;
+    int parity = 0;
+    for (int64_t row = row0; row < M; row += rstep, parity ^= 1) {
+        const uint16_t* x = X + row * ldx;
+        uint4 raw[C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-        const int64_t j = t + (int64_t)c * NT;
-        if (j < nch) {
-            uint4 raw = *reinterpret_cast<const uint4*>(x + j * 8);
-            uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        for (int c = 0; c < C; ++c) {
+            const int64_t j = t + (int64_t)c * NT;
+            raw[c] = j < nch ? *reinterpret_cast<const uint4*>(x + j * 8) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        // v = bf16 element * multiplier; chunk c, computed again in the second pass when the
+        // row does not fit in registers as fp32 (C > 12)
+        auto chunk_vals = [&](int c, float (&vc)[8]) __attribute__((always_inline)) {
+            const uint32_t w[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                v[c][2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
-                v[c][2 * e + 1] = bf16_to_f32(w[e] >> 16);
+                vc[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
+                vc[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
             }
-            if (colmul) {
-                float4 m0 = *reinterpret_cast<const float4*>(colmul + j * 8);
-                float4 m1 = *reinterpret_cast<const float4*>(colmul + j * 8 + 4);
-                v[c][0] *= m0.x; v[c][1] *= m0.y; v[c][2] *= m0.z; v[c][3] *= m0.w;
-                v[c][4] *= m1.x; v[c][5] *= m1.y; v[c][6] *= m1.z; v[c][7] *= m1.w;
-            }
+            const int64_t j = t + (int64_t)c * NT;
+            if (colmul && j < nch) {
+                float mm[8];
+                load_mul(j, mm);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[c][e]));
+                for (int e = 0; e < 8; ++e) vc[e] *= mm[e];
+            }
+        };
+        constexpr bool KEEP = C <= 12;
+        float v[KEEP ? C : 1][8];
+        float amax = 0.0f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            float vc[8];
+            chunk_vals(c, vc);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                amax = fmaxf(amax, fabsf(vc[e]));
+                if constexpr (KEEP) v[c][e] = vc[e];
+            }
         }
-    }
-    amax = wave_max(amax);
-    if (WPR > 1) {
-        if (lane == 0) red[threadIdx.x >> 6] = amax;
-        __syncthreads();
-        amax = red[0];
+        amax = wave_max(amax);
+        if (WPR > 1) {
+            // double-buffered across rows: a wave may start the next row while others still
+            // read this row's slot
+            if (lane == 0) red[parity][threadIdx.x >> 6] = amax;
+            __syncthreads();
+            amax = red[parity][0];
 #pragma unroll
-        for (int w = 1; w < WPR; ++w) amax = fmaxf(amax, red[w]);
-    }
-    const float sc = amax / 127.0f;  // correctly rounded; 0 for an all-zero row
-    if (t == 0) scale[row] = sc;
-    const bool fast = sc >= 1.17549435e-38f;
-    const float rcp = fast ? 1.0f / sc : 0.0f;
-    int8_t* q = Q + row * K;
+            for (int w = 1; w < WPR; ++w) amax = fmaxf(amax, red[parity][w]);
+        }
+        const float sc = amax / 127.0f;  // correctly rounded; 0 for an all-zero row
+        if (t == 0) scale[row] = sc;
+        int8_t* q = Q + row * K;
+        if (amax == 0.0f) {
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-        const int64_t j = t + (int64_t)c * NT;
-        if (j < nch) {
-            uint2 out;
-            if (amax == 0.0f) {
-                out = make_uint2(0u, 0u);
-            } else {
-                int qi[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qi[e] = quant_one(v[c][e], sc, rcp, fast);
-                out.x = pack4(qi[0], qi[1], qi[2], qi[3]);
-                out.y = pack4(qi[4], qi[5], qi[6], qi[7]);
+            for (int c = 0; c < C; ++c) {
+                const int64_t j = t + (int64_t)c * NT;
+                if (j < nch) *reinterpret_cast<uint2*>(q + j * 8) = make_uint2(0u, 0u);
             }
-            *reinterpret_cast<uint2*>(q + j * 8) = out;
+            continue;
+        }
+        const bool fast = sc >= 1.17549435e-38f;
+        const float rcp = 1.0f / sc;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int64_t j = t + (int64_t)c * NT;
+            float vc[8];
+            if constexpr (KEEP) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vc[e] = v[c][e];
+            } else {
+                chunk_vals(c, vc);
+            }
+            uint32_t b[8];
+            bool near = !fast;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float tq = vc[e] * rcp;
+                const float m = tq + kRoundMagic;
+                const float r = m - kRoundMagic;
+                near |= fabsf(tq - r) >= kNearTie;
+                b[e] = __float_as_uint(m);
+            }
+            if (near) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) b[e] = (uint32_t)quant_exact(vc[e], sc);
+            }
+            if (j < nch)
+                *reinterpret_cast<uint2*>(q + j * 8) =
+                    make_uint2(pack_low_bytes(b[0], b[1], b[2], b[3]), pack_low_bytes(b[4], b[5], b[6], b[7]));
         }
     }
 }
 
+// Grid: at most as many blocks as can be resident at once (occupancy query); rows are
+// grid-strided over them.  More waves in flight measured faster than an even row split.
 template <int WPR, int C>
 static hipError_t launch_quant_cfg(const uint16_t* X, int64_t ldx, const float* colmul, int64_t M, int64_t K,
                                    int8_t* Q, float* scale, hipStream_t st) {
-    const int64_t blocks = WPR == 1 ? (M + 3) / 4 : M;
+    static_assert(WPR > 1 || C * 64 * 8 <= kQuantMaxLdsK, "column multipliers fit in LDS");
     const int threads = WPR == 1 ? 256 : WPR * 64;
-    hipLaunchKernelGGL((quant_rows_kernel<WPR, C>), dim3((unsigned)blocks), dim3(threads), 0, st, X, ldx, colmul, M,
-                       K, Q, scale);
+    const size_t lds = (WPR == 1 && colmul) ? (size_t)K * sizeof(float) : 0;
+    // cached per configuration, for the largest LDS request of the configuration (K = 512 C)
+    static int per_cu_cache[2] = {0, 0};
+    int& per_cu = per_cu_cache[lds ? 1 : 0];
+    if (per_cu == 0) {
+        int v = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, quant_rows_kernel<WPR, C>, threads,
+                                                                    lds ? (size_t)C * 512 * sizeof(float) : 0);
+        if (e != hipSuccess) return e;
+        per_cu = max(v, 1);
+    }
+    const int64_t units = WPR == 1 ? (M + 3) / 4 : M;  // blocks for one row per wave
+    const int64_t blocks = min(units, (int64_t)per_cu * kNumCU);
+    hipLaunchKernelGGL((quant_rows_kernel<WPR, C>), dim3((unsigned)blocks), dim3(threads), lds, st, X, ldx, colmul,
+                       M, K, Q, scale);
     return hipGetLastError();
 }
 

@@ -62,23 +62,28 @@ def to_dev(a):
     return torch.from_numpy(a).cuda()
 
 
+EVENT_EVERY = 10  # steps between event-bracketed steps (a timing event record costs ~5 us of stream time)
+
+
 def time_loop(fn_step, sets, steps, warmup):
-    """Wall time of `steps` steps (sync on both sides) + per-phase HIP event times."""
+    """Wall time of `steps` steps (sync on both sides) + per-phase HIP event times.
+
+    Every EVENT_EVERY-th step of the timed region records HIP events (on the stream the library
+    launches on) around its two launches; the others run without events."""
     import torch
-    st = torch.cuda.current_stream()
     for i in range(warmup):
         fn_step(sets[i % len(sets)], None)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    sampled = list(range(0, steps, EVENT_EVERY))
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        fn_step(sets[i % len(sets)], evs[i])
+        fn_step(sets[i % len(sets)], evs.get(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ph1 = [e[0].elapsed_time(e[1]) for e in evs]
-    ph2 = [e[1].elapsed_time(e[2]) for e in evs]
-    del st
+    ph1 = [evs[i][0].elapsed_time(evs[i][1]) for i in sampled]
+    ph2 = [evs[i][1].elapsed_time(evs[i][2]) for i in sampled]
     return (t1 - t0) * 1e3 / steps, ph1, ph2
 
 

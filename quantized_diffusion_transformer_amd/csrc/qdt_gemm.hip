@@ -159,7 +159,8 @@ gemm_kernel(KArgs p) {
     constexpr int P_SX = P_SW + N_SW, N_SX = HAS_SCALE ? (BM + 63) / 64 * 64 : 0;
     constexpr int P_B = P_SX + N_SX, N_B = HAS_BIAS ? (BN / 2 + 63) / 64 * 64 : 0;
     constexpr int P_G = P_B + N_B, N_G = EPI == EPI_RMSNORM ? 128 : 0;
-    constexpr int NPRM = P_G + N_G;
+    constexpr int P_BF = P_G + N_G, N_BF = HAS_BIAS ? (BN + 63) / 64 * 64 : 0;  // bias as fp32 (epilogue)
+    constexpr int NPRM = P_BF + N_BF;
     __shared__ __attribute__((aligned(16))) uint32_t prm[NPRM > 0 ? NPRM : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -298,7 +299,7 @@ gemm_kernel(KArgs p) {
     // data is never used), which keeps the loop free of branches.
     // Parameter chunks go first, so the prologue's wait for stage 0 covers them.
 #pragma unroll
-    for (int c = 0; c < NPRM / 64; ++c) {
+    for (int c = 0; c < P_BF / 64; ++c) {
         const bool is_bias = c * 64 >= P_B && c * 64 < P_G;
         if (c % NW == wave && (!is_bias || p.bias != nullptr)) prm_dma(c);
     }
@@ -369,13 +370,8 @@ gemm_kernel(KArgs p) {
     // Staged parameters of tile weight rows rl .. rl+3 and tile token row.
     auto prm_sw4 = [&](int rl) __attribute__((always_inline)) { return *reinterpret_cast<const float4*>(&prm[P_SW + rl]); };
     auto prm_b4 = [&](int rl, float (&b)[4]) __attribute__((always_inline)) {
-        if (p.bias) {
-            const uint2 bb = *reinterpret_cast<const uint2*>(&prm[P_B + rl / 2]);
-            b[0] = bf16_to_f32(bb.x & 0xFFFFu); b[1] = bf16_to_f32(bb.x >> 16);
-            b[2] = bf16_to_f32(bb.y & 0xFFFFu); b[3] = bf16_to_f32(bb.y >> 16);
-        } else {
-            b[0] = b[1] = b[2] = b[3] = 0.0f;
-        }
+        const float4 v = *reinterpret_cast<const float4*>(&prm[P_BF + rl]);
+        b[0] = v.x; b[1] = v.y; b[2] = v.z; b[3] = v.w;
     };
     auto prm_sx = [&](int rt) __attribute__((always_inline)) { return __uint_as_float(prm[P_SX + rt]); };
     const int ncol0 = wn * (SILU ? FN / 2 : FN) * 16 + 4 * (lane >> 4);  // + fn * 16: tile weight row
@@ -388,6 +384,17 @@ gemm_kernel(KArgs p) {
     constexpr int ES = (EPI == EPI_ACC || EPI == EPI_PARTIAL) ? 4 : 2;   // output element bytes
     constexpr int CW = NF * 16 * ES, RS = CW + 16, CPR = CW / 16, NCH = 16 * CPR;
     static_assert(NW * 2 * 16 * RS <= NB * STAGE, "output strips fit in the stage buffers");
+    if constexpr (HAS_BIAS) {
+        // bias of the tile's weight rows to fp32 (0 without bias), once
+        for (int r = tid; r < BN; r += NW * 64) {
+            float v = 0.0f;
+            if (p.bias) {
+                const uint32_t pr = prm[P_B + r / 2];
+                v = bf16_to_f32((r & 1) ? pr >> 16 : pr & 0xFFFFu);
+            }
+            prm[P_BF + r] = __float_as_uint(v);
+        }
+    }
     __syncthreads();
     uint8_t* Yb;
     int64_t ldb;
@@ -416,22 +423,40 @@ gemm_kernel(KArgs p) {
         gofs[it] = (int64_t)r * ldb + (int64_t)n * ES;
         ok[it] = (NCH % 64 == 0 || c < NCH) && n < ncols;
     }
-    // frag_out(fn) gives the lane's 4 outputs of fragment (fn, fm): row lane & 15 of the strip,
-    // columns fn * 16 + 4 * (lane >> 4) .. + 3.
+    // Strip fm: the lane's 4 outputs of fragment (fn, fm) (frag_out(fn)) go to row lane & 15 of the
+    // LDS strip, columns fn * 16 + 4 * (lane >> 4) .. + 3.  Strips alternate between two LDS
+    // buffers and are software-pipelined: strip fm is written, then strip fm - 1 is read back and
+    // stored.  The LDS executes one wave's instructions in order, so a read-back sees the same
+    // wave's earlier strip writes (and strip fm - 1 was written a whole strip of work earlier);
+    // strip fm + 1 overwrites strip fm - 1's buffer only after the stores that consumed its
+    // read-back.  The asm statements are compiler barriers that keep this order.
+    auto store_strip = [&](int fm) __attribute__((always_inline)) {
+        const uint8_t* st = smem + (wave * 2 + (fm & 1)) * 16 * RS;
+        uint8_t* yrow = Yb + (int64_t)(m0 + wm * FM * 16 + fm * 16) * ldb;
+        const int rows_left = p.M - (m0 + wm * FM * 16 + fm * 16);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const v4u v = *reinterpret_cast<const v4u*>(st + lofs[it]);
+            if (ok[it] && rr[it] < rows_left) *reinterpret_cast<v4u*>(yrow + gofs[it]) = v;
+        }
+    };
     auto put_strip = [&](int fm, auto&& frag_out) __attribute__((always_inline)) {
+        // one strip at a time: keeps the scheduler from hoisting every accumulator read (and
+        // spilling) ahead of the first store
+        __builtin_amdgcn_sched_barrier(0);
         uint8_t* st = smem + (wave * 2 + (fm & 1)) * 16 * RS;
 #pragma unroll
         for (int fn = 0; fn < NF; ++fn) {
             const auto v = frag_out(fn);
             *reinterpret_cast<std::remove_const_t<decltype(v)>*>(st + (lane & 15) * RS + (fn * 16 + 4 * (lane >> 4)) * ES) = v;
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        const int r0 = m0 + wm * FM * 16 + fm * 16;
-        uint8_t* yrow = Yb + (int64_t)r0 * ldb;
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const v4u v = *reinterpret_cast<const v4u*>(st + lofs[it]);
-            if (ok[it] && r0 + rr[it] < p.M) *reinterpret_cast<v4u*>(yrow + gofs[it]) = v;
+        if (fm > 0) {
+            asm volatile("" ::: "memory");
+            store_strip(fm - 1);
+        }
+        if (fm == FM - 1) {
+            asm volatile("" ::: "memory");
+            store_strip(fm);
         }
     };
     auto prm_sxf = [&](int fm) __attribute__((always_inline)) { return prm_sx(wm * FM * 16 + fm * 16 + (lane & 15)); };

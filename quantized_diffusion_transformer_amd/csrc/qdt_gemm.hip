@@ -508,13 +508,13 @@ gemm_kernel(KArgs p) {
         for (int fm = 0; fm < FM; ++fm) {
             const float sx = prm_sxf(fm);
             put_strip(fm, [&](int fn) {
-                float y[4];
+                float g[4], u[4], y[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float g = dequant(acc[fn][fm][r], sx, swg[fn][r], bg[fn][r]);
-                    const float u = dequant(acc[fn + NF][fm][r], sx, swu[fn][r], bu[fn][r]);
-                    y[r] = silu_gate(g, u);
+                    g[r] = dequant(acc[fn][fm][r], sx, swg[fn][r], bg[fn][r]);
+                    u[r] = dequant(acc[fn + NF][fm][r], sx, swu[fn][r], bu[fn][r]);
                 }
+                silu_gate4(g, u, y);
                 return make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
             });
         }
@@ -659,8 +659,13 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(KArgs p) {
                 bu[0] = bf16_to_f32(bb.x & 0xFFFFu); bu[1] = bf16_to_f32(bb.x >> 16);
                 bu[2] = bf16_to_f32(bb.y & 0xFFFFu); bu[3] = bf16_to_f32(bb.y >> 16);
             }
+            float gg[4], uu[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) y[r] = silu_gate(dequant(a[r], sx, swv[r], b[r]), dequant(u[r], sx, swuv[r], bu[r]));
+            for (int r = 0; r < 4; ++r) {
+                gg[r] = dequant(a[r], sx, swv[r], b[r]);
+                uu[r] = dequant(u[r], sx, swuv[r], bu[r]);
+            }
+            silu_gate4(gg, uu, y);
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = dequant(a[r], sx, swv[r], b[r]);

@@ -194,6 +194,22 @@ def test_silu_gate_epilogue(M, F, K, split):
     assert u.max() <= 1, f"max ulp {u.max()}"
 
 
+@pytest.mark.parametrize("split", [None, 2])
+def test_silu_gate_large_gates(split):
+    """Gate values far beyond |g| = 64 (where the exact expf / division form takes over): the
+    sigmoid tail underflows to +-0 or tiny values exactly as in the oracle, within 1 ulp."""
+    announce(f"silu large gates split={split}")
+    M, F, K = 96, 128, 256
+    d = W.make_linear(M, 2 * F, K, seed=77, x_kind="none", w_sigma=8.0, bias=True)
+    Y, Y_ref, ref, _ = run_linear(d, "silu_gate", split=split)
+    acc = oracle.gemm_i32(ref["Xq"], ref["Wq"]).astype(np.float64)
+    g = acc[:, :F] * ref["sx"][:, None] * ref["sw"][None, :F]
+    assert (np.abs(g) > 64).mean() > 0.2 and (np.abs(g) <= 64).mean() > 0.2  # both forms exercised
+    assert not is_nan_bf16(Y).any()
+    u = ulp_bf16(Y, Y_ref)
+    assert u.max() <= 1, f"max ulp {u.max()}"
+
+
 @pytest.mark.parametrize("M,N,K", [(64, 256, 256), (300, 1024, 1024), (257, 512, 4608)])
 @pytest.mark.parametrize("split", [None, 3])
 def test_head_rmsnorm_epilogue(M, N, K, split):

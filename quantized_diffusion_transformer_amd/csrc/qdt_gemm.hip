@@ -181,7 +181,10 @@ gemm_kernel(KArgs p) {
     const int n0 = tn * (SILU ? BN / 2 : BN);  // first output column (SILU) / weight row
     const int kt0 = split * p.kt_per_split;
     const int kt1 = min(p.kt_total, kt0 + p.kt_per_split);
-    const int nk = kt1 - kt0;
+    const int nk = max(kt1 - kt0, 0);
+    // first stage the LDS-DMAs address: an empty K slice still loads (unused) stage data from
+    // inside the matrix, which keeps the prologue free of branches
+    const int kta = min(kt0, p.kt_total - 1);
 
     // LDS rows are 128 bytes; chunk c of row g sits in slot c ^ (g & 7), which keeps the 16 rows
     // of a fragment read by one ds_read_b128 free of bank conflicts on gfx950 (measured with the
@@ -213,7 +216,7 @@ gemm_kernel(KArgs p) {
         rlocal0 = rw0 - BN;
         rlast = xlast;
     }
-    wbase = uniform_ptr(wbase + (int64_t)kt0 * BK);
+    wbase = uniform_ptr(wbase + (int64_t)kta * BK);
     uint32_t voff[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) voff[i] = (uint32_t)(min(rlocal0 + i * 8 + (lane >> 3), rlast) * Kb) + lchunk * 16;
@@ -272,10 +275,6 @@ gemm_kernel(KArgs p) {
     const int lck1 = ((4 + (lane >> 4)) ^ (lane & 7)) << 4;
 
     Acc acc[FN][FM];
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = Acc{0, 0, 0, 0};
 
     // One MFMA of the group for weight fragment g, token fragment fm.
     auto mma = [&](int g, int fm, const v4u& a, const v4u& b) __attribute__((always_inline)) {
@@ -297,74 +296,78 @@ gemm_kernel(KArgs p) {
     // own stage.  Every LDS read and LDS-DMA is issued between two MFMAs, so a wave never waits
     // on LDS latency after a barrier.  Past the last stage, loads are clamped to stage nk-1 (their
     // data is never used), which keeps the loop free of branches.
-    // Parameter chunks go first, so the prologue's wait for stage 0 covers them.
+    // Prologue: the LDS-DMAs of stages 0 and 1 go out first, then the parameter chunks (needed
+    // only by the epilogue); the accumulators are cleared while they are in flight.  Loads
+    // complete in issue order, so vmcnt <= NI means stage 0 has landed.
+    const int nkc = max(nk, 1);
+    v4u a0[FN], b0[FM], a1[FN], b1[FM];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma(0, 0, i);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma(1, min(1, nkc - 1), i);
 #pragma unroll
     for (int c = 0; c < P_BF / 64; ++c) {
         const bool is_bias = c * 64 >= P_B && c * 64 < P_G;
         if (c % NW == wave && (!is_bias || p.bias != nullptr)) prm_dma(c);
     }
-    if (nk > 0) {
-        v4u a0[FN], b0[FM], a1[FN], b1[FM];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) dma(0, 0, i);
+    for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-        for (int i = 0; i < NI; ++i) dma(1, min(1, nk - 1), i);
-        wait_vmcnt<NI>();
-        __syncthreads();
-        {
-            const uint8_t* s = smem + lrow;
+        for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = Acc{0, 0, 0, 0};
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<NI>();
+    __syncthreads();
+    {
+        const uint8_t* s = smem + lrow;
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) a0[fn] = frag(s, wrow[fn], lck0);
+        for (int fn = 0; fn < FN; ++fn) a0[fn] = frag(s, wrow[fn], lck0);
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) b0[fm] = frag(s, xrow0 + fm * 16, lck0);
-        }
-        for (int j = 0; j < nk; ++j) {
-            const uint8_t* s = smem + (j % NB) * STAGE + lrow;
-            const uint8_t* sn = smem + ((j + 1) % NB) * STAGE + lrow;
-            const int jd = min(j + 2, nk - 1);
-            // sub-step 0: every SP-th slot reads b1[0..FM-1], then a1[0..FN-1]
-#pragma unroll
-            for (int g = 0; g < FN; ++g) {
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm) {
-                    mma(g, fm, a0[g], b0[fm]);
-                    const int k = g * FM + fm, q = k / SP;
-                    if (k % SP == 0 && q < FM)
-                        b1[q] = frag(s, xrow0 + q * 16, lck1);
-                    else if (k % SP == 0 && q < FM + FN)
-                        a1[q - FM] = frag(s, wrow[q - FM], lck1);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            wait_vmcnt<0>();
-            __syncthreads();
-            // sub-step 1: slot SP q issues LDS-DMA q of stage j+2 (and points M0 at LDS-DMA q+1);
-            // slot SP q + SP/2 reads b0[q] / a0[q - FM] of stage j+1
-            const uint32_t ldsd = ldsw + (uint32_t)((j % NB) * STAGE);
-            const uint8_t* sbase = wbase + (int64_t)jd * BK;
-            set_m0(ldsd);
-#pragma unroll
-            for (int g = 0; g < FN; ++g) {
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm) {
-                    mma(g, fm, a1[g], b1[fm]);
-                    const int k = g * FM + fm, q = k / SP;
-                    if (k % SP == 0 && q < NI)
-                        lds_dma16_next(voff[q], sbase, ldsd + (uint32_t)((q + 1) * 1024));
-                    else if (k % SP == SP / 2 && q < FM)
-                        b0[q] = frag(sn, xrow0 + q * 16, lck0);
-                    else if (k % SP == SP / 2 && q < FM + FN)
-                        a0[q - FM] = frag(sn, wrow[q - FM], lck0);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        }
-        wait_vmcnt<0>();
-        mfma_drain();
-    } else {
-        wait_vmcnt<0>();
-        __syncthreads();
+        for (int fm = 0; fm < FM; ++fm) b0[fm] = frag(s, xrow0 + fm * 16, lck0);
     }
+    for (int j = 0; j < nk; ++j) {
+        const uint8_t* s = smem + (j % NB) * STAGE + lrow;
+        const uint8_t* sn = smem + ((j + 1) % NB) * STAGE + lrow;
+        const int jd = min(j + 2, nk - 1);
+        // sub-step 0: every SP-th slot reads b1[0..FM-1], then a1[0..FN-1]
+#pragma unroll
+        for (int g = 0; g < FN; ++g) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                mma(g, fm, a0[g], b0[fm]);
+                const int k = g * FM + fm, q = k / SP;
+                if (k % SP == 0 && q < FM)
+                    b1[q] = frag(s, xrow0 + q * 16, lck1);
+                else if (k % SP == 0 && q < FM + FN)
+                    a1[q - FM] = frag(s, wrow[q - FM], lck1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+        // sub-step 1: slot SP q issues LDS-DMA q of stage j+2 (and points M0 at LDS-DMA q+1);
+        // slot SP q + SP/2 reads b0[q] / a0[q - FM] of stage j+1
+        const uint32_t ldsd = ldsw + (uint32_t)((j % NB) * STAGE);
+        const uint8_t* sbase = wbase + (int64_t)jd * BK;
+        set_m0(ldsd);
+#pragma unroll
+        for (int g = 0; g < FN; ++g) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                mma(g, fm, a1[g], b1[fm]);
+                const int k = g * FM + fm, q = k / SP;
+                if (k % SP == 0 && q < NI)
+                    lds_dma16_next(voff[q], sbase, ldsd + (uint32_t)((q + 1) * 1024));
+                else if (k % SP == SP / 2 && q < FM)
+                    b0[q] = frag(sn, xrow0 + q * 16, lck0);
+                else if (k % SP == SP / 2 && q < FM + FN)
+                    a0[q - FM] = frag(sn, wrow[q - FM], lck0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    wait_vmcnt<0>();
+    mfma_drain();
 
     // ---------------------------------------------------------------- epilogues
     // Staged parameters of tile weight rows rl .. rl+3 and tile token row.

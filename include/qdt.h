@@ -92,7 +92,7 @@ typedef struct qdt_linear_plan {
     int32_t split_k;         /* number of K slices; 1 = no split (epilogue fused in the GEMM) */
     int32_t tile_m, tile_n;  /* token rows and weight rows per workgroup */
     int32_t tiles_m, tiles_n;
-    int32_t k_tiles;         /* K stages of the main loop (64 bytes of K each) */
+    int32_t k_tiles;         /* K stages of the main loop (128 bytes of K each) */
     int32_t grid;            /* workgroups launched by the GEMM kernel */
     int64_t workspace_bytes; /* int32 partial sums for split_k > 1, else 0 */
 } qdt_linear_plan;

@@ -8,19 +8,21 @@
 // independence: "Faster Ideogram 4 with Less Prompt Compute", "Most of the Tensor Was Zero".
 //
 // Design (gfx950):
-//   * One workgroup of 4 waves (one per SIMD) computes a BM x BN tile; each wave owns an
+//   * One workgroup of 4 waves (one per SIMD) computes a BM x BN tile (256 x 256, or 288 x 288
+//     where that makes the tile count a multiple of the 256 CUs); each wave owns an
 //     (FM*16) x (FN*16) sub-tile as FN x FM accumulators of v_mfma_i32_16x16x64_i8
 //     (v_mfma_f32_16x16x32_bf16 for bf16).  The MFMA A operand is the weight fragment and
 //     the B operand the token fragment, so lane l holds 4 consecutive output columns of one
-//     output row: the epilogue stores 8 bytes per lane straight from registers.
-//   * K advances 128 bytes (two MFMA K steps; 64 bytes for the 288 tile) per stage through two
-//     LDS buffers: the global loads of stage k+1 are in flight (register staged) while the
-//     MFMAs of stage k run, then written to the other buffer -- one barrier per stage.  LDS
-//     rows are XOR-swizzled so that the 16 rows read by one ds_read_b128 fall in distinct
-//     banks.
+//     output row.
+//   * K advances 128 bytes per stage (two MFMA K steps, whole cache lines) through two LDS
+//     buffers filled by LDS-DMA (global_load_lds_dwordx4, no register staging); one barrier per
+//     stage, between its two K steps.  LDS rows are XOR-swizzled so that the 16 rows read by
+//     one ds_read_b128 fall in distinct banks.
 //   * Tile order is XCD-aware: workgroup ids are dealt round-robin to the 8 XCDs, so ids are
 //     remapped to give each XCD a contiguous run of tiles, walked in groups of `group_m` tile
 //     rows, which keeps the operands of neighbouring tiles in that XCD's L2.
+//   * Epilogue parameters are staged in LDS during the prologue; outputs go through LDS strips
+//     so that each store writes 16 contiguous bytes per lane.
 //   * Rows beyond M (or N) are clamped loads whose outputs are not stored; the integer sum is
 //     exact, so the result is independent of the tile shape and of the K split.
 #include <type_traits>

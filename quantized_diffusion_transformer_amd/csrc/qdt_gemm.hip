@@ -442,7 +442,15 @@ gemm_kernel(KArgs p) {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const v4u v = *reinterpret_cast<const v4u*>(st + lofs[it]);
-            if (ok[it] && rr[it] < rows_left) *reinterpret_cast<v4u*>(yrow + gofs[it]) = v;
+            if (ok[it] && rr[it] < rows_left) {
+                v4u* dst = reinterpret_cast<v4u*>(yrow + gofs[it]);
+                // the output is consumed by a later kernel: stream it past the caches (measured
+                // faster for back-to-back linears); split-K partials are re-read at once, cached
+                if constexpr (EPI == EPI_PARTIAL)
+                    *dst = v;
+                else
+                    __builtin_nontemporal_store(v, dst);
+            }
         }
     };
     auto put_strip = [&](int fm, auto&& frag_out) __attribute__((always_inline)) {

@@ -81,8 +81,10 @@ typedef struct qdt_rmsnorm_params {
 /* Workgroup tile shapes of the MFMA GEMM. */
 typedef enum qdt_tile {
     QDT_TILE_AUTO = -1,
-    QDT_TILE_256 = 0, /* 256 token rows x 256 weight rows per workgroup */
-    QDT_TILE_288 = 1  /* 288 x 288: 16 x 16 = 256 tiles at 4608 x 4608, one per compute unit */
+    QDT_TILE_256 = 0,    /* 256 token rows x 256 weight rows per workgroup */
+    QDT_TILE_288 = 1,    /* 288 x 288: 16 x 16 = 256 tiles at 4608 x 4608, one per compute unit */
+    QDT_TILE_288x256 = 2 /* 288 token rows x 256 weight rows (any epilogue); only on request: the
+                            planner does not pick it (slower per tile than 256 x 256 on the FFN) */
 } qdt_tile;
 
 /* Launch plan of qdt_w8a8_linear.  The planner fills every field; callers of

@@ -27,10 +27,14 @@ qdt_status make_plan(int64_t M, int64_t N, int64_t K, int epi, int esize, int ti
     const bool silu = epi == EPI_SILU, rms = epi == EPI_RMSNORM;
     Plan best{};
     double best_cost = -1.0;
-    for (int tile = QDT_TILE_256; tile <= QDT_TILE_288; ++tile) {
+    for (int tile = QDT_TILE_256; tile <= QDT_TILE_288x256; ++tile) {
         if (tile_req != QDT_TILE_AUTO && tile != tile_req) continue;
         if (tile == QDT_TILE_288 && (silu || rms)) continue;  // heads / gate-up halves need 256-wide tiles
-        const int bm = tile == QDT_TILE_288 ? 288 : 256, bn = bm;
+        // 288 x 256 only on request: its weight and token waves issue unequal LDS-DMA counts and it
+        // measured ~5% slower per FFN gate/up step than 256 x 256 despite fewer tile rounds
+        if (tile == QDT_TILE_288x256 && tile_req == QDT_TILE_AUTO) continue;
+        const int bm = tile == QDT_TILE_256 ? 256 : 288;       // token rows
+        const int bn = tile == QDT_TILE_288 ? 288 : 256;       // weight rows
         const int64_t kstage = 128;  // bytes of K per main-loop stage (whole cache lines)
         const int64_t kt_total = cdiv(K * esize, kstage);
         const int64_t tiles_m = cdiv(M > 0 ? M : 1, bm);
@@ -202,7 +206,7 @@ qdt_status qdt_w8a8_linear_plan_for(int64_t M, int64_t N, int64_t K, qdt_epilogu
     if (!plan) return QDT_EINVAL;
     qdt_status r = check_shape(M, N, K, epi);
     if (r != QDT_OK) return r;
-    if (tile != QDT_TILE_AUTO && tile != QDT_TILE_256 && tile != QDT_TILE_288) return QDT_EINVAL;
+    if (tile != QDT_TILE_AUTO && (tile < QDT_TILE_256 || tile > QDT_TILE_288x256)) return QDT_EINVAL;
     if (split_k < 0) return QDT_EINVAL;
     Plan p;
     if ((r = make_plan(M, N, K, epi_kind(epi), 1, tile, split_k, &p)) != QDT_OK) return r;
@@ -225,7 +229,7 @@ static qdt_status linear_impl(const int8_t* Xq, const float* x_scale, const int8
                               int tile_req, int split_req, qdt_linear_plan* plan_out, void* stream) {
     qdt_status r = check_shape(M, N, K, epi);
     if (r != QDT_OK) return r;
-    if (tile_req != QDT_TILE_AUTO && tile_req != QDT_TILE_256 && tile_req != QDT_TILE_288) return QDT_EINVAL;
+    if (tile_req != QDT_TILE_AUTO && (tile_req < QDT_TILE_256 || tile_req > QDT_TILE_288x256)) return QDT_EINVAL;
     if (split_req < 0) return QDT_EINVAL;
     const int kind = epi_kind(epi);
     const qdt_rmsnorm_params* rp = reinterpret_cast<const qdt_rmsnorm_params*>(epi_params);

@@ -140,12 +140,15 @@ gemm_kernel(KArgs p) {
     constexpr int NB = 2;                  // LDS stages (double buffer)
     constexpr int ROWS = BN + BM;          // LDS rows per stage: weight rows, then token rows
     constexpr int STAGE = ROWS * BK;
-    constexpr int NBLK = ROWS / 8;         // 1 KiB LDS blocks (8 rows) per stage
-    constexpr int NI = NBLK / NW;          // LDS-DMA instructions per wave per stage
+    // 1 KiB LDS blocks (8 rows) per stage: waves 0 and 1 copy the weight rows (gate and up
+    // halves for SILU), waves 2 and 3 the token rows, NIW / NIX LDS-DMA instructions each
+    constexpr int NBW = BN / 8, NBX = BM / 8;
+    constexpr int NIW = NBW / 2, NIX = NBX / 2;
+    constexpr int NI = NIW > NIX ? NIW : NIX;  // LDS-DMA slots per wave per stage
     constexpr int NACC_A = 64;             // accumulator tuples held in AGPRs (the rest in VGPRs)
     constexpr bool SILU = EPI == EPI_SILU;
-    static_assert(NBLK % NW == 0, "whole LDS blocks per wave");
-    static_assert(BN % 8 == 0 && (!SILU || ((BN / 2) % 8 == 0 && FN % 2 == 0)), "blocks never straddle");
+    static_assert(WM == 2 && WN == 2 && NBW % 2 == 0 && NBX % 2 == 0, "two waves per operand region");
+    static_assert(!SILU || (NIW * 8 == BN / 2 && FN % 2 == 0), "one weight wave per gate / up half");
     constexpr int SP = 4;                  // MFMA slots between consecutive LDS-DMAs / reads
     static_assert(NI * SP <= FN * FM && (FN + FM) * SP <= FN * FM, "LDS-DMAs and reads fit between the MFMAs of a sub-step");
     using Acc = typename AccT<BF16>::type;
@@ -202,30 +205,35 @@ gemm_kernel(KArgs p) {
     const int nlim = SILU ? p.F : p.N;
     const int wlast = nlim - n0 - 1, xlast = p.M - m0 - 1;
     const int lchunk = (lane & 7) ^ ((lane >> 3) & 7);
-    // The NI blocks of a wave lie in one operand region (weight rows; gate or up rows for SILU;
+    // The blocks of a wave lie in one operand region (weight rows; gate or up rows for SILU;
     // token rows): one scalar base per wave, a 32-bit offset per lane and instruction.
-    static_assert(BN % (NI * 8) == 0 && (!SILU || (BN / 2) % (NI * 8) == 0), "one operand region per wave");
-    const int rw0 = wave * NI * 8;  // first tile row of the wave's blocks
+    const bool wwave = wave < 2;                 // weight-row wave
+    const int niw = wwave ? NIW : NIX;           // its LDS-DMA instructions per stage
     const uint8_t* wbase;
     int rlocal0, rlast;
-    if (rw0 < BN) {
-        const bool up = SILU && rw0 >= BN / 2;
+    if (wwave) {
+        const bool up = SILU && wave == 1;
         wbase = p.W + (int64_t)((up ? p.F : 0) + n0) * Kb;
-        rlocal0 = up ? rw0 - BN / 2 : rw0;
+        rlocal0 = SILU ? 0 : wave * NIW * 8;
         rlast = wlast;
     } else {
         wbase = p.X + (int64_t)m0 * Kb;
-        rlocal0 = rw0 - BN;
+        rlocal0 = (wave - 2) * NIX * 8;
         rlast = xlast;
     }
     wbase = uniform_ptr(wbase + (int64_t)kta * BK);
-    uint32_t voff[NI];
+    // lane offset of LDS-DMA i: row rlocal0 + 8 i + lane / 8, clamped to the region's last row
+    uint32_t voffs[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) voff[i] = (uint32_t)(min(rlocal0 + i * 8 + (lane >> 3), rlast) * Kb) + lchunk * 16;
-    const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds_offset(smem) + wave * NI * 1024);
+    for (int i = 0; i < NI; ++i) voffs[i] = (uint32_t)(min(rlocal0 + i * 8 + (lane >> 3), rlast) * Kb) + lchunk * 16;
+    auto voff = [&](int i) __attribute__((always_inline)) { return voffs[i]; };
+    const int blk0 = wwave ? wave * NIW : NBW + (wave - 2) * NIX;  // first LDS block of the wave
+    const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds_offset(smem) + blk0 * 1024);
+    // whether LDS-DMA slot i is used by this wave (all are when both regions have equal rows)
+    auto dma_used = [&](int i) __attribute__((always_inline)) { return NIW == NIX || i < niw; };
     // LDS-DMA instruction i of `stage` into LDS buffer `buf` (sets M0 itself)
     auto dma = [&](int buf, int stage, int i) __attribute__((always_inline)) {
-        lds_dma16_s(ldsw + (uint32_t)(buf * STAGE + i * 1024), voff[i], wbase + (int64_t)stage * BK);
+        lds_dma16_s(ldsw + (uint32_t)(buf * STAGE + i * 1024), voff(i), wbase + (int64_t)stage * BK);
     };
 
     // Global weight row of tile weight row r (clamped like the operand rows).
@@ -304,9 +312,11 @@ gemm_kernel(KArgs p) {
     const int nkc = max(nk, 1);
     v4u a0[FN], b0[FM], a1[FN], b1[FM];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma(0, 0, i);
+    for (int i = 0; i < NI; ++i)
+        if (dma_used(i)) dma(0, 0, i);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma(1, min(1, nkc - 1), i);
+    for (int i = 0; i < NI; ++i)
+        if (dma_used(i)) dma(1, min(1, nkc - 1), i);
 #pragma unroll
     for (int c = 0; c < P_BF / 64; ++c) {
         const bool is_bias = c * 64 >= P_B && c * 64 < P_G;
@@ -318,7 +328,12 @@ gemm_kernel(KArgs p) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = Acc{0, 0, 0, 0};
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<NI>();
+    if (NIW == NIX)
+        wait_vmcnt<NI>();
+    else if (wwave)
+        wait_vmcnt<NIW>();
+    else
+        wait_vmcnt<NIX>();
     __syncthreads();
     {
         const uint8_t* s = smem + lrow;
@@ -358,8 +373,9 @@ gemm_kernel(KArgs p) {
             for (int fm = 0; fm < FM; ++fm) {
                 mma(g, fm, a1[g], b1[fm]);
                 const int k = g * FM + fm, q = k / SP;
-                if (k % SP == 0 && q < NI)
-                    lds_dma16_next(voff[q], sbase, ldsd + (uint32_t)((q + 1) * 1024));
+                if (k % SP == 0 && q < NI) {
+                    if (dma_used(q)) lds_dma16_next(voff(q), sbase, ldsd + (uint32_t)((q + 1) * 1024));
+                }
                 else if (k % SP == SP / 2 && q < FM)
                     b0[q] = frag(sn, xrow0 + q * 16, lck0);
                 else if (k % SP == SP / 2 && q < FM + FN)
@@ -715,9 +731,9 @@ static KArgs make_kargs(const GemmArgs& a, const Plan& pl, int esize) {
     return k;
 }
 
-template <int FMN, bool BF16, int EPI>
+template <int FM, int FN, bool BF16, int EPI>
 static hipError_t go(const KArgs& k, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_kernel<2, 2, FMN, FMN, BF16, EPI>), dim3(grid), dim3(256), 0, st, k);
+    hipLaunchKernelGGL((gemm_kernel<2, 2, FM, FN, BF16, EPI>), dim3(grid), dim3(256), 0, st, k);
     return hipGetLastError();
 }
 
@@ -726,26 +742,37 @@ hipError_t launch_gemm_i8(const GemmArgs& a, const Plan& pl, hipStream_t st) {
     const int epi = pl.split_k > 1 ? EPI_PARTIAL : a.epi;
     if (pl.tile == QDT_TILE_288) {
         switch (epi) {
-            case EPI_BIAS: return go<9, false, EPI_BIAS>(k, pl.grid, st);
-            case EPI_ACC: return go<9, false, EPI_ACC>(k, pl.grid, st);
-            case EPI_PARTIAL: return go<9, false, EPI_PARTIAL>(k, pl.grid, st);
+            case EPI_BIAS: return go<9, 9, false, EPI_BIAS>(k, pl.grid, st);
+            case EPI_ACC: return go<9, 9, false, EPI_ACC>(k, pl.grid, st);
+            case EPI_PARTIAL: return go<9, 9, false, EPI_PARTIAL>(k, pl.grid, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (pl.tile == QDT_TILE_288x256) {
+        switch (epi) {
+            case EPI_BIAS: return go<9, 8, false, EPI_BIAS>(k, pl.grid, st);
+            case EPI_SILU: return go<9, 8, false, EPI_SILU>(k, pl.grid, st);
+            case EPI_RMSNORM: return go<9, 8, false, EPI_RMSNORM>(k, pl.grid, st);
+            case EPI_ACC: return go<9, 8, false, EPI_ACC>(k, pl.grid, st);
+            case EPI_PARTIAL: return go<9, 8, false, EPI_PARTIAL>(k, pl.grid, st);
             default: return hipErrorInvalidValue;
         }
     }
     switch (epi) {
-        case EPI_BIAS: return go<8, false, EPI_BIAS>(k, pl.grid, st);
-        case EPI_SILU: return go<8, false, EPI_SILU>(k, pl.grid, st);
-        case EPI_RMSNORM: return go<8, false, EPI_RMSNORM>(k, pl.grid, st);
-        case EPI_ACC: return go<8, false, EPI_ACC>(k, pl.grid, st);
-        case EPI_PARTIAL: return go<8, false, EPI_PARTIAL>(k, pl.grid, st);
+        case EPI_BIAS: return go<8, 8, false, EPI_BIAS>(k, pl.grid, st);
+        case EPI_SILU: return go<8, 8, false, EPI_SILU>(k, pl.grid, st);
+        case EPI_RMSNORM: return go<8, 8, false, EPI_RMSNORM>(k, pl.grid, st);
+        case EPI_ACC: return go<8, 8, false, EPI_ACC>(k, pl.grid, st);
+        case EPI_PARTIAL: return go<8, 8, false, EPI_PARTIAL>(k, pl.grid, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, const Plan& pl, hipStream_t st) {
     KArgs k = make_kargs(a, pl, 2);
-    if (pl.tile == QDT_TILE_288) return go<9, true, EPI_F32BIAS>(k, pl.grid, st);
-    return go<8, true, EPI_F32BIAS>(k, pl.grid, st);
+    if (pl.tile == QDT_TILE_288) return go<9, 9, true, EPI_F32BIAS>(k, pl.grid, st);
+    if (pl.tile == QDT_TILE_288x256) return go<9, 8, true, EPI_F32BIAS>(k, pl.grid, st);
+    return go<8, 8, true, EPI_F32BIAS>(k, pl.grid, st);
 }
 
 hipError_t launch_splitk_epilogue(const GemmArgs& a, int split_k, int epi, hipStream_t st) {

@@ -110,20 +110,20 @@ def test_bf16_linear_validation():
     assert f(A(), A(0x200000), None, 0, 128, 128, A(0x900000), 128, None) == qdt.QDT_OK
 
 
-@pytest.mark.parametrize("M,N,K,epi,tile,split", [
-    (4608, 4608, 4608, "bias", 288, 1),          # attention projection: 256 tiles of 288 x 288
-    (512, 4608, 53248, "bias", 256, 7),          # deep-K text projection: split K over 7 slices
-    (4608, 4608, 53248, "bias", 288, 1),         # its zero-padded variant fills the GPU without a split
-    (16896, 4608, 4608, "head_rmsnorm", 256, 1),  # heads need 256-wide tiles
-    (6037, 4608, 4608, "head_rmsnorm", 256, 1),
-    (4608, 24576, 4608, "silu_gate", 256, 1),
-    (64, 128, 256, "bias", 256, 1),
+@pytest.mark.parametrize("M,N,K,epi,tm,tn,split", [
+    (4608, 4608, 4608, "bias", 288, 288, 1),          # attention projection: 256 tiles of 288 x 288
+    (512, 4608, 53248, "bias", 256, 256, 7),          # deep-K text projection: split K over 7 slices
+    (4608, 4608, 53248, "bias", 288, 288, 1),         # its zero-padded variant fills the GPU without a split
+    (16896, 4608, 4608, "head_rmsnorm", 256, 256, 1),  # heads need 256-wide tiles
+    (6037, 4608, 4608, "head_rmsnorm", 256, 256, 1),
+    (4608, 24576, 4608, "silu_gate", 256, 256, 1),
+    (64, 128, 256, "bias", 256, 256, 1),
 ])
-def test_planner_choices(M, N, K, epi, tile, split):
+def test_planner_choices(M, N, K, epi, tm, tn, split):
     p = qdt.linear_plan(M, N, K, epi)
-    assert p["tile_m"] == tile and p["split_k"] == split
-    nout_tiles = -(-(N // 2) // (tile // 2)) if epi == "silu_gate" else -(-N // tile)
-    assert p["tiles_m"] == -(-M // tile) and p["tiles_n"] == nout_tiles
+    assert p["tile_m"] == tm and p["tile_n"] == tn and p["split_k"] == split
+    nout_tiles = -(-(N // 2) // (tn // 2)) if epi == "silu_gate" else -(-N // tn)
+    assert p["tiles_m"] == -(-M // tm) and p["tiles_n"] == nout_tiles
     assert p["grid"] == p["tiles_m"] * p["tiles_n"] * p["split_k"]
     assert p["workspace_bytes"] == (split * M * N * 4 if split > 1 else 0)
 
@@ -136,3 +136,7 @@ def test_plan_for_honours_requests():
     assert p["split_k"] == 2
     with pytest.raises(qdt.QdtError):
         qdt.linear_plan(600, 1024, 4096, "head_rmsnorm", tile=qdt.QDT_TILE_288)
+    p = qdt.linear_plan(600, 1024, 4096, "head_rmsnorm", tile=qdt.QDT_TILE_288x256)
+    assert p["tile_m"] == 288 and p["tile_n"] == 256
+    with pytest.raises(qdt.QdtError):
+        qdt.linear_plan(600, 1024, 4096, "bias", tile=3)

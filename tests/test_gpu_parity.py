@@ -131,7 +131,8 @@ SHAPES = [
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
 @pytest.mark.parametrize("tile,split", [(None, None), (qdt.QDT_TILE_256, 1), (qdt.QDT_TILE_288, 1),
-                                        (qdt.QDT_TILE_256, 3)])
+                                        (qdt.QDT_TILE_288x256, 1), (qdt.QDT_TILE_256, 3),
+                                        (qdt.QDT_TILE_288x256, 2)])
 def test_int32_accumulators_bit_exact(M, N, K, tile, split):
     announce(f"acc M={M} N={N} K={K} tile={tile} split={split}")
     d = W.make_linear(M, N, K, seed=M + N + K, x_kind="pct1")
@@ -172,7 +173,8 @@ def run_linear(d, epi, tile=None, split=None, bias=True):
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES + [(700, 4608, 4608)])
-@pytest.mark.parametrize("tile,split", [(None, None), (qdt.QDT_TILE_288, 1), (qdt.QDT_TILE_256, 4)])
+@pytest.mark.parametrize("tile,split", [(None, None), (qdt.QDT_TILE_288, 1), (qdt.QDT_TILE_256, 4),
+                                        (qdt.QDT_TILE_288x256, 1)])
 def test_bias_epilogue_exact(M, N, K, tile, split):
     announce(f"bias M={M} N={N} K={K} tile={tile} split={split}")
     d = W.make_linear(M, N, K, seed=11 + M, x_kind="pct1")
@@ -184,11 +186,11 @@ def test_bias_epilogue_exact(M, N, K, tile, split):
 
 
 @pytest.mark.parametrize("M,F,K", [(64, 64, 256), (300, 640, 1024), (513, 1152, 512)])
-@pytest.mark.parametrize("split", [None, 3])
-def test_silu_gate_epilogue(M, F, K, split):
-    announce(f"silu M={M} F={F} K={K} split={split}")
+@pytest.mark.parametrize("tile,split", [(None, None), (None, 3), (qdt.QDT_TILE_288x256, 1)])
+def test_silu_gate_epilogue(M, F, K, tile, split):
+    announce(f"silu M={M} F={F} K={K} tile={tile} split={split}")
     d = W.make_linear(M, 2 * F, K, seed=21 + M, x_kind="pct1", bias=True)
-    Y, Y_ref, _, _ = run_linear(d, "silu_gate", split=split)
+    Y, Y_ref, _, _ = run_linear(d, "silu_gate", tile=tile, split=split)
     assert Y.shape == (M, F) and not is_nan_bf16(Y).any()
     u = ulp_bf16(Y, Y_ref)
     assert u.max() <= 1, f"max ulp {u.max()}"
@@ -211,11 +213,11 @@ def test_silu_gate_large_gates(split):
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 256, 256), (300, 1024, 1024), (257, 512, 4608)])
-@pytest.mark.parametrize("split", [None, 3])
-def test_head_rmsnorm_epilogue(M, N, K, split):
-    announce(f"rmsnorm M={M} N={N} K={K} split={split}")
+@pytest.mark.parametrize("tile,split", [(None, None), (None, 3), (qdt.QDT_TILE_288x256, 1)])
+def test_head_rmsnorm_epilogue(M, N, K, tile, split):
+    announce(f"rmsnorm M={M} N={N} K={K} tile={tile} split={split}")
     d = W.make_linear(M, N, K, seed=31 + M, x_kind="pct1", epi="head_rmsnorm")
-    Y, Y_ref, _, _ = run_linear(d, "head_rmsnorm", split=split)
+    Y, Y_ref, _, _ = run_linear(d, "head_rmsnorm", tile=tile, split=split)
     assert not is_nan_bf16(Y).any()
     u = ulp_bf16(Y, Y_ref)
     assert u.max() <= 1, f"max ulp {u.max()}"
@@ -227,7 +229,8 @@ def test_results_do_not_depend_on_plan():
     announce("plan independence")
     d = W.make_linear(600, 1152, 2048, seed=41, x_kind="pct1")
     outs = [run_linear(d, "bias", t, s)[0] for t, s in ((None, None), (qdt.QDT_TILE_288, 1), (qdt.QDT_TILE_256, 1),
-                                                         (qdt.QDT_TILE_256, 5), (qdt.QDT_TILE_288, 2))]
+                                                         (qdt.QDT_TILE_256, 5), (qdt.QDT_TILE_288, 2),
+                                                         (qdt.QDT_TILE_288x256, 1), (qdt.QDT_TILE_288x256, 3))]
     for o in outs[1:]:
         assert bits_equal(o, outs[0])
     ref, dev = prepared(d)

@@ -9,12 +9,6 @@ namespace qdt {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
 
-// Round-half-to-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    __bf16 b = static_cast<__bf16>(f);
-    return (uint32_t)__builtin_bit_cast(uint16_t, b);
-}
-
 // Two round-half-to-even conversions in one v_cvt_pk_bf16_f32; lo in bits 0..15.
 typedef float qdt_v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 qdt_v2bf __attribute__((ext_vector_type(2)));

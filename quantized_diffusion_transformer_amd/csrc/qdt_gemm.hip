@@ -87,24 +87,18 @@ __device__ __forceinline__ void mfma_drain() {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
-// LDS-DMA (gfx950 global_load_lds_dwordx4): lane l of the wave copies 16 bytes from its global
-// address to LDS at m0 + 16 l, i.e. one wave instruction fills 1 KiB of LDS without passing
-// through registers.  Issued from inline asm so that the compiler does not wait for it before
-// every LDS read; completion is tracked by explicit vmcnt waits before the barrier that
-// publishes a stage.  M0 is set in the same statement (the compiler sets M0 itself before
-// each of its own uses).
-__device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* gptr) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(gptr)
-                 : "memory", "m0");
-}
 // LDS-DMA of one dword per lane (global_load_lds_dword): lane l writes LDS m0 + 4 l.
 __device__ __forceinline__ void lds_dma4(uint32_t lds_addr, const void* gptr) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr), "v"(gptr)
                  : "memory", "m0");
 }
-// Same, addressed as a 64-bit scalar base plus a 32-bit per-lane offset, with M0 already set;
-// sets M0 to the LDS address of the next LDS-DMA afterwards, so the MFMAs issued in between
-// cover the M0 -> LDS-DMA hazard.  The compiler does not use M0 on gfx950 (LDS instructions do
+// LDS-DMA (gfx950 global_load_lds_dwordx4): lane l of the wave copies 16 bytes from its global
+// address to LDS at m0 + 16 l, i.e. one wave instruction fills 1 KiB of LDS without passing
+// through registers.  Issued from inline asm so that the compiler does not wait for it before
+// every LDS read; completion is tracked by explicit vmcnt waits before the barrier that
+// publishes a stage.  Addressed as a 64-bit scalar base plus a 32-bit per-lane offset.
+// This form expects M0 already set and sets M0 to the LDS address of the next LDS-DMA
+// afterwards, so the MFMAs issued in between cover the M0 -> LDS-DMA hazard.  The compiler does not use M0 on gfx950 (LDS instructions do
 // not read it), so keeping it live between statements is safe.
 __device__ __forceinline__ void lds_dma16_next(uint32_t voff, const void* sbase, uint32_t next_lds) {
     asm volatile("global_load_lds_dwordx4 %0, %1\n\ts_mov_b32 m0, %2" ::"v"(voff), "s"(sbase), "s"(next_lds)

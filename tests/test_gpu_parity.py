@@ -223,6 +223,29 @@ def test_head_rmsnorm_epilogue(M, N, K, tile, split):
     assert u.max() <= 1, f"max ulp {u.max()}"
 
 
+@pytest.mark.parametrize("epi", ["bias", "silu_gate", "head_rmsnorm", "acc_i32"])
+@pytest.mark.parametrize("split", [None, 3])
+def test_strided_output_into_wider_buffer(epi, split):
+    """Y written into a column window of a wider row-major buffer (ldy > N_out): the window
+    equals the packed result and the columns around it keep their sentinel."""
+    announce(f"strided output epi={epi} split={split}")
+    M, N, K = 300, 512, 1024
+    d = W.make_linear(M, N, K, seed=57, x_kind="pct1", epi=epi if epi == "head_rmsnorm" else "bias")
+    ref, dev = prepared(d)
+    b = to_dev(d["bias"])
+    kw = dict(gamma=to_dev(d["gamma"]), eps=d["eps"]) if epi == "head_rmsnorm" else {}
+    nout = N // 2 if epi == "silu_gate" else N
+    dt = torch.int32 if epi == "acc_i32" else torch.bfloat16
+    packed = qdt.w8a8_linear(dev["Xq"], dev["sx"], dev["Wq"], dev["sw"], b, epi, split_k=split, **kw)
+    wide = torch.full((M, nout + 48), 7, dtype=dt, device="cuda")
+    view = wide[:, 16:16 + nout]
+    qdt.w8a8_linear(dev["Xq"], dev["sx"], dev["Wq"], dev["sw"], b, epi, out=view, split_k=split, **kw)
+    torch.cuda.synchronize()
+    assert view.stride(0) == nout + 48
+    assert torch.equal(view, packed)
+    assert bool((wide[:, :16] == 7).all()) and bool((wide[:, 16 + nout:] == 7).all())
+
+
 def test_results_do_not_depend_on_plan():
     # the integer sum is exact and every element gets the same fp32 sequence, so every plan
     # (tile shape, K split) gives the same bits; rows are independent of M

@@ -143,8 +143,11 @@ gemm_kernel(KArgs p) {
     constexpr bool SILU = EPI == EPI_SILU;
     static_assert(WM == 2 && WN == 2 && NBW % 2 == 0 && NBX % 2 == 0, "two waves per operand region");
     static_assert(!SILU || (NIW * 8 == BN / 2 && FN % 2 == 0), "one weight wave per gate / up half");
-    constexpr int SP = 4;                  // MFMA slots between consecutive LDS-DMAs / reads
-    static_assert(NI * SP <= FN * FM && (FN + FM) * SP <= FN * FM, "LDS-DMAs and reads fit between the MFMAs of a sub-step");
+    constexpr int SP = 4;                  // MFMA slots between consecutive reads of sub-step 0
+    static_assert((FN + FM) * SP <= FN * FM, "sub-step 0 reads fit between its MFMAs");
+    // sub-step 1 puts LDS-DMA q at slot floor(q FN FM / NI) and read q two slots later: distinct
+    // slots inside the sub-step when the DMA slots are at least 3 apart and reads <= DMAs
+    static_assert(FN * FM >= 3 * NI && FN + FM <= NI, "sub-step 1 LDS-DMAs and reads fit between its MFMAs");
     using Acc = typename AccT<BF16>::type;
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * STAGE];
@@ -356,8 +359,9 @@ gemm_kernel(KArgs p) {
         }
         wait_vmcnt<0>();
         __syncthreads();
-        // sub-step 1: slot SP q issues LDS-DMA q of stage j+2 (and points M0 at LDS-DMA q+1);
-        // slot SP q + SP/2 reads b0[q] / a0[q - FM] of stage j+1
+        // sub-step 1: the LDS-DMAs of stage j+2 are spread evenly over the sub-step's MFMA slots
+        // (each points M0 at the next one); two slots after LDS-DMA slot q, read q of stage j+1
+        // (b0[q], then a0[q - FM])
         const uint32_t ldsd = ldsw + (uint32_t)((j % NB) * STAGE);
         const uint8_t* sbase = wbase + (int64_t)jd * BK;
         set_m0(ldsd);
@@ -366,14 +370,20 @@ gemm_kernel(KArgs p) {
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
                 mma(g, fm, a1[g], b1[fm]);
-                const int k = g * FM + fm, q = k / SP;
-                if (k % SP == 0 && q < NI) {
-                    if (dma_used(q)) lds_dma16_next(voff(q), sbase, ldsd + (uint32_t)((q + 1) * 1024));
-                }
-                else if (k % SP == SP / 2 && q < FM)
-                    b0[q] = frag(sn, xrow0 + q * 16, lck0);
-                else if (k % SP == SP / 2 && q < FM + FN)
-                    a0[q - FM] = frag(sn, wrow[q - FM], lck0);
+                const int k = g * FM + fm;
+                // LDS-DMA q at slot floor(q * S / NI), read q two slots later
+                constexpr int S = FN * FM;
+                int qd = -1, qr = -1;
+#pragma unroll
+                for (int t = 0; t < NI; ++t) if ((t * S) / NI == k) qd = t;
+#pragma unroll
+                for (int t = 0; t < FM + FN; ++t) if ((t * S) / NI + 2 == k) qr = t;
+                if (qd >= 0) {
+                    if (dma_used(qd)) lds_dma16_next(voff(qd), sbase, ldsd + (uint32_t)((qd + 1) * 1024));
+                } else if (qr >= 0 && qr < FM)
+                    b0[qr] = frag(sn, xrow0 + qr * 16, lck0);
+                else if (qr >= FM)
+                    a0[qr - FM] = frag(sn, wrow[qr - FM], lck0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }

@@ -40,7 +40,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=6, help="rotating buffer sets (cold Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
-    ap.add_argument("--only", default=None, help="run only this workload's timing loop (profiling)")
+    ap.add_argument("--only", default=None,
+                    help="run only this workload's timing loop (per-workload profiles); the headline "
+                         "workload skips the others and the CPU baseline, another prints its own line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of known size (HBM counter calibration)")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
@@ -280,14 +282,33 @@ def cpu_baseline(d):
                       f"after a warm-up on 8 rows"}
 
 
-def extra_workloads(args):
-    """Timings of the other workloads (one rotating set; context for the other epilogues)."""
+EXTRA_WORKLOADS = ("dit_ffn_gate_up_4608x24576x4608", "text_cond_proj_512x4608x53248",
+                   "text_cond_proj_padded_4608x4608x53248", "qk_proj_headnorm_16896x4608x4608",
+                   "qk_proj_headnorm_6037x4608x4608")
+
+
+def extra_workloads(args, only=None):
+    """Timings of the other workloads (one rotating set; context for the other epilogues).
+    ``only`` restricts the run to one of EXTRA_WORKLOADS (for per-workload profiles)."""
     import torch
 
     import qdt_workloads as W
     import quantized_diffusion_transformer_amd as qdt
     res = {}
-    steps, warm = max(5, args.steps // 5), 20
+    min_steps = max(5, args.steps // 5)
+
+    def counts(step):
+        """Warm-up of at least 50 ms of load (the clock settles after about 20 ms) and at least
+        20 ms of timed steps, from the duration of a few untimed steps."""
+        for _ in range(3):
+            step(None, None)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            step(None, None)
+        torch.cuda.synchronize()
+        t = (time.perf_counter() - t0) / 5
+        return max(min_steps, int(0.020 / t) + 1), max(20, int(0.050 / t) + 1)
 
     def prep(name, padded=False):
         d = W.make_workload(name, padded=padded)
@@ -316,10 +337,12 @@ def extra_workloads(args):
             qdt.w8a8_linear(Xq, sx, Wq, sw, b, epi, out=Y, workspace=ws, **kw)
             if ev is not None:
                 ev[2].record()
+        steps, warm = counts(step)
         ms, tq, tg = time_loop(step, [None], steps, warm)
         ops = 2.0 * M * N * K
         g = stats(tg)["mean"]
-        r = {"M": M, "N": N, "K": K, "epilogue": epi, "plan": plan, "ms_per_step": round(ms, 4),
+        r = {"M": M, "N": N, "K": K, "epilogue": epi, "plan": plan, "steps": steps, "warmup": warm,
+             "ms_per_step": round(ms, 4),
              "eff_tops": round(ops / (ms * 1e-3) / 1e12, 1), "gemm_ms": round(g, 4),
              "gemm_tops": round(ops / (g * 1e-3) / 1e12, 1),
              "gemm_frac_int8_peak": round(ops / (g * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
@@ -329,8 +352,10 @@ def extra_workloads(args):
         res[name] = r
         log(f"{name}: {r['ms_per_step']} ms/step, GEMM {r['gemm_tops']} TOPS")
 
-    d, X, Wq, sw, inv = prep("dit_ffn_gate_up_4608x24576x4608")
-    Wd = to_dev(d["W_down"])
+    want = (lambda n: True) if only is None else (lambda n: n == only)
+    if want("dit_ffn_gate_up_4608x24576x4608"):
+        d, X, Wq, sw, inv = prep("dit_ffn_gate_up_4608x24576x4608")
+        Wd = to_dev(d["W_down"])
 
     def down(H):
         Z = torch.empty((H.shape[0], Wd.shape[0]), dtype=torch.bfloat16, device="cuda")
@@ -342,23 +367,30 @@ def extra_workloads(args):
             qdt.bf16_linear(H, Wd, out=Z)
             if ev is not None:
                 ev[2].record()
+        steps, warm = counts(step)
         _, _, tg = time_loop(step, [None], steps, warm)
         g = stats(tg)["mean"]
         fl = 2.0 * H.shape[0] * Wd.shape[0] * H.shape[1]
         return {"bf16_down_proj": {"M": H.shape[0], "N": Wd.shape[0], "K": H.shape[1], "ms": round(g, 4),
                                    "tflops": round(fl / (g * 1e-3) / 1e12, 1),
                                    "frac_bf16_peak": round(fl / (g * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
-    run("dit_ffn_gate_up_4608x24576x4608", d, X, Wq, sw, inv, "silu_gate", extra=down)
-    del d, X, Wq, Wd
-    d, X, Wq, sw, inv = prep("text_cond_proj_512x4608x53248")
-    run("text_cond_proj_512x4608x53248", d, X, Wq, sw, inv, "bias")
-    dp = W.make_workload("text_cond_proj_512x4608x53248", padded=True)
-    run("text_cond_proj_padded_4608x4608x53248", dp, to_dev(dp["X"]), Wq, sw, inv, "bias")
-    del d, dp, X, Wq
-    for name in ("qk_proj_headnorm_16896x4608x4608", "qk_proj_headnorm_6037x4608x4608"):
-        d, X, Wq, sw, inv = prep(name)
-        run(name, d, X, Wq, sw, inv, "head_rmsnorm", gamma=to_dev(d["gamma"]), eps=d["eps"])
+    if want("dit_ffn_gate_up_4608x24576x4608"):
+        run("dit_ffn_gate_up_4608x24576x4608", d, X, Wq, sw, inv, "silu_gate", extra=down)
+        del d, X, Wq, Wd
+    if want("text_cond_proj_512x4608x53248") or want("text_cond_proj_padded_4608x4608x53248"):
+        d, X, Wq, sw, inv = prep("text_cond_proj_512x4608x53248")
+        if want("text_cond_proj_512x4608x53248"):
+            run("text_cond_proj_512x4608x53248", d, X, Wq, sw, inv, "bias")
+        if want("text_cond_proj_padded_4608x4608x53248"):
+            dp = W.make_workload("text_cond_proj_512x4608x53248", padded=True)
+            run("text_cond_proj_padded_4608x4608x53248", dp, to_dev(dp["X"]), Wq, sw, inv, "bias")
+            del dp
         del d, X, Wq
+    for name in ("qk_proj_headnorm_16896x4608x4608", "qk_proj_headnorm_6037x4608x4608"):
+        if want(name):
+            d, X, Wq, sw, inv = prep(name)
+            run(name, d, X, Wq, sw, inv, "head_rmsnorm", gamma=to_dev(d["gamma"]), eps=d["eps"])
+            del d, X, Wq
     torch.cuda.empty_cache()
     return res
 
@@ -380,6 +412,13 @@ def main():
         sys.exit(1)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.only is not None and args.only != "dit_attn_proj_4608x4608x4608":
+        if args.only not in EXTRA_WORKLOADS:
+            print(json.dumps({"error": f"unknown workload {args.only}", "workloads": list(EXTRA_WORKLOADS)}),
+                  flush=True)
+            sys.exit(2)
+        print(json.dumps({"workload": args.only, **extra_workloads(args, args.only)[args.only]}), flush=True)
         return
     out, d = headline(args)
     log(f"headline: {out['value']} TOPS ({out['pct_int8_peak']}% of INT8 peak), {out['ms_per_step']} ms/step")

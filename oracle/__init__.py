@@ -53,6 +53,7 @@ def lib():
             "oracle_epilogue": ([P, I64, I64, P, P, P, I, P, I64, F, P, I64], None),
             "oracle_linear_rows": ([P, P, P, P, P, P, I64, I64, I64, I, P, I64, F, P, I64, P], None),
             "oracle_bf16_gemm_rows": ([P, P, P, P, I64, I64, I64, P, P], None),
+            "oracle_adaln_modulate": ([P, I64, I64, I64, P, P, F, P], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -195,3 +196,19 @@ def bf16_gemm_rows(H, W, bias=None, rows=None, want_f32=False):
     Zf = np.empty((nr, N), np.float32) if want_f32 else None
     lib().oracle_bf16_gemm_rows(_p(H), _p(W), _p(_c(bias, np.uint16)), _p(r), nr, N, K, _p(Z), _p(Zf))
     return (Z, Zf) if want_f32 else Z
+
+
+def adaln_modulate(X, shift=None, scale=None, eps: float = 1e-6) -> np.ndarray:
+    """bf16 [M,K] = bf16(LayerNorm(X) * (1 + scale) + shift), the input of the next linear."""
+    X = _c(X, np.uint16)
+    M, K = X.shape
+    H = np.empty((M, K), np.uint16)
+    lib().oracle_adaln_modulate(_p(X), M, K, K, _p(_c(shift, np.uint16)), _p(_c(scale, np.uint16)), eps, _p(H))
+    return H
+
+
+def adaln_quantize(X, shift, scale, inv_lambda, eps: float = 1e-6):
+    """The fused producer's three outputs on the CPU: (Xq, x_scale, H)."""
+    H = adaln_modulate(X, shift, scale, eps)
+    Xq, sx = quantize_rows(H, inv_lambda)
+    return Xq, sx, H

@@ -34,6 +34,13 @@
  *     one gamma of head_dim entries shared by all heads.
  *   - bf16 GEMM (the protected layer kept unquantized): exact products summed in fp64,
  *     plus bias, rounded to fp32 and then to bf16.
+ *   - adaLN before a quantized linear ([PTQ] related work: the modulation is generated at
+ *     run time; [FAL]: the small op around a matmul is fused): a LayerNorm over the row
+ *     without a learned affine, mean and biased variance summed in fp64 and rounded to fp32,
+ *     r = 1 / sqrtf(var + eps), n = (x - mean) * r, h = bf16(n * (1 + scale_j) + shift_j),
+ *     with one shift and one scale vector for all rows; h then goes through the per-token
+ *     quantizer above.  Parity unpinned by the pages (they do not print the norm); pinned by
+ *     closed forms and invariants in the tests.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math (no intrinsics, no SIMD pragmas).
  * Floating point: every fp32 operation is IEEE round-to-nearest-even, as written.
@@ -358,4 +365,43 @@ void oracle_bf16_gemm_rows(const uint16_t* H, const uint16_t* W, const uint16_t*
                            int64_t nrows, int64_t N, int64_t K, uint16_t* Z, float* Zf) {
     bgemm_ctx c = {H, W, bias, rows, N, K, Z, Zf};
     parallel_rows(nrows, bgemm_rows, &c);
+}
+
+/* ---------------------------------------------------------------- O8: adaLN modulation */
+typedef struct {
+    const uint16_t* X; int64_t ldx; const uint16_t* shift; const uint16_t* scale; float eps; int64_t K;
+    uint16_t* H;
+} adaln_ctx;
+
+static void adaln_rows(void* p, int64_t r0, int64_t r1) {
+    adaln_ctx* c = (adaln_ctx*)p;
+    for (int64_t m = r0; m < r1; ++m) {
+        const uint16_t* x = c->X + m * c->ldx;
+        double sum = 0.0;
+        for (int64_t j = 0; j < c->K; ++j) sum += (double)oracle_bf16_to_f32(x[j]);
+        double mean = sum / (double)c->K;
+        double ss = 0.0;
+        for (int64_t j = 0; j < c->K; ++j) {
+            double d = (double)oracle_bf16_to_f32(x[j]) - mean;
+            ss += d * d;
+        }
+        float mu = (float)mean;
+        float var = (float)(ss / (double)c->K);
+        float r = 1.0f / sqrtf(var + c->eps);
+        uint16_t* h = c->H + m * c->K;
+        for (int64_t j = 0; j < c->K; ++j) {
+            float n = (oracle_bf16_to_f32(x[j]) - mu) * r;
+            float g = 1.0f + (c->scale ? oracle_bf16_to_f32(c->scale[j]) : 0.0f);
+            float b = c->shift ? oracle_bf16_to_f32(c->shift[j]) : 0.0f;
+            h[j] = oracle_f32_to_bf16(n * g + b);
+        }
+    }
+}
+
+/* H = bf16(LayerNorm(X) * (1 + scale) + shift) per row; shift / scale [K] bf16 or NULL (0).
+ * H is [M, K] row-major.  The activations for the next linear are quantize_rows(H, inv_lambda). */
+void oracle_adaln_modulate(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, const uint16_t* shift,
+                           const uint16_t* scale, float eps, uint16_t* H) {
+    adaln_ctx c = {X, ldx, shift, scale, eps, K, H};
+    parallel_rows(M, adaln_rows, &c);
 }

@@ -351,6 +351,76 @@ def test_head_rmsnorm_closed_forms():
     assert np.allclose(Y2[0], g * 1e-6 / np.sqrt(1e-2 + 1e-12), rtol=2 ** -7)
 
 
+# ----------------------------------------------------------------------------- adaLN producer
+def _ln_fp64(x, shift, scale, eps):
+    """LayerNorm over each row in fp64 (biased variance), then x (1 + scale) + shift."""
+    x = f32(x).astype(np.float64)
+    mu = x.mean(axis=1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=1, keepdims=True)
+    n = (x - mu) / np.sqrt(var + eps)
+    sc = 0.0 if scale is None else f32(scale).astype(np.float64)
+    sh = 0.0 if shift is None else f32(shift).astype(np.float64)
+    return n * (1.0 + sc) + sh
+
+
+@pytest.mark.parametrize("K", [16, 256, 4608])
+def test_adaln_matches_fp64_layernorm(K):
+    rng = np.random.default_rng(20 + K)
+    M = 12
+    x = rng.standard_normal((M, K))
+    x[:, rng.integers(0, K, max(1, K // 100))] *= 30.0          # outlier channels
+    x[3] *= 1e-3                                                  # variance ~ eps: eps must count
+    x[4] += 7.0                                                   # mean far from 0
+    x[5] = np.abs(x[5])                                           # one-signed row
+    X = bf(x)
+    shift, scale = bf(0.3 * rng.standard_normal(K)), bf(0.5 * rng.standard_normal(K))
+    for sh, sc in ((shift, scale), (None, None), (shift, None), (None, scale)):
+        H = oracle.adaln_modulate(X, sh, sc, 1e-6)
+        ref = _ln_fp64(X, sh, sc, 1e-6)
+        # fp32 intermediates cost far less than half a bf16 ulp; the final rounding at most half an ulp
+        assert np.all(ulp_dist_bf16(H, bf(ref)) <= 1)
+        # the reference itself rounds to H on almost every element (not a 1-ulp drift everywhere)
+        assert np.mean(ulp_dist_bf16(H, bf(ref)) == 0) > 0.99
+
+
+def test_adaln_constant_rows_give_shift_exactly():
+    K = 64
+    rng = np.random.default_rng(21)
+    X = bf(np.repeat(np.array([[0.0], [3.25], [-1e4], [1e-20]]), K, axis=1))
+    shift, scale = bf(rng.standard_normal(K)), bf(rng.standard_normal(K))
+    H = oracle.adaln_modulate(X, shift, scale, 1e-6)
+    assert np.array_equal(H, np.broadcast_to(shift, H.shape))    # x - mean == 0 exactly
+    H0 = oracle.adaln_modulate(X, None, scale, 1e-6)
+    assert not f32(H0).any()
+
+
+@pytest.mark.parametrize("k", [-6, 3])
+def test_adaln_power_of_two_scaling_invariance(k):
+    """With eps = 0 every step scales exactly by 2^k, so LayerNorm(2^k x) == LayerNorm(x) bit for bit."""
+    rng = np.random.default_rng(22)
+    X = bf(rng.standard_normal((6, 512)) * 4)
+    X2 = bf(f32(X).astype(np.float64) * 2.0 ** k)
+    assert np.array_equal(f32(X2).astype(np.float64), f32(X).astype(np.float64) * 2.0 ** k)
+    shift, scale = bf(rng.standard_normal(512)), bf(rng.standard_normal(512))
+    assert np.array_equal(oracle.adaln_modulate(X, shift, scale, 0.0), oracle.adaln_modulate(X2, shift, scale, 0.0))
+
+
+def test_adaln_quantize_is_the_quantizer_on_h():
+    """The fused producer's int8 codes are the per-token quantizer applied to H: checked here on
+    H with a power-of-two row maximum, where the scale is exact and the codes are known."""
+    K = 256
+    X = np.zeros((2, K))
+    X[:, 0], X[:, 1] = 1.0, -1.0          # mean 0, var 2/K: n = +-sqrt(K/2) = +-11.3137...
+    shift = bf(np.zeros(K))
+    scale = bf(np.zeros(K))
+    Xq, sx, H = oracle.adaln_quantize(bf(X), shift, scale, None, 0.0)
+    n = f32(H)
+    assert n[0, 0] == -n[0, 1] and abs(n[0, 0] - math.sqrt(K / 2)) <= math.sqrt(K / 2) * 2.0 ** -8
+    assert np.all(n[:, 2:] == 0)
+    assert np.all(Xq[:, 0] == 127) and np.all(Xq[:, 1] == -127) and not Xq[:, 2:].any()
+    assert np.all(sx == np.float32(n[0, 0]) / np.float32(127.0))
+
+
 def test_bf16_gemm_within_fp64_bound():
     rng = np.random.default_rng(14)
     M, N, K = 9, 13, 512

@@ -284,7 +284,7 @@ def cpu_baseline(d):
 
 EXTRA_WORKLOADS = ("dit_ffn_gate_up_4608x24576x4608", "text_cond_proj_512x4608x53248",
                    "text_cond_proj_padded_4608x4608x53248", "qk_proj_headnorm_16896x4608x4608",
-                   "qk_proj_headnorm_6037x4608x4608")
+                   "qk_proj_headnorm_6037x4608x4608", "adaln_quantize_4608x4608", "adaln_quantize_16896x4608")
 
 
 def extra_workloads(args, only=None):
@@ -391,8 +391,58 @@ def extra_workloads(args, only=None):
             d, X, Wq, sw, inv = prep(name)
             run(name, d, X, Wq, sw, inv, "head_rmsnorm", gamma=to_dev(d["gamma"]), eps=d["eps"])
             del d, X, Wq
+    for M in (4608, 16896):
+        name = f"adaln_quantize_{M}x4608"
+        if want(name):
+            res[name] = adaln_producer(M, 4608, counts)
     torch.cuda.empty_cache()
     return res
+
+
+def adaln_producer(M, K, counts):
+    """The producer-fused quantizer (adaLN + per-token INT8 in one pass) against the same work
+    unfused (the adaLN writing bf16 h, then the quantizer reading it), on 6 rotating X buffers."""
+    import torch
+
+    import qdt_workloads as W
+    import quantized_diffusion_transformer_amd as qdt
+    d = W.make_adaln(M, K)
+    X0 = to_dev(d["X"])
+    shift, scale = to_dev(d["shift"]), to_dev(d["scale"])
+    H = qdt.adaln_modulate(X0, shift, scale)
+    Wq, sw, inv, _ = qdt.smooth_prepare(to_dev(d["W"]), qdt.channel_absmax(H))
+    Xs = [X0] + [X0.clone() for _ in range(5)]
+    Xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sx = torch.empty(M, dtype=torch.float32, device="cuda")
+    it = [0]
+
+    def fused(_, ev):
+        it[0] += 1
+        if ev is not None:
+            ev[0].record()
+        qdt.adaln_quantize(Xs[it[0] % 6], shift, scale, inv, Xq=Xq, x_scale=sx)
+        if ev is not None:
+            ev[1].record()
+            ev[2].record()
+
+    def unfused(_, ev):
+        it[0] += 1
+        if ev is not None:
+            ev[0].record()
+        qdt.adaln_modulate(Xs[it[0] % 6], shift, scale, H=H)
+        if ev is not None:
+            ev[1].record()
+        qdt.quantize_per_token(H, inv, Xq, sx)
+        if ev is not None:
+            ev[2].record()
+    steps, warm = counts(fused)
+    tf, _, _ = time_loop(fused, [None], steps, warm)
+    tu, t_ln, t_q = time_loop(unfused, [None], steps, warm)
+    b = 3 * M * K + 4 * M + 4 * K + 4 * K
+    return {"M": M, "K": K, "steps": steps, "warmup": warm, "fused_ms": round(tf, 4),
+            "fused_gbs": round(b / (tf * 1e-3) / 1e9, 1), "fused_frac_hbm": round(b / (tf * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "unfused_ms": round(tu, 4), "unfused_adaln_ms": round(stats(t_ln)["mean"], 4),
+            "unfused_quantize_ms": round(stats(t_q)["mean"], 4), "speedup": round(tu / tf, 3)}
 
 
 def main():

@@ -144,6 +144,35 @@ qdt_status qdt_smooth_prepare(const uint16_t* W, const float* s, int64_t N, int6
 qdt_status qdt_quantize_per_token(const uint16_t* X, const float* inv_lambda, int64_t M, int64_t K,
                                   int64_t ldx, int8_t* Xq, float* x_scale, void* stream);
 
+/* Largest K of qdt_adaln_quantize (one wavefront holds a row). */
+#define QDT_MAX_ADALN_K 8192
+
+/*
+ * Producer-fused quantization: the adaptive LayerNorm in front of a quantized linear in a DiT
+ * block, and the per-token quantizer of that linear's input, in one pass over each row.  With
+ * Xq and x_scale both NULL only H is written (the adaLN alone, for a bf16 consumer).
+ * ([PTQ] related work: the adaLN modulation is generated at run time, so it cannot be folded
+ * into the weights offline; [FAL] fused-epilogue paragraph: the small op next to a large one is
+ * fused so its input never makes a round trip through memory.)  Per row m of X:
+ *   mean = sum_j x_j / K;  var = sum_j (x_j - mean)^2 / K   (fp64 sums in any order, rounded to fp32)
+ *   r = 1 / sqrtf(var + eps);  n_j = (x_j - mean) * r
+ *   h_j = bf16(n_j * (1 + scale_j) + shift_j)               (fp32, no contraction, one rounding)
+ *   then x_scale[m] and Xq[m][:] exactly as qdt_quantize_per_token of h with inv_lambda.
+ *   X: bf16 [M, ldx] (first K columns), the residual stream.  shift, scale: bf16 [K] modulation
+ *   vectors shared by all rows (NULL = 0).  inv_lambda: fp32 [K] of the consumer linear (NULL =
+ *   no smoothing).  eps > 0.
+ *   Outputs: Xq int8 [M, K], x_scale fp32 [M], and H bf16 [M, K] (the h values) when not NULL.
+ *   K % 64 == 0 and K <= QDT_MAX_ADALN_K; ldx >= K, ldx % 8 == 0; pointers 16-byte aligned; no
+ *   output may overlap an input or another output.  QDT_EINVAL for eps <= 0 or not finite, for
+ *   only one of Xq / x_scale, or for no output at all.
+ *   mean and var match the fp64 definition rounded to fp32 except on rare near-ties of that
+ *   rounding, where h may differ by 1 bf16 ulp.  Xq and x_scale are bit-exact functions of h.
+ *   M = 0 is a no-op.
+ */
+qdt_status qdt_adaln_quantize(const uint16_t* X, int64_t ldx, const uint16_t* shift, const uint16_t* scale, float eps,
+                              const float* inv_lambda, int64_t M, int64_t K, int8_t* Xq, float* x_scale,
+                              uint16_t* H, void* stream);
+
 /* The plan qdt_w8a8_linear uses for this problem (pure host computation, no device call). */
 qdt_status qdt_w8a8_linear_plan(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, qdt_linear_plan* plan);
 

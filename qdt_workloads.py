@@ -31,6 +31,7 @@ import numpy as np
 
 # tensor ids for SeedSequence([seed, tensor_id])
 _TID_X, _TID_W, _TID_BIAS, _TID_GAMMA, _TID_WDOWN, _TID_OUTCH, _TID_OUTF = 1, 2, 3, 4, 5, 6, 7
+_TID_SHIFT, _TID_SCALE = 8, 9
 
 BASE_SEED = 1000  # the fixed generation seed of the INT8/GGUF quantization paper's setup
 
@@ -182,3 +183,14 @@ def make_workload(name: str, M: int | None = None, padded: bool = False) -> dict
                               cfg["down_sigma"], tensor_id=_TID_WDOWN)
     d["name"] = name
     return d
+
+
+def make_adaln(M: int, K: int, seed: int = BASE_SEED + 1, x_kind: str = "pct1", shift_sigma: float = 0.25,
+               scale_sigma: float = 0.5, w_sigma: float = 0.015) -> dict:
+    """Inputs of the adaLN producer in front of a quantized linear: the residual stream X (the
+    attention projection's recipe and seed by default), the run-time modulation vectors shift
+    and scale [K] (a synthetic choice: the pages print no values), and a weight W [K, K] of the
+    consumer linear whose column max-abs enters the smoothing vector."""
+    return dict(M=M, K=K, seed=seed, X=activations(M, K, seed, x_kind),
+                shift=vector(K, seed, _TID_SHIFT, shift_sigma), scale=vector(K, seed, _TID_SCALE, scale_sigma),
+                W=weights(K, K, seed, w_sigma))

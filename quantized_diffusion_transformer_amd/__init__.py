@@ -29,6 +29,7 @@ QDT_OK, QDT_EINVAL, QDT_ESHAPE, QDT_EALIGN, QDT_EWORKSPACE, QDT_EALIAS, QDT_EHIP
 QDT_EPI_BIAS, QDT_EPI_SILU_GATE, QDT_EPI_HEAD_RMSNORM, QDT_EPI_ACC_I32 = range(4)
 QDT_TILE_AUTO, QDT_TILE_256, QDT_TILE_288, QDT_TILE_288x256 = -1, 0, 1, 2
 QDT_MAX_K = 131072
+QDT_MAX_ADALN_K = 8192
 
 EPILOGUES = {"bias": QDT_EPI_BIAS, "silu_gate": QDT_EPI_SILU_GATE, "head_rmsnorm": QDT_EPI_HEAD_RMSNORM,
              "acc_i32": QDT_EPI_ACC_I32}
@@ -54,6 +55,7 @@ _SIGS = {
     "qdt_channel_absmax": ([_P, _I64, _I64, _I64, _P, _I, _P], _I),
     "qdt_smooth_prepare": ([_P, _P, _I64, _I64, _F, _P, _P, _P, _P, _P], _I),
     "qdt_quantize_per_token": ([_P, _P, _I64, _I64, _I64, _P, _P, _P], _I),
+    "qdt_adaln_quantize": ([_P, _I64, _P, _P, _F, _P, _I64, _I64, _P, _P, _P, _P], _I),
     "qdt_w8a8_linear_plan": ([_I64, _I64, _I64, _I, C.POINTER(qdt_linear_plan)], _I),
     "qdt_w8a8_linear_plan_for": ([_I64, _I64, _I64, _I, C.c_int32, C.c_int32, C.POINTER(qdt_linear_plan)], _I),
     "qdt_w8a8_linear_workspace_size": ([_I64, _I64, _I64, _I, C.POINTER(_SZ)], _I),
@@ -153,6 +155,42 @@ def quantize_per_token(X: torch.Tensor, inv_lambda: torch.Tensor | None, Xq=None
     _check(qdt_quantize_per_token(_ptr(X), _ptr(inv_lambda), M, K, ldx, _ptr(Xq), _ptr(x_scale), _stream(stream)),
            "qdt_quantize_per_token")
     return Xq, x_scale
+
+
+def adaln_quantize(X: torch.Tensor, shift: torch.Tensor | None, scale: torch.Tensor | None,
+                   inv_lambda: torch.Tensor | None, eps: float = 1e-6, Xq=None, x_scale=None, H=None,
+                   want_h: bool = False, stream=None):
+    """adaLN of bf16 X [M, K] (LayerNorm, * (1 + scale) + shift) fused with the per-token INT8 of
+    the result for the next linear.  Returns (Xq, x_scale), or (Xq, x_scale, H) when ``want_h`` or
+    ``H`` is given (H: bf16 [M, K], the modulated activations)."""
+    _dev(X, torch.bfloat16, "X")
+    X, ldx = _rows(X, "X")
+    M, K = X.shape
+    for t, n in ((shift, "shift"), (scale, "scale")):
+        if t is not None:
+            _dev(t, torch.bfloat16, n)
+    if Xq is None:
+        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(M, dtype=torch.float32, device=X.device)
+    if H is None and want_h:
+        H = torch.empty((M, K), dtype=torch.bfloat16, device=X.device)
+    _check(qdt_adaln_quantize(_ptr(X), ldx, _ptr(shift), _ptr(scale), float(eps), _ptr(inv_lambda), M, K, _ptr(Xq),
+                              _ptr(x_scale), _ptr(H), _stream(stream)), "qdt_adaln_quantize")
+    return (Xq, x_scale) if H is None else (Xq, x_scale, H)
+
+
+def adaln_modulate(X: torch.Tensor, shift: torch.Tensor | None, scale: torch.Tensor | None, eps: float = 1e-6,
+                   H=None, stream=None) -> torch.Tensor:
+    """adaLN alone: bf16 H [M, K] = bf16(LayerNorm(X) * (1 + scale) + shift), for a bf16 consumer."""
+    _dev(X, torch.bfloat16, "X")
+    X, ldx = _rows(X, "X")
+    M, K = X.shape
+    if H is None:
+        H = torch.empty((M, K), dtype=torch.bfloat16, device=X.device)
+    _check(qdt_adaln_quantize(_ptr(X), ldx, _ptr(shift), _ptr(scale), float(eps), None, M, K, None, None, _ptr(H),
+                              _stream(stream)), "qdt_adaln_quantize")
+    return H
 
 
 def linear_plan(M: int, N: int, K: int, epilogue: str = "bias", tile: int | None = None,

@@ -160,6 +160,33 @@ qdt_status qdt_quantize_per_token(const uint16_t* X, const float* inv_lambda, in
     return hip_status(launch_quant_rows(X, ldx, inv_lambda, M, K, Xq, x_scale, reinterpret_cast<hipStream_t>(stream)));
 }
 
+qdt_status qdt_adaln_quantize(const uint16_t* X, int64_t ldx, const uint16_t* shift, const uint16_t* scale, float eps,
+                              const float* inv_lambda, int64_t M, int64_t K, int8_t* Xq, float* x_scale, uint16_t* H,
+                              void* stream) {
+    if (M < 0) return QDT_ESHAPE;
+    if (!(eps > 0.0f) || !(eps < INFINITY)) return QDT_EINVAL;
+    // Xq and x_scale together, or neither (then only H is written, and H is required)
+    if (M > 0 && (!X || (!Xq != !x_scale) || (!Xq && !H))) return QDT_EINVAL;
+    if (K <= 0 || K % 64 != 0 || K > QDT_MAX_ADALN_K || ldx < K || M > INT32_MAX) return QDT_ESHAPE;
+    if (!aligned16(X) || !aligned16(shift) || !aligned16(scale) || !aligned16(inv_lambda) || !aligned16(Xq) ||
+        !aligned16(x_scale) || !aligned16(H) || ldx % 8 != 0)
+        return QDT_EALIGN;
+    if (M == 0) return QDT_OK;
+    const int64_t xb = ((M - 1) * ldx + K) * 2;
+    struct Span { const void* p; int64_t n; };
+    const Span in[4] = {{X, xb}, {shift, shift ? K * 2 : 0}, {scale, scale ? K * 2 : 0},
+                        {inv_lambda, inv_lambda ? K * 4 : 0}};
+    const Span out[3] = {{Xq, M * K}, {x_scale, M * 4}, {H, H ? M * K * 2 : 0}};
+    for (const Span& o : out) {
+        for (const Span& i : in)
+            if (overlap(o.p, o.n, i.p, i.n)) return QDT_EALIAS;
+        for (const Span& o2 : out)
+            if (&o2 != &o && overlap(o.p, o.n, o2.p, o2.n)) return QDT_EALIAS;
+    }
+    return hip_status(launch_adaln_quant(X, ldx, shift, scale, eps, inv_lambda, M, K, Xq, x_scale, H,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
 static int epi_kind(qdt_epilogue e) {
     switch (e) {
         case QDT_EPI_BIAS: return EPI_BIAS;

@@ -17,6 +17,11 @@ hipError_t launch_lambda(const float* s, float* lam_inout, float* inv, int64_t K
 // Per-row symmetric INT8 of X[m][:K] * colmul (colmul may be null).
 hipError_t launch_quant_rows(const uint16_t* X, int64_t ldx, const float* colmul, int64_t M, int64_t K, int8_t* Q,
                              float* scale, hipStream_t st);
+// adaLN (LayerNorm, * (1 + scale) + shift, bf16) of X's rows fused with the per-row INT8 of the
+// result times colmul; H (bf16 [M, K]) is written when not null.  K <= 8192.
+hipError_t launch_adaln_quant(const uint16_t* X, int64_t ldx, const uint16_t* shift, const uint16_t* scale, float eps,
+                              const float* colmul, int64_t M, int64_t K, int8_t* Q, float* xscale, uint16_t* H,
+                              hipStream_t st);
 
 // ------------------------------------------------------------------ GEMM
 enum EpiKind { EPI_BIAS = 0, EPI_SILU = 1, EPI_RMSNORM = 2, EPI_ACC = 3, EPI_PARTIAL = 4, EPI_F32BIAS = 5 };

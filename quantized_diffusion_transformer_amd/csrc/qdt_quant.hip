@@ -296,4 +296,203 @@ hipError_t launch_quant_rows(const uint16_t* X, int64_t ldx, const float* colmul
     return launch_quant_cfg<16, 16>(X, ldx, colmul, M, K, Q, scale, st);
 }
 
+// ---------------------------------------------------------------------------- adaLN + INT8
+// Producer-fused quantization: the adaptive LayerNorm in front of a quantized linear of a DiT
+// block, with the per-token quantizer of that linear's input in the same pass over the row.
+// ("Quantizing a Dual-Branch Flow-Matching DiT", related work: the adaLN modulation is
+// generated at run time; "Serving sub-second Ideogram v4", fused-epilogue paragraph: the
+// small op next to a large one belongs in the same kernel, without a round trip to memory.)
+//   mean = sum_j x_j / K,  var = sum_j (x_j - mean)^2 / K
+//   r = 1 / sqrtf(var + eps),  n_j = (x_j - mean) * r,  h_j = bf16(n_j * (1 + scale_j) + shift_j)
+//   v_j = h_j * inv_lambda_j,  x_scale = max |v| / 127,  q_j = rne(v_j / x_scale) clamped to +-127
+// mean and var: sum x and sum x^2 in fp64 (one pass), var = sum x^2 / K - mean^2, both rounded
+// to fp32.  The fp64 rounding errors stay far below the fp32 rounding of the results, so these
+// are the correctly rounded fp32 statistics except on rare near-ties, whatever the order.
+// One wave per row (K <= 8192), 8 waves per block.  The block stages inv_lambda (1 when absent),
+// 1 + scale and shift (0 when absent) as fp32 in LDS, 12 K bytes; 1 + scale is rounded exactly
+// as in the definition.  The row stays in registers from the load to the last store: X is read
+// once, Xq (and H on request) written once.  The kernel is bound by VALU issue more than by HBM
+// (about 20 operations per element).
+constexpr int kAdalnWaves = 8;
+
+template <int C, bool QUANT>
+__global__ __launch_bounds__(kAdalnWaves * 64) void adaln_quant_kernel(
+    const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ shift,
+    const uint16_t* __restrict__ scale, float eps, const float* __restrict__ colmul, int64_t M, int64_t K,
+    int8_t* __restrict__ Q, float* __restrict__ xscale, uint16_t* __restrict__ H) {
+    extern __shared__ __attribute__((aligned(16))) float smem_f[];
+    float* smul = smem_f;      // K: inv_lambda
+    float* sg = smem_f + K;    // K: 1 + scale
+    float* sb = sg + K;        // K: shift
+    const int lane = threadIdx.x & 63;
+    const int64_t nch = K >> 3;
+    for (int64_t j = threadIdx.x; j < nch; j += blockDim.x) {
+        float4 m0 = make_float4(1.0f, 1.0f, 1.0f, 1.0f), m1 = m0;
+        if (colmul) {
+            m0 = *reinterpret_cast<const float4*>(colmul + j * 8);
+            m1 = *reinterpret_cast<const float4*>(colmul + j * 8 + 4);
+        }
+        *reinterpret_cast<float4*>(smul + j * 8) = m0;
+        *reinterpret_cast<float4*>(smul + j * 8 + 4) = m1;
+        const uint4 sc = scale ? *reinterpret_cast<const uint4*>(scale + j * 8) : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 sh = shift ? *reinterpret_cast<const uint4*>(shift + j * 8) : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w}, shw[4] = {sh.x, sh.y, sh.z, sh.w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            sg[j * 8 + 2 * p] = 1.0f + bf16_to_f32(scw[p] & 0xFFFFu);
+            sg[j * 8 + 2 * p + 1] = 1.0f + __uint_as_float(scw[p] & 0xFFFF0000u);
+            sb[j * 8 + 2 * p] = bf16_to_f32(shw[p] & 0xFFFFu);
+            sb[j * 8 + 2 * p + 1] = __uint_as_float(shw[p] & 0xFFFF0000u);
+        }
+    }
+    __syncthreads();
+    auto lds8 = [&](const float* base, int64_t j, float (&o)[8]) __attribute__((always_inline)) {
+        const float4 a = *reinterpret_cast<const float4*>(base + j * 8);
+        const float4 b = *reinterpret_cast<const float4*>(base + j * 8 + 4);
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    };
+    const int64_t row0 = (int64_t)blockIdx.x * kAdalnWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t rstep = (int64_t)gridDim.x * kAdalnWaves;
+    for (int64_t row = row0; row < M; row += rstep) {
+        const uint16_t* x = X + row * ldx;
+        uint4 raw[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int64_t j = lane + (int64_t)c * 64;
+            raw[c] = j < nch ? *reinterpret_cast<const uint4*>(x + j * 8) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        // element e of chunk c (bf16 pairs, low half first)
+        auto elem = [&](int c, int e) __attribute__((always_inline)) {
+            const uint32_t ww[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
+            return (e & 1) ? __uint_as_float(ww[e >> 1] & 0xFFFF0000u) : bf16_to_f32(ww[e >> 1] & 0xFFFFu);
+        };
+        // statistics; padding chunks hold zeros and add nothing
+        double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double v = (double)elem(c, e);
+                s1 += v;
+                s2 = __builtin_fma(v, v, s2);
+            }
+        s1 = wave_sum64(s1);
+        s2 = wave_sum64(s2);
+        const double mean64 = s1 / (double)K;
+        const double var64 = __builtin_fmax(__builtin_fma(-mean64, mean64, s2 / (double)K), 0.0);
+        const float mean = (float)mean64;
+        const float r = 1.0f / sqrtf((float)var64 + eps);
+        // Each pass converts the packed row again (one shift or mask per element) instead of
+        // keeping 8 C fp32 values live across passes: an empty asm that "modifies" the packed
+        // registers stops the compiler from reusing conversions of the statistics pass.
+#pragma unroll
+        for (int c = 0; c < C; ++c) asm volatile("" : "+v"(raw[c].x), "+v"(raw[c].y), "+v"(raw[c].z), "+v"(raw[c].w));
+        // h = bf16(n * (1 + scale) + shift); v = h * inv_lambda
+        float amax = 0.0f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int64_t j = lane + (int64_t)c * 64;
+            if (j >= nch) continue;
+            float g[8], bb[8], mm[8];
+            lds8(sg, j, g);
+            lds8(sb, j, bb);
+            if constexpr (QUANT) lds8(smul, j, mm);
+            uint32_t hp[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float h0 = ((elem(c, 2 * p) - mean) * r) * g[2 * p] + bb[2 * p];
+                const float h1 = ((elem(c, 2 * p + 1) - mean) * r) * g[2 * p + 1] + bb[2 * p + 1];
+                hp[p] = pack_bf16x2(h0, h1);
+            }
+            raw[c] = make_uint4(hp[0], hp[1], hp[2], hp[3]);
+            if (H) *reinterpret_cast<uint4*>(H + row * K + j * 8) = raw[c];
+            if constexpr (QUANT) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(elem(c, e) * mm[e]));
+            }
+        }
+        if constexpr (!QUANT) continue;
+        amax = wave_max(amax);
+        const float sc = amax / 127.0f;
+        if (lane == 0) xscale[row] = sc;
+        int8_t* q = Q + row * K;
+        const bool fast = sc >= 1.17549435e-38f;
+        const float rcp = 1.0f / sc;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int64_t j = lane + (int64_t)c * 64;
+            if (j >= nch) continue;
+            if (amax == 0.0f) {
+                *reinterpret_cast<uint2*>(q + j * 8) = make_uint2(0u, 0u);
+                continue;
+            }
+            // v again from the packed h (keeping 8 C fp32 values live instead measured slower:
+            // fewer waves per SIMD)
+            float vc[8], mm[8];
+            lds8(smul, j, mm);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vc[e] = elem(c, e) * mm[e];
+            uint32_t b[8];
+            bool near = !fast;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float tq = vc[e] * rcp;
+                const float m = tq + kRoundMagic;
+                const float rr = m - kRoundMagic;
+                near |= fabsf(tq - rr) >= kNearTie;
+                b[e] = __float_as_uint(m);
+            }
+            if (near) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) b[e] = (uint32_t)quant_exact(vc[e], sc);
+            }
+            *reinterpret_cast<uint2*>(q + j * 8) =
+                make_uint2(pack_low_bytes(b[0], b[1], b[2], b[3]), pack_low_bytes(b[4], b[5], b[6], b[7]));
+        }
+    }
+}
+
+template <int C, bool QUANT>
+static hipError_t launch_adaln_cfg(const uint16_t* X, int64_t ldx, const uint16_t* shift, const uint16_t* scale,
+                                   float eps, const float* colmul, int64_t M, int64_t K, int8_t* Q, float* xscale,
+                                   uint16_t* H, hipStream_t st) {
+    const int threads = kAdalnWaves * 64;
+    const size_t lds = (size_t)K * 12;
+    static int per_cu = 0;  // for the largest LDS request of the configuration (K = 512 C)
+    if (per_cu == 0) {
+        int v = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, adaln_quant_kernel<C, QUANT>, threads,
+                                                                    (size_t)C * 512 * 12);
+        if (e != hipSuccess) return e;
+        per_cu = max(v, 1);
+    }
+    const int64_t units = (M + kAdalnWaves - 1) / kAdalnWaves;
+    const int64_t blocks = min(units, (int64_t)per_cu * kNumCU);
+    hipLaunchKernelGGL((adaln_quant_kernel<C, QUANT>), dim3((unsigned)blocks), dim3(threads), lds, st, X, ldx, shift,
+                       scale, eps, colmul, M, K, Q, xscale, H);
+    return hipGetLastError();
+}
+
+template <bool QUANT>
+static hipError_t launch_adaln(const uint16_t* X, int64_t ldx, const uint16_t* shift, const uint16_t* scale, float eps,
+                               const float* colmul, int64_t M, int64_t K, int8_t* Q, float* xscale, uint16_t* H,
+                               hipStream_t st) {
+    const int64_t nch = K / 8;
+    if (nch <= 64 * 1) return launch_adaln_cfg<1, QUANT>(X, ldx, shift, scale, eps, colmul, M, K, Q, xscale, H, st);
+    if (nch <= 64 * 2) return launch_adaln_cfg<2, QUANT>(X, ldx, shift, scale, eps, colmul, M, K, Q, xscale, H, st);
+    if (nch <= 64 * 4) return launch_adaln_cfg<4, QUANT>(X, ldx, shift, scale, eps, colmul, M, K, Q, xscale, H, st);
+    if (nch <= 64 * 6) return launch_adaln_cfg<6, QUANT>(X, ldx, shift, scale, eps, colmul, M, K, Q, xscale, H, st);
+    if (nch <= 64 * 9) return launch_adaln_cfg<9, QUANT>(X, ldx, shift, scale, eps, colmul, M, K, Q, xscale, H, st);
+    if (nch <= 64 * 12) return launch_adaln_cfg<12, QUANT>(X, ldx, shift, scale, eps, colmul, M, K, Q, xscale, H, st);
+    return launch_adaln_cfg<16, QUANT>(X, ldx, shift, scale, eps, colmul, M, K, Q, xscale, H, st);
+}
+
+hipError_t launch_adaln_quant(const uint16_t* X, int64_t ldx, const uint16_t* shift, const uint16_t* scale, float eps,
+                              const float* colmul, int64_t M, int64_t K, int8_t* Q, float* xscale, uint16_t* H,
+                              hipStream_t st) {
+    if (M <= 0) return hipSuccess;
+    if (Q) return launch_adaln<true>(X, ldx, shift, scale, eps, colmul, M, K, Q, xscale, H, st);
+    return launch_adaln<false>(X, ldx, shift, scale, eps, colmul, M, K, Q, xscale, H, st);
+}
+
 }  // namespace qdt

@@ -53,6 +53,32 @@ def test_quantize_validation():
     assert f(A(), None, 0, 128, 128, A(0x20000), A(0x30000), None) == qdt.QDT_OK        # M = 0: no-op
 
 
+def test_adaln_quantize_validation():
+    f = qdt.qdt_adaln_quantize
+    outs = (A(0x200000), A(0x300000), A(0x400000))              # Xq, x_scale, H
+
+    def call(X=A(), ldx=128, shift=None, scale=None, eps=1e-6, inv=None, M=4, K=128, outs=outs):
+        return f(X, ldx, shift, scale, eps, inv, M, K, *outs, None)
+    assert call(K=100, ldx=100) == qdt.QDT_ESHAPE                      # K % 64
+    assert call(K=qdt.QDT_MAX_ADALN_K + 64, ldx=qdt.QDT_MAX_ADALN_K + 64,
+                outs=(A(0x2000000), A(0x3000000), None)) == qdt.QDT_ESHAPE  # one wave holds a row
+    assert call(ldx=64) == qdt.QDT_ESHAPE
+    assert call(M=-1) == qdt.QDT_ESHAPE
+    assert call(eps=0.0) == qdt.QDT_EINVAL
+    assert call(eps=float("nan")) == qdt.QDT_EINVAL
+    assert call(eps=float("inf")) == qdt.QDT_EINVAL
+    assert call(X=None) == qdt.QDT_EINVAL
+    assert call(X=A(0x10008)) == qdt.QDT_EALIGN
+    assert call(shift=A(0x500004)) == qdt.QDT_EALIGN
+    assert call(ldx=132) == qdt.QDT_EALIGN
+    assert call(outs=(A(0x10100), A(0x300000), None)) == qdt.QDT_EALIAS           # Xq inside X
+    assert call(outs=(A(0x200000), A(0x300000), A(0x200100))) == qdt.QDT_EALIAS    # H over Xq
+    assert call(inv=A(0x300000)) == qdt.QDT_EALIAS                                 # x_scale over inv_lambda
+    assert call(outs=(A(0x200000), None, A(0x400000))) == qdt.QDT_EINVAL           # Xq without x_scale
+    assert call(outs=(None, None, None)) == qdt.QDT_EINVAL                        # nothing to write
+    assert call(M=0) == qdt.QDT_OK
+
+
 def test_smooth_prepare_validation():
     f = qdt.qdt_smooth_prepare
     outs = (A(0x100000), A(0x200000), A(0x300000), A(0x400000))

@@ -54,6 +54,9 @@ def lib():
             "oracle_linear_rows": ([P, P, P, P, P, P, I64, I64, I64, I, P, I64, F, P, I64, P], None),
             "oracle_bf16_gemm_rows": ([P, P, P, P, I64, I64, I64, P, P], None),
             "oracle_adaln_modulate": ([P, I64, I64, I64, P, P, F, P], None),
+            "oracle_fp4_value": ([I], C.c_double),
+            "oracle_mxfp4_quantize_rows": ([P, P, I64, I64, I64, P, P], None),
+            "oracle_mxfp4_gemm_rows": ([P, P, P, P, P, P, I64, I64, I64, P, P], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -212,3 +215,40 @@ def adaln_quantize(X, shift, scale, inv_lambda, eps: float = 1e-6):
     H = adaln_modulate(X, shift, scale, eps)
     Xq, sx = quantize_rows(H, inv_lambda)
     return Xq, sx, H
+
+
+def fp4_value(code: int) -> float:
+    return float(lib().oracle_fp4_value(int(code)))
+
+
+def mxfp4_quantize(X, colmul=None):
+    """Block-scaled FP4 of bf16 X [M,K] (times colmul): (codes uint8 [M,K/2], exponents uint8 [M,K/32])."""
+    X = _c(X, np.uint16)
+    M, K = X.shape
+    Q = np.zeros((M, K // 2), np.uint8)
+    S = np.empty((M, K // 32), np.uint8)
+    lib().oracle_mxfp4_quantize_rows(_p(X), _p(_c(colmul, np.float32)), M, K, K, _p(Q), _p(S))
+    return Q, S
+
+
+def mxfp4_dequantize(Q, S) -> np.ndarray:
+    """fp64 values of block-scaled FP4 rows (for tests)."""
+    Q, S = np.asarray(Q, np.uint8), np.asarray(S, np.uint8)
+    codes = np.empty((Q.shape[0], Q.shape[1] * 2), np.int64)
+    codes[:, 0::2] = Q & 15
+    codes[:, 1::2] = Q >> 4
+    table = np.array([fp4_value(c) for c in range(16)])
+    return table[codes] * np.ldexp(1.0, np.repeat(S.astype(np.int64) - 127, 32, axis=1))
+
+
+def mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias=None, rows=None, want_acc=False):
+    """fp64 accumulators of the decoded product and Y = bf16((float)acc + bias) for the given rows."""
+    Xq, Xs, Wq, Ws = (_c(a, np.uint8) for a in (Xq, Xs, Wq, Ws))
+    N, K = Wq.shape[0], Wq.shape[1] * 2
+    r = None if rows is None else _c(rows, np.int64)
+    nr = Xq.shape[0] if r is None else r.size
+    Y = np.empty((nr, N), np.uint16)
+    acc = np.empty((nr, N), np.float64) if want_acc else None
+    lib().oracle_mxfp4_gemm_rows(_p(Xq), _p(Xs), _p(Wq), _p(Ws), _p(_c(bias, np.uint16)), _p(r), nr, N, K, _p(acc),
+                                 _p(Y))
+    return (Y, acc) if want_acc else Y

@@ -41,6 +41,15 @@
  *     with one shift and one scale vector for all rows; h then goes through the per-token
  *     quantizer above.  Parity unpinned by the pages (they do not print the norm); pinned by
  *     closed forms and invariants in the tests.
+ *   - Block-scaled 4-bit floating point ([FAL]: the DiT runs in a 4-bit floating-point format
+ *     with block scales; the pages name NVFP4 but print none of its parameters): the MXFP4
+ *     form native to the target GPU.  Blocks of 32 consecutive elements of a row share a
+ *     power-of-two scale 2^e with e = floor(log2(max |v|)) - 2 (the largest element magnitude,
+ *     6 = 1.5 * 2^2, has exponent 2), clamped to [-127, 127] and stored biased by 127 in a
+ *     byte; e = -127 for an all-zero block.  Each element is v / 2^e rounded to the nearest of
+ *     0, 0.5, 1, 1.5, 2, 3, 4, 6 (ties to the even 1-bit mantissa), magnitudes above 6 saturate
+ *     to 6, and the 4-bit code is sign << 3 | index with zero always +0.  Two codes per byte,
+ *     the even element in the low nibble.  The GEMM sums exact products of the decoded values.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math (no intrinsics, no SIMD pragmas).
  * Floating point: every fp32 operation is IEEE round-to-nearest-even, as written.
@@ -404,4 +413,109 @@ void oracle_adaln_modulate(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
                            const uint16_t* scale, float eps, uint16_t* H) {
     adaln_ctx c = {X, ldx, shift, scale, eps, K, H};
     parallel_rows(M, adaln_rows, &c);
+}
+
+/* ---------------------------------------------------------------- O9: MXFP4 (block-scaled FP4) */
+/* Magnitudes of the eight 4-bit codes 0..7: exponent field e (2 bits, bias 1) and mantissa m
+ * (1 bit): e = 0 gives m * 0.5, e > 0 gives (1 + m / 2) * 2^(e - 1). */
+double oracle_fp4_value(int code) {
+    int idx = code & 7, e = idx >> 1, m = idx & 1;
+    double mag = e == 0 ? 0.5 * m : (1.0 + 0.5 * m) * ldexp(1.0, e - 1);
+    return (code & 8) ? -mag : mag;
+}
+
+/* Nearest of the eight magnitudes to |t|, ties to the code with mantissa bit 0; saturates. */
+static int fp4_round_index(double a) {
+    int best = 0;
+    double bd = INFINITY;
+    for (int i = 0; i < 8; ++i) {
+        double d = fabs(a - oracle_fp4_value(i));
+        if (d < bd || (d == bd && (i & 1) == 0)) { bd = d; best = i; }
+    }
+    return best;
+}
+
+typedef struct {
+    const uint16_t* X; const float* colmul; int64_t K, ldx; uint8_t* q; uint8_t* s;
+} mx_ctx;
+
+static void mx_rows(void* p, int64_t r0, int64_t r1) {
+    mx_ctx* c = (mx_ctx*)p;
+    for (int64_t m = r0; m < r1; ++m) {
+        const uint16_t* x = c->X + m * c->ldx;
+        for (int64_t b = 0; b < c->K / 32; ++b) {
+            float v[32];
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                int64_t j = b * 32 + i;
+                float f = oracle_bf16_to_f32(x[j]);
+                v[i] = c->colmul ? f * c->colmul[j] : f;
+                if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+            }
+            int e = -127;
+            if (amax > 0.0f) {
+                int ex;
+                frexpf(amax, &ex);         /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+                e = (ex - 1) - 2;
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+            }
+            c->s[m * (c->K / 32) + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < 32; ++i) {
+                double t = ldexp((double)v[i], -e);  /* exact: a power-of-two scaling in fp64 */
+                int idx = fp4_round_index(fabs(t));
+                int code = idx == 0 ? 0 : ((t < 0.0 ? 8 : 0) | idx);
+                int64_t j = b * 32 + i;
+                uint8_t* qb = c->q + m * (c->K / 2) + j / 2;
+                if (j % 2 == 0) *qb = (uint8_t)code; else *qb = (uint8_t)(*qb | (code << 4));
+            }
+        }
+    }
+}
+
+/* Row m of X (times colmul when given): codes Q [M, K/2] and biased block exponents S [M, K/32]. */
+void oracle_mxfp4_quantize_rows(const uint16_t* X, const float* colmul, int64_t M, int64_t K, int64_t ldx,
+                                uint8_t* Q, uint8_t* S) {
+    mx_ctx c = {X, colmul, K, ldx, Q, S};
+    parallel_rows(M, mx_rows, &c);
+}
+
+/* Element j of a quantized row: code value times its block's power of two. */
+static double mx_elem(const uint8_t* q, const uint8_t* s, int64_t j) {
+    int code = (j % 2 == 0) ? (q[j / 2] & 15) : (q[j / 2] >> 4);
+    return ldexp(oracle_fp4_value(code), (int)s[j / 32] - 127);
+}
+
+typedef struct {
+    const uint8_t* Xq; const uint8_t* Xs; const uint8_t* Wq; const uint8_t* Ws; const uint16_t* bias;
+    const int64_t* rows; int64_t N, K; double* acc; uint16_t* Y;
+} mxg_ctx;
+
+static void mxg_rows(void* p, int64_t i0, int64_t i1) {
+    mxg_ctx* c = (mxg_ctx*)p;
+    for (int64_t i = i0; i < i1; ++i) {
+        int64_t m = c->rows ? c->rows[i] : i;
+        const uint8_t* xq = c->Xq + m * (c->K / 2);
+        const uint8_t* xs = c->Xs + m * (c->K / 32);
+        for (int64_t n = 0; n < c->N; ++n) {
+            const uint8_t* wq = c->Wq + n * (c->K / 2);
+            const uint8_t* ws = c->Ws + n * (c->K / 32);
+            double a = 0.0; /* products are exact; the fp64 sum rounds far below fp32 */
+            for (int64_t k = 0; k < c->K; ++k) a += mx_elem(xq, xs, k) * mx_elem(wq, ws, k);
+            if (c->acc) c->acc[i * c->N + n] = a;
+            if (c->Y) {
+                float b = c->bias ? oracle_bf16_to_f32(c->bias[n]) : 0.0f;
+                c->Y[i * c->N + n] = oracle_f32_to_bf16((float)a + b);
+            }
+        }
+    }
+}
+
+/* acc[i][n] = sum_k dec(X row rows[i], k) * dec(W row n, k) (fp64) and Y = bf16((float)acc + bias).
+ * rows == NULL computes every row; acc or Y may be NULL. */
+void oracle_mxfp4_gemm_rows(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                            const uint16_t* bias, const int64_t* rows, int64_t nrows, int64_t N, int64_t K,
+                            double* acc, uint16_t* Y) {
+    mxg_ctx c = {Xq, Xs, Wq, Ws, bias, rows, N, K, acc, Y};
+    parallel_rows(nrows, mxg_rows, &c);
 }

@@ -421,6 +421,112 @@ def test_adaln_quantize_is_the_quantizer_on_h():
     assert np.all(sx == np.float32(n[0, 0]) / np.float32(127.0))
 
 
+# ----------------------------------------------------------------------------- block-scaled FP4
+FP4_POS = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # the 2-bit-exponent, 1-bit-mantissa magnitudes
+
+
+def test_fp4_code_table():
+    vals = [oracle.fp4_value(c) for c in range(16)]
+    assert vals[:8] == FP4_POS
+    assert all(vals[8 + i] == -vals[i] for i in range(8))
+    # one binade per exponent step: the spacing doubles from [1, 2) to [2, 4) to [4, 8)
+    assert np.diff(FP4_POS[2:4]) == 0.5 and np.diff(FP4_POS[4:6]) == 1.0 and np.diff(FP4_POS[6:8]) == 2.0
+
+
+def _mx_block(vals):
+    """One 32-element bf16 row from up to 32 values (rest zero)."""
+    v = np.zeros(32, np.float32)
+    v[:len(vals)] = vals
+    return bf(v)[None, :]
+
+
+def test_mx_scale_rule_and_zero_blocks():
+    rng = np.random.default_rng(30)
+    x = rng.standard_normal((16, 256)) * 10.0 ** rng.integers(-6, 6, (16, 1))
+    x[3, 64:96] = 0.0                                        # an all-zero block
+    X = bf(x)
+    Q, S = oracle.mxfp4_quantize(X)
+    v = f32(X).astype(np.float64).reshape(16, 8, 32)
+    amax = np.abs(v).max(axis=2)
+    e = S.astype(np.int64) - 127
+    nz = amax > 0
+    ratio = amax[nz] / np.ldexp(1.0, e[nz])
+    assert np.all((ratio >= 4.0) & (ratio < 8.0))            # the block max lands in [4, 8)
+    assert S[3, 2] == 0 and not Q[3, 32:48].any()             # zero block: exponent -127, codes +0
+
+
+def test_mx_rounding_nearest_ties_even_and_saturation():
+    # block max 4 pins the exponent to 0 (scale 1), so every element is rounded as written
+    ties = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0, 5.0: 4.0}
+    sat = {6.5: 6.0, 7.75: 6.0}
+    t = list(ties) + list(sat) + [-0.25, -0.1, -5.0, 0.3, 0.7, 2.75, 4.5]
+    want = list(ties.values()) + list(sat.values()) + [0.0, 0.0, -4.0, 0.5, 0.5, 3.0, 4.0]
+    Q, S = oracle.mxfp4_quantize(_mx_block([4.0] + t))
+    assert S[0, 0] == 127
+    d = oracle.mxfp4_dequantize(Q, S)[0]
+    assert list(d[1:1 + len(t)]) == want
+    # negative values rounding to zero are stored as +0 (code 0)
+    j = 1 + len(ties) + len(sat)                                 # the -0.25 element
+    assert (Q[0, j // 2] >> (4 * (j % 2))) & 15 == 0
+    # dense check: the decoded value is a nearest representable value
+    rng = np.random.default_rng(31)
+    vals = np.sort(rng.uniform(-6, 6, 31).astype(np.float32))
+    Q, S = oracle.mxfp4_quantize(_mx_block(np.concatenate([[6.0], vals])))
+    d = oracle.mxfp4_dequantize(Q, S)[0][1:]
+    x = f32(bf(vals)).astype(np.float64)
+    grid = np.array(FP4_POS + [-v for v in FP4_POS[1:]])
+    best = np.abs(x[:, None] - grid[None, :]).min(axis=1)
+    assert np.all(np.abs(x - d) == best)
+
+
+def test_mx_nibble_order_and_lossless_values():
+    codes = np.arange(32) % 16
+    vals = np.array([oracle.fp4_value(c) for c in codes]) * 0.25   # block max 6 * 0.25 = 1.5 -> exponent -2
+    Q, S = oracle.mxfp4_quantize(_mx_block(vals))
+    assert S[0, 0] == 127 - 2
+    assert Q[0, 0] == (codes[0] | (codes[1] << 4)) and Q[0, 5] == (codes[10] | (codes[11] << 4))
+    assert np.array_equal(oracle.mxfp4_dequantize(Q, S)[0], vals)
+
+
+def test_mx_error_bound():
+    rng = np.random.default_rng(32)
+    X = bf(rng.standard_normal((8, 512)) * 3)
+    Q, S = oracle.mxfp4_quantize(X)
+    x = f32(X).astype(np.float64)
+    err = np.abs(oracle.mxfp4_dequantize(Q, S) - x)
+    unit = np.repeat(np.ldexp(1.0, S.astype(np.int64) - 127), 32, axis=1)
+    t = np.abs(x) / unit
+    # half the grid spacing inside [0, 6]; up to the distance to 6 above it
+    half = np.where(t < 2, 0.25, np.where(t < 4, 0.5, 1.0))
+    assert np.all(np.where(t <= 6, err <= half * unit, err <= (t - 6) * unit + 1e-300))
+
+
+def test_mx_column_multiplier_is_applied_first():
+    """Power-of-two multipliers are exact, so quantizing X * colmul equals quantizing the scaled X."""
+    rng = np.random.default_rng(34)
+    X = bf(rng.standard_normal((4, 128)))
+    mul = np.ldexp(1.0, rng.integers(-3, 4, 128)).astype(np.float32)
+    Xm = bf(f32(X) * mul)
+    assert np.array_equal(f32(Xm), f32(X) * mul)
+    for a, b in zip(oracle.mxfp4_quantize(X, mul), oracle.mxfp4_quantize(Xm)):
+        assert np.array_equal(a, b)
+    assert not np.array_equal(oracle.mxfp4_quantize(X, mul)[0], oracle.mxfp4_quantize(X)[0])
+
+
+def test_mx_gemm_exact_against_rationals():
+    from fractions import Fraction
+    rng = np.random.default_rng(33)
+    M, N, K = 3, 4, 64
+    Xq, Xs = oracle.mxfp4_quantize(bf(rng.standard_normal((M, K))))
+    Wq, Ws = oracle.mxfp4_quantize(bf(rng.standard_normal((N, K)) * 0.01))
+    _, acc = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, want_acc=True)
+    xd, wd = oracle.mxfp4_dequantize(Xq, Xs), oracle.mxfp4_dequantize(Wq, Ws)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(xd[m], wd[n]))
+            assert Fraction(float(acc[m, n])) == exact
+
+
 def test_bf16_gemm_within_fp64_bound():
     rng = np.random.default_rng(14)
     M, N, K = 9, 13, 512

@@ -29,6 +29,7 @@ METRIC = "W8A8 DiT linear effective TOPS at 4608³ (quant+GEMM+epilogue), % INT8
 PEAK_INT8_TOPS = 5000.0    # MI355X dense INT8 MFMA
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_FP4_TOPS = 10100.0    # MI355X dense FP4 MFMA
 
 
 def parse():
@@ -284,7 +285,8 @@ def cpu_baseline(d):
 
 EXTRA_WORKLOADS = ("dit_ffn_gate_up_4608x24576x4608", "text_cond_proj_512x4608x53248",
                    "text_cond_proj_padded_4608x4608x53248", "qk_proj_headnorm_16896x4608x4608",
-                   "qk_proj_headnorm_6037x4608x4608", "adaln_quantize_4608x4608", "adaln_quantize_16896x4608")
+                   "qk_proj_headnorm_6037x4608x4608", "adaln_quantize_4608x4608", "adaln_quantize_16896x4608",
+                   "mxfp4_attn_proj_4608x4608x4608", "mxfp4_ffn_up_4608x24576x4608")
 
 
 def extra_workloads(args, only=None):
@@ -395,8 +397,51 @@ def extra_workloads(args, only=None):
         name = f"adaln_quantize_{M}x4608"
         if want(name):
             res[name] = adaln_producer(M, 4608, counts)
+    for name, src in (("mxfp4_attn_proj_4608x4608x4608", "dit_attn_proj_4608x4608x4608"),
+                      ("mxfp4_ffn_up_4608x24576x4608", "dit_ffn_gate_up_4608x24576x4608")):
+        if want(name):
+            res[name] = mxfp4_workload(src, counts)
     torch.cuda.empty_cache()
     return res
+
+
+def mxfp4_workload(src, counts):
+    """Block-scaled FP4 on a workload's shapes and inputs: per step the activations are quantized
+    (qdt_mxfp4_quantize) and multiplied (qdt_mxfp4_linear, bias epilogue); weights offline."""
+    import torch
+
+    import qdt_workloads as W
+    import quantized_diffusion_transformer_amd as qdt
+    d = W.make_workload(src)
+    M, N, K = d["M"], d["N"], d["K"]
+    X = to_dev(d["X"])
+    Wq, Ws = qdt.mxfp4_quantize(to_dev(d["W"]))
+    b = None if d.get("bias") is None else to_dev(d["bias"])
+    Xq = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+    Xs = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(_, ev):
+        if ev is not None:
+            ev[0].record()
+        qdt.mxfp4_quantize(X, None, Xq, Xs)
+        if ev is not None:
+            ev[1].record()
+        qdt.mxfp4_linear(Xq, Xs, Wq, Ws, b, out=Y)
+        if ev is not None:
+            ev[2].record()
+    steps, warm = counts(step)
+    ms, tq, tg = time_loop(step, [None], steps, warm)
+    ops = 2.0 * M * N * K
+    g = stats(tg)["mean"]
+    qb = 2 * M * K + M * K // 2 + M * K // 32
+    return {"M": M, "N": N, "K": K, "format": "MXFP4 (32-element blocks, E8M0 scales)", "epilogue": "bias",
+            "steps": steps, "warmup": warm, "ms_per_step": round(ms, 4),
+            "eff_tops": round(ops / (ms * 1e-3) / 1e12, 1), "gemm_ms": round(g, 4),
+            "gemm_tops": round(ops / (g * 1e-3) / 1e12, 1),
+            "gemm_frac_fp4_peak": round(ops / (g * 1e-3) / 1e12 / PEAK_FP4_TOPS, 4),
+            "quantize_ms": round(stats(tq)["mean"], 4),
+            "quantize_gbs": round(qb / (stats(tq)["mean"] * 1e-3) / 1e9, 1)}
 
 
 def adaln_producer(M, K, counts):

@@ -68,7 +68,9 @@ typedef enum qdt_epilogue {
      * Y = bf16_rne((y * r) * gamma[n mod head_dim]).  [FAL] RMSNorm over 256-wide heads. */
     QDT_EPI_HEAD_RMSNORM = 2,
     /* Y is int32 [M, N]: the raw accumulators sum_k Xq[m][k] * Wq[n][k] (for testing). */
-    QDT_EPI_ACC_I32 = 3
+    QDT_EPI_ACC_I32 = 3,
+    /* Y is fp32 [M, N]: the raw accumulators of qdt_mxfp4_linear (for testing). */
+    QDT_EPI_ACC_F32 = 4
 } qdt_epilogue;
 
 /* Parameters of QDT_EPI_HEAD_RMSNORM.  gamma: device bf16 [head_dim], shared by all heads. */
@@ -172,6 +174,39 @@ qdt_status qdt_quantize_per_token(const uint16_t* X, const float* inv_lambda, in
 qdt_status qdt_adaln_quantize(const uint16_t* X, int64_t ldx, const uint16_t* shift, const uint16_t* scale, float eps,
                               const float* inv_lambda, int64_t M, int64_t K, int8_t* Xq, float* x_scale,
                               uint16_t* H, void* stream);
+
+/*
+ * Block-scaled FP4 (MXFP4) of the rows of X * colmul, the 4-bit format native to MI355X's matrix
+ * cores ([FAL]: the DiT runs in a block-scaled 4-bit floating-point format).  Per block of 32
+ * consecutive elements of a row, v = (float)X[m][j] * colmul[j] (v = (float)X[m][j] when colmul is
+ * NULL):
+ *   e = clamp(floor(log2(max |v|)) - 2, -127, 127)  (-127 for an all-zero block); S[m][b] = e + 127
+ *   code_j = nearest of {0, 0.5, 1, 1.5, 2, 3, 4, 6} to |v_j| / 2^e (ties to the even mantissa,
+ *            saturating at 6), sign in bit 3, zero stored as +0
+ *   Q[m][j / 2] holds code_j in its low nibble for even j, high nibble for odd j.
+ *   Used for the activations (colmul = inv_lambda or NULL, per step) and for the weights (colmul =
+ *   lambda or NULL, offline).  X: bf16 [M, ldx] (first K columns).  Q: uint8 [M, K/2].  S: uint8
+ *   [M, K/32].  K % 64 == 0, ldx >= K, ldx % 8 == 0; X, colmul and Q 16-byte aligned.  Bit-exact.
+ *   M = 0 is a no-op.
+ */
+qdt_status qdt_mxfp4_quantize(const uint16_t* X, const float* colmul, int64_t M, int64_t K, int64_t ldx,
+                              uint8_t* Q, uint8_t* S, void* stream);
+
+/*
+ * Block-scaled FP4 linear on the FP4 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4):
+ *   acc[m][n] = sum_k dec(Xq, Xs)[m][k] * dec(Wq, Ws)[n][k], dec = code value * 2^(exponent - 127),
+ *   accumulated in fp32 (order unspecified: within the fp32 summation bound of the exact sum);
+ *   QDT_EPI_BIAS: Y bf16 [M, ldy], Y[m][n] = bf16_rne(acc + (float)bias[n]) (bias NULL = 0);
+ *   QDT_EPI_ACC_F32: Y fp32 [M, ldy], the accumulators.
+ *   Xq / Xs: qdt_mxfp4_quantize of the activations ([M, K/2] codes, [M, K/32] exponents); Wq / Ws
+ *   the same of the weights ([N, K/2], [N, K/32]).  K % 256 == 0 (whole 128-byte stages of codes),
+ *   N % 16 == 0, ldy >= N, ldy % 8 == 0; code and Y pointers 16-byte aligned, exponent rows
+ *   4-byte aligned (K % 128 == 0 gives that).  Y must not overlap an input.  M = 0 is a no-op.
+ *   The scales of the block exponents are powers of two, so they take no rounding of their own.
+ */
+qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                            const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi, void* Y,
+                            int64_t ldy, void* stream);
 
 /* The plan qdt_w8a8_linear uses for this problem (pure host computation, no device call). */
 qdt_status qdt_w8a8_linear_plan(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, qdt_linear_plan* plan);

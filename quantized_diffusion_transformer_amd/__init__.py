@@ -26,7 +26,7 @@ _lib = C.CDLL(LIB_PATH)
 
 # ------------------------------------------------------------------------------- C types
 QDT_OK, QDT_EINVAL, QDT_ESHAPE, QDT_EALIGN, QDT_EWORKSPACE, QDT_EALIAS, QDT_EHIP, QDT_EUNSUPPORTED = range(8)
-QDT_EPI_BIAS, QDT_EPI_SILU_GATE, QDT_EPI_HEAD_RMSNORM, QDT_EPI_ACC_I32 = range(4)
+QDT_EPI_BIAS, QDT_EPI_SILU_GATE, QDT_EPI_HEAD_RMSNORM, QDT_EPI_ACC_I32, QDT_EPI_ACC_F32 = range(5)
 QDT_TILE_AUTO, QDT_TILE_256, QDT_TILE_288, QDT_TILE_288x256 = -1, 0, 1, 2
 QDT_MAX_K = 131072
 QDT_MAX_ADALN_K = 8192
@@ -56,6 +56,8 @@ _SIGS = {
     "qdt_smooth_prepare": ([_P, _P, _I64, _I64, _F, _P, _P, _P, _P, _P], _I),
     "qdt_quantize_per_token": ([_P, _P, _I64, _I64, _I64, _P, _P, _P], _I),
     "qdt_adaln_quantize": ([_P, _I64, _P, _P, _F, _P, _I64, _I64, _P, _P, _P, _P], _I),
+    "qdt_mxfp4_quantize": ([_P, _P, _I64, _I64, _I64, _P, _P, _P], _I),
+    "qdt_mxfp4_linear": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _P], _I),
     "qdt_w8a8_linear_plan": ([_I64, _I64, _I64, _I, C.POINTER(qdt_linear_plan)], _I),
     "qdt_w8a8_linear_plan_for": ([_I64, _I64, _I64, _I, C.c_int32, C.c_int32, C.POINTER(qdt_linear_plan)], _I),
     "qdt_w8a8_linear_workspace_size": ([_I64, _I64, _I64, _I, C.POINTER(_SZ)], _I),
@@ -191,6 +193,42 @@ def adaln_modulate(X: torch.Tensor, shift: torch.Tensor | None, scale: torch.Ten
     _check(qdt_adaln_quantize(_ptr(X), ldx, _ptr(shift), _ptr(scale), float(eps), None, M, K, None, None, _ptr(H),
                               _stream(stream)), "qdt_adaln_quantize")
     return H
+
+
+def mxfp4_quantize(X: torch.Tensor, colmul: torch.Tensor | None = None, Q=None, S=None, stream=None):
+    """Block-scaled FP4 of bf16 X [M, K] (times colmul): (codes uint8 [M, K/2], exponents uint8 [M, K/32])."""
+    _dev(X, torch.bfloat16, "X")
+    X, ldx = _rows(X, "X")
+    M, K = X.shape
+    if Q is None:
+        Q = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+    if S is None:
+        S = torch.empty((M, K // 32), dtype=torch.uint8, device=X.device)
+    _check(qdt_mxfp4_quantize(_ptr(X), _ptr(colmul), M, K, ldx, _ptr(Q), _ptr(S), _stream(stream)),
+           "qdt_mxfp4_quantize")
+    return Q, S
+
+
+def mxfp4_linear(Xq: torch.Tensor, Xs: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor,
+                 bias: torch.Tensor | None = None, epilogue: str = "bias", out=None, stream=None) -> torch.Tensor:
+    """Block-scaled FP4 linear: bf16 [M, N] = acc + bias ("bias"), or the fp32 accumulators ("acc_f32").
+    Xq uint8 [M, K/2] and Xs uint8 [M, K/32] from mxfp4_quantize of the activations; Wq, Ws the
+    same of the weights."""
+    for t, n in ((Xq, "Xq"), (Xs, "Xs"), (Wq, "Wq"), (Ws, "Ws")):
+        _dev(t, torch.uint8, n)
+    if bias is not None:
+        _dev(bias, torch.bfloat16, "bias")
+    M, N, K = Xq.shape[0], Wq.shape[0], Xq.shape[1] * 2
+    if Wq.shape[1] * 2 != K or Xs.shape != (M, K // 32) or Ws.shape != (N, K // 32):
+        raise ValueError("mxfp4_linear: inconsistent operand shapes")
+    epi = {"bias": QDT_EPI_BIAS, "acc_f32": QDT_EPI_ACC_F32}[epilogue]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32 if epi == QDT_EPI_ACC_F32 else torch.bfloat16,
+                          device=Xq.device)
+    out, ldy = _rows(out, "out")
+    _check(qdt_mxfp4_linear(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(bias), M, N, K, epi, _ptr(out), ldy,
+                            _stream(stream)), "qdt_mxfp4_linear")
+    return out
 
 
 def linear_plan(M: int, N: int, K: int, epilogue: str = "bias", tile: int | None = None,

@@ -187,6 +187,21 @@ qdt_status qdt_adaln_quantize(const uint16_t* X, int64_t ldx, const uint16_t* sh
                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
+qdt_status qdt_mxfp4_quantize(const uint16_t* X, const float* colmul, int64_t M, int64_t K, int64_t ldx, uint8_t* Q,
+                              uint8_t* S, void* stream) {
+    if (M < 0) return QDT_ESHAPE;
+    if (M > 0 && (!X || !Q || !S)) return QDT_EINVAL;
+    if (K <= 0 || K % 64 != 0 || K > QDT_MAX_K || ldx < K || M > INT32_MAX) return QDT_ESHAPE;
+    if (!aligned16(X) || !aligned16(colmul) || !aligned16(Q) || ldx % 8 != 0) return QDT_EALIGN;
+    if (M == 0) return QDT_OK;
+    const int64_t xb = ((M - 1) * ldx + K) * 2, qb = M * K / 2, sb = M * K / 32;
+    const int64_t cb = colmul ? K * 4 : 0;
+    if (overlap(Q, qb, X, xb) || overlap(Q, qb, colmul, cb) || overlap(S, sb, X, xb) || overlap(S, sb, colmul, cb) ||
+        overlap(S, sb, Q, qb))
+        return QDT_EALIAS;
+    return hip_status(launch_mx_quant(X, ldx, colmul, M, K, Q, S, reinterpret_cast<hipStream_t>(stream)));
+}
+
 static int epi_kind(qdt_epilogue e) {
     switch (e) {
         case QDT_EPI_BIAS: return EPI_BIAS;
@@ -352,6 +367,39 @@ qdt_status qdt_bf16_linear(const uint16_t* X, const uint16_t* W, const uint16_t*
     a.K = (int)K;
     a.epi = EPI_F32BIAS;
     return hip_status(launch_gemm_bf16(a, p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                            const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi, void* Y,
+                            int64_t ldy, void* stream) {
+    if (epi != QDT_EPI_BIAS && epi != QDT_EPI_ACC_F32) return QDT_EINVAL;
+    if (M < 0 || M > INT32_MAX / 2 || N <= 0 || N > INT32_MAX / 2 || N % 16 != 0) return QDT_ESHAPE;
+    if (K <= 0 || K % 256 != 0 || K > QDT_MAX_K || ldy < N) return QDT_ESHAPE;
+    if (M == 0) return QDT_OK;
+    if (!Xq || !Xs || !Wq || !Ws || !Y) return QDT_EINVAL;
+    if (!aligned16(Xq) || !aligned16(Wq) || !aligned16(bias) || !aligned16(Y) || ldy % 8 != 0 ||
+        (reinterpret_cast<uintptr_t>(Xs) & 3u) != 0 || (reinterpret_cast<uintptr_t>(Ws) & 3u) != 0)
+        return QDT_EALIGN;
+    const int64_t es = epi == QDT_EPI_ACC_F32 ? 4 : 2;
+    const int64_t ybytes = ((M - 1) * ldy + N) * es;
+    if (overlap(Y, ybytes, Xq, M * K / 2) || overlap(Y, ybytes, Xs, M * K / 32) || overlap(Y, ybytes, Wq, N * K / 2) ||
+        overlap(Y, ybytes, Ws, N * K / 32) || overlap(Y, ybytes, bias, bias ? N * 2 : 0))
+        return QDT_EALIAS;
+    Plan p;
+    qdt_status r = make_plan(M, N, K / 2, EPI_F32BIAS, 1, QDT_TILE_256, 1, &p);
+    if (r != QDT_OK) return r;
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.X = Xq;
+    a.W = Wq;
+    a.bias = bias;
+    a.Y = Y;
+    a.ldy = ldy;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.epi = epi == QDT_EPI_ACC_F32 ? EPI_ACC : EPI_F32BIAS;
+    return hip_status(launch_gemm_mx(a, Xs, Ws, p, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -25,6 +25,11 @@
 //     so that each store writes 16 contiguous bytes per lane.
 //   * Rows beyond M (or N) are clamped loads whose outputs are not stored; the integer sum is
 //     exact, so the result is independent of the tile shape and of the K split.
+//   * Block-scaled FP4 (MXFP4) uses the same tiles: a 128-byte stage holds 256 FP4 elements,
+//     exactly the bytes of two int8 K steps, and v_mfma_scale_f32_16x16x128_f8f6f4 reads its
+//     fragments in the int8 layout.  Its per-lane block exponents (lane l covers the 32 elements
+//     of one block) ride along in LDS: 8 bytes per row and stage, copied by dword LDS-DMAs with
+//     the operand rows and read as single bytes beside the fragments.
 #include <type_traits>
 
 #include "qdt_device.h"
@@ -46,6 +51,8 @@ struct KArgs {
     const float* sw;
     const uint16_t* bias;
     const uint16_t* gamma;
+    const uint8_t* xsc;  // block-scaled FP4: biased block exponents of X [M][K/32] and W [N][K/32]
+    const uint8_t* wsc;
     void* Y;
     int32_t* ws;
     int64_t ldy;
@@ -82,6 +89,19 @@ __device__ __forceinline__ void mfma(typename AccT<BF16>::type& c, const v4u& a,
     }
 }
 
+// Block-scaled FP4 MFMA, accumulator tied in place: A and B are 32 FP4 codes per lane (16 bytes,
+// the int8 fragment layout), sa / sb the biased block exponents of the lane's A and B blocks in
+// byte 0 (cbsz / blgp 4 select FP4 for both operands).
+template <bool ACC_AGPR>
+__device__ __forceinline__ void mfma_mx(v4f& c, const v4u& a, const v4u& b, uint32_t sa, uint32_t sb) {
+    if constexpr (ACC_AGPR)
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                     : "+a"(c) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    else
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                     : "+v"(c) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+
 // Wait for the MFMA pipeline to drain before accumulators are read by other instructions.
 __device__ __forceinline__ void mfma_drain() {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -105,6 +125,15 @@ __device__ __forceinline__ void lds_dma16_next(uint32_t voff, const void* sbase,
                  : "memory", "m0");
 }
 __device__ __forceinline__ void set_m0(uint32_t lds_addr) { asm volatile("s_mov_b32 m0, %0" ::"s"(lds_addr) : "m0"); }
+// The dword forms of the two above (lane l writes LDS m0 + 4 l): block exponents of FP4 rows.
+__device__ __forceinline__ void lds_dma4_next(uint32_t voff, const void* sbase, uint32_t next_lds) {
+    asm volatile("global_load_lds_dword %0, %1\n\ts_mov_b32 m0, %2" ::"v"(voff), "s"(sbase), "s"(next_lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4_s(uint32_t lds_addr, uint32_t voff, const void* sbase) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_addr), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
 __device__ __forceinline__ void lds_dma16_s(uint32_t lds_addr, uint32_t voff, const void* sbase) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(sbase)
                  : "memory", "m0");
@@ -123,8 +152,9 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// WM x WN waves, FM x FN fragments of 16x16 per wave.
-template <int WM, int WN, int FM, int FN, bool BF16, int EPI>
+// WM x WN waves, FM x FN fragments of 16x16 per wave.  BF16: bf16 operands; MX: block-scaled FP4
+// operands (both with fp32 accumulators); neither: int8 operands, int32 accumulators.
+template <int WM, int WN, int FM, int FN, bool BF16, int EPI, bool MX = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(WM * WN * 64, WM * WN * 64), amdgpu_waves_per_eu(1, 1))) void
 gemm_kernel(KArgs p) {
     constexpr int NW = WM * WN;            // waves
@@ -139,6 +169,12 @@ gemm_kernel(KArgs p) {
     constexpr int NBW = BN / 8, NBX = BM / 8;
     constexpr int NIW = NBW / 2, NIX = NBX / 2;
     constexpr int NI = NIW > NIX ? NIW : NIX;  // LDS-DMA slots per wave per stage
+    // FP4: 4 dword LDS-DMAs per wave and stage carry the block exponents of its 128 rows
+    // (8 bytes per row: the stage's 256 elements are 8 blocks)
+    constexpr int NSC = MX ? 4 : 0;
+    constexpr int NDMA = NI + NSC;
+    static_assert(!MX || (BM == 256 && BN == 256 && !BF16 && (EPI == EPI_F32BIAS || EPI == EPI_ACC)),
+                  "FP4: 256 x 256 tiles, fp32-accumulator epilogues");
     constexpr int NACC_A = 64;             // accumulator tuples held in AGPRs (the rest in VGPRs)
     constexpr bool SILU = EPI == EPI_SILU;
     static_assert(WM == 2 && WN == 2 && NBW % 2 == 0 && NBX % 2 == 0, "two waves per operand region");
@@ -147,10 +183,12 @@ gemm_kernel(KArgs p) {
     static_assert((FN + FM) * SP <= FN * FM, "sub-step 0 reads fit between its MFMAs");
     // sub-step 1 puts LDS-DMA q at slot floor(q FN FM / NI) and read q two slots later: distinct
     // slots inside the sub-step when the DMA slots are at least 3 apart and reads <= DMAs
-    static_assert(FN * FM >= 3 * NI && FN + FM <= NI, "sub-step 1 LDS-DMAs and reads fit between its MFMAs");
-    using Acc = typename AccT<BF16>::type;
+    static_assert(FN * FM >= 3 * NDMA && FN + FM <= NDMA, "sub-step 1 LDS-DMAs and reads fit between its MFMAs");
+    using Acc = typename AccT<BF16 || MX>::type;
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * STAGE];
+    constexpr int SCST = ROWS * 8;  // block-exponent bytes per stage (FP4)
+    __shared__ __attribute__((aligned(16))) uint8_t smem_sc[MX ? NB * SCST : 16];
     __shared__ float red[EPI == EPI_RMSNORM ? WN * BM : 1];
     // Epilogue parameters staged in LDS (dwords, each array padded to whole 64-lane DMA chunks):
     // w_scale per tile weight row, x_scale per tile token row, bias per weight row (bf16 pairs),
@@ -232,6 +270,23 @@ gemm_kernel(KArgs p) {
     auto dma = [&](int buf, int stage, int i) __attribute__((always_inline)) {
         lds_dma16_s(ldsw + (uint32_t)(buf * STAGE + i * 1024), voff(i), wbase + (int64_t)stage * BK);
     };
+    // FP4 block exponents: dword LDS-DMA i of a wave copies rows rlocal0 + 32 i .. + 31 of its
+    // region (lane l: row + l / 2, dword l % 2), to LDS [row][8 bytes] of the stage
+    uint32_t scvoffs[NSC > 0 ? NSC : 1];
+    const uint8_t* scbase = nullptr;
+    uint32_t ldss = 0;
+    if constexpr (MX) {
+        const int64_t scb = Kb / 16;  // exponent bytes per row: K / 32 = 2 Kb / 32
+        scbase = uniform_ptr((wwave ? p.wsc + (int64_t)n0 * scb : p.xsc + (int64_t)m0 * scb) + (int64_t)kta * 8);
+#pragma unroll
+        for (int i = 0; i < NSC; ++i)
+            scvoffs[i] = (uint32_t)(min(rlocal0 + i * 32 + (lane >> 1), rlast) * scb) + (lane & 1) * 4;
+        const int row0 = wwave ? wave * NIW * 8 : BN + (wave - 2) * NIX * 8;
+        ldss = __builtin_amdgcn_readfirstlane(lds_offset(smem_sc) + row0 * 8);
+    }
+    auto sdma = [&](int buf, int stage, int i) __attribute__((always_inline)) {
+        lds_dma4_s(ldss + (uint32_t)(buf * SCST + i * 256), scvoffs[i], scbase + (int64_t)stage * 8);
+    };
 
     // Global weight row of tile weight row r (clamped like the operand rows).
     auto wglobal = [&](int r) __attribute__((always_inline)) {
@@ -285,10 +340,18 @@ gemm_kernel(KArgs p) {
 
     // One MFMA of the group for weight fragment g, token fragment fm.
     auto mma = [&](int g, int fm, const v4u& a, const v4u& b) __attribute__((always_inline)) {
-        if (g * FM + fm < NACC_A)
-            mfma<BF16, true>(acc[g][fm], a, b);
-        else
-            mfma<BF16, false>(acc[g][fm], a, b);
+        if constexpr (!MX) {
+            if (g * FM + fm < NACC_A)
+                mfma<BF16, true>(acc[g][fm], a, b);
+            else
+                mfma<BF16, false>(acc[g][fm], a, b);
+        }
+    };
+    // FP4: the block exponent of this lane's row (lane & 15) of a fragment starting at tile row
+    // `row`, K step ks of the stage (lane group lane >> 4 covers block 4 ks + (lane >> 4))
+    const int sclane = (lane & 15) * 8 + (lane >> 4);
+    auto sc = [&](int buf, int row, int ks) __attribute__((always_inline)) {
+        return (uint32_t)smem_sc[buf * SCST + row * 8 + ks * 4 + sclane];
     };
     auto frag = [&](const uint8_t* s, int row, int lck) __attribute__((always_inline)) {
         return *reinterpret_cast<const v4u*>(s + row * BK + lck);
@@ -308,12 +371,28 @@ gemm_kernel(KArgs p) {
     // complete in issue order, so vmcnt <= NI means stage 0 has landed.
     const int nkc = max(nk, 1);
     v4u a0[FN], b0[FM], a1[FN], b1[FM];
+    // FP4 block exponents of the fragments (one byte per lane in byte 0), per K step
+    uint32_t sa0[MX ? FN : 1], sb0[MX ? FM : 1], sa1[MX ? FN : 1], sb1[MX ? FM : 1];
+    auto mmx = [&](int g, int fm, const v4u& a, const v4u& b, uint32_t sa, uint32_t sb) __attribute__((always_inline)) {
+        if constexpr (MX) {
+            if (g * FM + fm < NACC_A)
+                mfma_mx<true>(acc[g][fm], a, b, sa, sb);
+            else
+                mfma_mx<false>(acc[g][fm], a, b, sa, sb);
+        } else {
+            mma(g, fm, a, b);
+        }
+    };
 #pragma unroll
     for (int i = 0; i < NI; ++i)
         if (dma_used(i)) dma(0, 0, i);
 #pragma unroll
+    for (int i = 0; i < NSC; ++i) sdma(0, 0, i);
+#pragma unroll
     for (int i = 0; i < NI; ++i)
         if (dma_used(i)) dma(1, min(1, nkc - 1), i);
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) sdma(1, min(1, nkc - 1), i);
 #pragma unroll
     for (int c = 0; c < P_BF / 64; ++c) {
         const bool is_bias = c * 64 >= P_B && c * 64 < P_G;
@@ -326,11 +405,11 @@ gemm_kernel(KArgs p) {
         for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = Acc{0, 0, 0, 0};
     __builtin_amdgcn_sched_barrier(0);
     if (NIW == NIX)
-        wait_vmcnt<NI>();
+        wait_vmcnt<NDMA>();
     else if (wwave)
-        wait_vmcnt<NIW>();
+        wait_vmcnt<NIW + NSC>();
     else
-        wait_vmcnt<NIX>();
+        wait_vmcnt<NIX + NSC>();
     __syncthreads();
     {
         const uint8_t* s = smem + lrow;
@@ -338,6 +417,12 @@ gemm_kernel(KArgs p) {
         for (int fn = 0; fn < FN; ++fn) a0[fn] = frag(s, wrow[fn], lck0);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) b0[fm] = frag(s, xrow0 + fm * 16, lck0);
+        if constexpr (MX) {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) sa0[fn] = sc(0, wrow[fn], 0);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) sb0[fm] = sc(0, xrow0 + fm * 16, 0);
+        }
     }
     for (int j = 0; j < nk; ++j) {
         const uint8_t* s = smem + (j % NB) * STAGE + lrow;
@@ -348,12 +433,19 @@ gemm_kernel(KArgs p) {
         for (int g = 0; g < FN; ++g) {
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
-                mma(g, fm, a0[g], b0[fm]);
+                mmx(g, fm, a0[g], b0[fm], sa0[MX ? g : 0], sb0[MX ? fm : 0]);
                 const int k = g * FM + fm, q = k / SP;
                 if (k % SP == 0 && q < FM)
                     b1[q] = frag(s, xrow0 + q * 16, lck1);
                 else if (k % SP == 0 && q < FM + FN)
                     a1[q - FM] = frag(s, wrow[q - FM], lck1);
+                if constexpr (MX) {
+                    // block exponents of K step 1, between the fragment reads
+                    if (k % SP == SP / 2 && q < FM)
+                        sb1[q] = sc(j % NB, xrow0 + q * 16, 1);
+                    else if (k % SP == SP / 2 && q < FM + FN)
+                        sa1[q - FM] = sc(j % NB, wrow[q - FM], 1);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -364,26 +456,43 @@ gemm_kernel(KArgs p) {
         // (b0[q], then a0[q - FM])
         const uint32_t ldsd = ldsw + (uint32_t)((j % NB) * STAGE);
         const uint8_t* sbase = wbase + (int64_t)jd * BK;
+        const uint32_t ldssd = ldss + (uint32_t)((j % NB) * SCST);
+        const uint8_t* scbased = MX ? scbase + (int64_t)jd * 8 : nullptr;
+        (void)ldssd;
+        (void)scbased;
         set_m0(ldsd);
 #pragma unroll
         for (int g = 0; g < FN; ++g) {
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
-                mma(g, fm, a1[g], b1[fm]);
+                mmx(g, fm, a1[g], b1[fm], sa1[MX ? g : 0], sb1[MX ? fm : 0]);
                 const int k = g * FM + fm;
-                // LDS-DMA q at slot floor(q * S / NI), read q two slots later
+                // LDS-DMA q at slot floor(q * S / NDMA), read q two slots later (FP4: its block
+                // exponents one slot later); the FP4 exponent LDS-DMAs follow the operand ones
                 constexpr int S = FN * FM;
-                int qd = -1, qr = -1;
+                int qd = -1, qr = -1, qs = -1;
 #pragma unroll
-                for (int t = 0; t < NI; ++t) if ((t * S) / NI == k) qd = t;
+                for (int t = 0; t < NDMA; ++t) if ((t * S) / NDMA == k) qd = t;
 #pragma unroll
-                for (int t = 0; t < FM + FN; ++t) if ((t * S) / NI + 2 == k) qr = t;
-                if (qd >= 0) {
-                    if (dma_used(qd)) lds_dma16_next(voff(qd), sbase, ldsd + (uint32_t)((qd + 1) * 1024));
+                for (int t = 0; t < FM + FN; ++t) if ((t * S) / NDMA + 2 == k) qr = t;
+#pragma unroll
+                for (int t = 0; t < FM + FN; ++t) if ((t * S) / NDMA + 1 == k) qs = t;
+                if (qd >= 0 && qd < NI) {
+                    const uint32_t next = qd + 1 < NI || !MX ? ldsd + (uint32_t)((qd + 1) * 1024) : ldssd;
+                    if (dma_used(qd)) lds_dma16_next(voff(qd), sbase, next);
+                } else if (qd >= NI) {
+                    if constexpr (MX)
+                        lds_dma4_next(scvoffs[qd - NI], scbased, ldssd + (uint32_t)((qd - NI + 1) * 256));
                 } else if (qr >= 0 && qr < FM)
                     b0[qr] = frag(sn, xrow0 + qr * 16, lck0);
                 else if (qr >= FM)
                     a0[qr - FM] = frag(sn, wrow[qr - FM], lck0);
+                if constexpr (MX) {
+                    if (qs >= 0 && qs < FM)
+                        sb0[qs] = sc((j + 1) % NB, xrow0 + qs * 16, 0);
+                    else if (qs >= FM)
+                        sa0[qs - FM] = sc((j + 1) % NB, wrow[qs - FM], 0);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -732,12 +841,14 @@ static KArgs make_kargs(const GemmArgs& a, const Plan& pl, int esize) {
     k.kt_total = pl.kt_total;
     k.group_m = pl.group_m;
     k.head_dim = 256;
+    k.xsc = nullptr;
+    k.wsc = nullptr;
     return k;
 }
 
-template <int FM, int FN, bool BF16, int EPI>
+template <int FM, int FN, bool BF16, int EPI, bool MX = false>
 static hipError_t go(const KArgs& k, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_kernel<2, 2, FM, FN, BF16, EPI>), dim3(grid), dim3(256), 0, st, k);
+    hipLaunchKernelGGL((gemm_kernel<2, 2, FM, FN, BF16, EPI, MX>), dim3(grid), dim3(256), 0, st, k);
     return hipGetLastError();
 }
 
@@ -777,6 +888,17 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, const Plan& pl, hipStream_t st) {
     if (pl.tile == QDT_TILE_288) return go<9, 9, true, EPI_F32BIAS>(k, pl.grid, st);
     if (pl.tile == QDT_TILE_288x256) return go<9, 8, true, EPI_F32BIAS>(k, pl.grid, st);
     return go<8, 8, true, EPI_F32BIAS>(k, pl.grid, st);
+}
+
+hipError_t launch_gemm_mx(const GemmArgs& a, const uint8_t* xsc, const uint8_t* wsc, const Plan& pl, hipStream_t st) {
+    KArgs k = make_kargs(a, pl, 1);
+    k.Kb = a.K / 2;  // two FP4 codes per byte
+    k.xsc = xsc;
+    k.wsc = wsc;
+    if (pl.tile != QDT_TILE_256 || pl.split_k != 1) return hipErrorInvalidValue;
+    if (a.epi == EPI_F32BIAS) return go<8, 8, false, EPI_F32BIAS, true>(k, pl.grid, st);
+    if (a.epi == EPI_ACC) return go<8, 8, false, EPI_ACC, true>(k, pl.grid, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_splitk_epilogue(const GemmArgs& a, int split_k, int epi, hipStream_t st) {

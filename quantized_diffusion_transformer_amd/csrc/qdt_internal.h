@@ -22,6 +22,9 @@ hipError_t launch_quant_rows(const uint16_t* X, int64_t ldx, const float* colmul
 hipError_t launch_adaln_quant(const uint16_t* X, int64_t ldx, const uint16_t* shift, const uint16_t* scale, float eps,
                               const float* colmul, int64_t M, int64_t K, int8_t* Q, float* xscale, uint16_t* H,
                               hipStream_t st);
+// Block-scaled FP4 (MXFP4) of X's rows times colmul: codes Q [M, K/2], biased exponents S [M, K/32].
+hipError_t launch_mx_quant(const uint16_t* X, int64_t ldx, const float* colmul, int64_t M, int64_t K, uint8_t* Q,
+                           uint8_t* S, hipStream_t st);
 
 // ------------------------------------------------------------------ GEMM
 enum EpiKind { EPI_BIAS = 0, EPI_SILU = 1, EPI_RMSNORM = 2, EPI_ACC = 3, EPI_PARTIAL = 4, EPI_F32BIAS = 5 };
@@ -54,6 +57,9 @@ struct GemmArgs {
 
 hipError_t launch_gemm_i8(const GemmArgs& a, const Plan& p, hipStream_t st);
 hipError_t launch_gemm_bf16(const GemmArgs& a, const Plan& p, hipStream_t st);
+// Block-scaled FP4 GEMM (256 x 256 tiles, no K split): a.K is the element count; xsc / wsc the
+// biased block exponents [M][K/32] / [N][K/32]; a.epi EPI_F32BIAS or EPI_ACC (fp32 accumulators).
+hipError_t launch_gemm_mx(const GemmArgs& a, const uint8_t* xsc, const uint8_t* wsc, const Plan& p, hipStream_t st);
 // Sum of the S int32 partial slices followed by epilogue `epi` (BIAS, SILU, RMSNORM, ACC).
 hipError_t launch_splitk_epilogue(const GemmArgs& a, int split_k, int epi, hipStream_t st);
 

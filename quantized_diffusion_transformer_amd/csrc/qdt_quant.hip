@@ -495,4 +495,76 @@ hipError_t launch_adaln_quant(const uint16_t* X, int64_t ldx, const uint16_t* sh
     return launch_adaln<false>(X, ldx, shift, scale, eps, colmul, M, K, Q, xscale, H, st);
 }
 
+// ---------------------------------------------------------------------------- block-scaled FP4
+// MXFP4, the block-scaled 4-bit floating point native to the MI355X matrix cores ("Serving
+// sub-second Ideogram v4 without quality loss": the DiT runs in a block-scaled 4-bit float on the
+// authors' GPUs).  Per block of 32 consecutive elements of a row (v = x * colmul):
+//   e = clamp(floor(log2(max |v|)) - 2, -127, 127)   (-127 for an all-zero block), byte e + 127
+//   code = fp4(v / 2^e): nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to mantissa 0, saturating at
+//          6; sign << 3 | index, zero stored as +0; two codes per byte, even element low.
+// One lane converts 8 consecutive elements (16 bytes of bf16), so a block is a quad of lanes;
+// the quad max takes two lane exchanges.  v / 2^e is exact (v_ldexp_f32) and lies in (-8, 8);
+// v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds it to the nearest code with ties to even and
+// saturates, as the definition reads, except that it keeps the sign of values that round to
+// zero, which is cleared afterwards.  Bytes per element: 2 read, 0.5 + 1/32 written.
+__global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                       const float* __restrict__ colmul, int64_t M, int64_t K,
+                                                       uint8_t* __restrict__ Q, uint8_t* __restrict__ S) {
+    const int64_t cpr = K >> 3;  // 8-element chunks per row
+    const int64_t total = M * cpr;
+    const int lane = threadIdx.x & 63;
+    for (int64_t base = ((int64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~63)); base < total;
+         base += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t c = base + lane;  // quads of lanes are blocks: cpr % 4 == 0 and base % 64 == 0
+        const bool ok = c < total;
+        const int64_t row = ok ? c / cpr : 0, cc = ok ? c % cpr : 0;
+        float v[8];
+        const uint4 raw = ok ? *reinterpret_cast<const uint4*>(X + row * ldx + cc * 8) : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
+            v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+        }
+        if (colmul && ok) {
+            const float4 m0 = *reinterpret_cast<const float4*>(colmul + cc * 8);
+            const float4 m1 = *reinterpret_cast<const float4*>(colmul + cc * 8 + 4);
+            const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] *= mm[e];
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+        // amax = f * 2^ex with f in [0.5, 1): floor(log2 amax) = ex - 1
+        int ex = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 3 : -127;
+        ex = min(max(ex, -127), 127);
+        float t[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = __builtin_ldexpf(v[e], -ex);
+        uint32_t packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, t[0], t[1], 1.0f, 0);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, t[2], t[3], 1.0f, 1);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, t[4], t[5], 1.0f, 2);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, t[6], t[7], 1.0f, 3);
+        // clear the sign of zero magnitudes: a nibble keeps bit 3 only if its low 3 bits are nonzero
+        const uint32_t mag = packed & 0x77777777u;
+        packed &= 0x77777777u | ((mag + 0x77777777u) & 0x88888888u);
+        if (ok) {
+            *reinterpret_cast<uint32_t*>(Q + row * (K >> 1) + cc * 4) = packed;
+            if ((lane & 3) == 0) S[row * (K >> 5) + (cc >> 2)] = (uint8_t)(ex + 127);
+        }
+    }
+}
+
+hipError_t launch_mx_quant(const uint16_t* X, int64_t ldx, const float* colmul, int64_t M, int64_t K, uint8_t* Q,
+                           uint8_t* S, hipStream_t st) {
+    if (M <= 0) return hipSuccess;
+    const int64_t chunks = M * (K >> 3);
+    const int64_t blocks = min((chunks + 255) / 256, (int64_t)kNumCU * 16);
+    hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, st, X, ldx, colmul, M, K, Q, S);
+    return hipGetLastError();
+}
+
 }  // namespace qdt

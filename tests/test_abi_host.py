@@ -79,6 +79,28 @@ def test_adaln_quantize_validation():
     assert call(M=0) == qdt.QDT_OK
 
 
+def test_mxfp4_validation():
+    q = qdt.qdt_mxfp4_quantize
+    assert q(A(), None, 4, 96, 96, A(0x200000), A(0x300000), None) == qdt.QDT_ESHAPE      # K % 64
+    assert q(A(), None, 4, 128, 64, A(0x200000), A(0x300000), None) == qdt.QDT_ESHAPE     # ldx < K
+    assert q(A(), None, 4, 128, 128, A(0x200008), A(0x300000), None) == qdt.QDT_EALIGN
+    assert q(A(), None, 4, 128, 128, A(0x10010), A(0x300000), None) == qdt.QDT_EALIAS     # Q inside X
+    assert q(A(), None, 4, 128, 128, None, A(0x300000), None) == qdt.QDT_EINVAL
+    assert q(A(), None, 0, 128, 128, A(0x200000), A(0x300000), None) == qdt.QDT_OK
+    f = qdt.qdt_mxfp4_linear
+
+    def lin(M=64, N=128, K=256, epi=0, Y=0x900000, ldy=None, xs=0x200000, ws=0x400000):
+        return f(A(0x100000), A(xs), A(0x300000), A(ws), None, M, N, K, epi, A(Y), N if ldy is None else ldy, None)
+    assert lin(K=128) == qdt.QDT_ESHAPE                 # whole 256-element stages
+    assert lin(N=120) == qdt.QDT_ESHAPE
+    assert lin(epi=1) == qdt.QDT_EINVAL                 # bias or fp32 accumulators only
+    assert lin(epi=3) == qdt.QDT_EINVAL
+    assert lin(ldy=64) == qdt.QDT_ESHAPE
+    assert lin(xs=0x200002) == qdt.QDT_EALIGN           # exponent rows read as dwords
+    assert lin(Y=0x300000 + 64) == qdt.QDT_EALIAS        # Y over Wq
+    assert lin(M=0) == qdt.QDT_OK
+
+
 def test_smooth_prepare_validation():
     f = qdt.qdt_smooth_prepare
     outs = (A(0x100000), A(0x200000), A(0x300000), A(0x400000))

@@ -1,0 +1,127 @@
+"""Parity of the block-scaled FP4 (MXFP4) path against the oracle.
+
+The quantizer's codes and block exponents are gated bit for bit.  The GEMM is gated bit for bit
+on inputs whose partial sums are exact in fp32 (any summation order gives the exact sum), which
+pins the fragment layout, the nibble order and the placement of every block exponent.  On
+general inputs its bf16 output is gated by 1 bf16 ulp plus the fp32 summation bound
+gamma_K * sum_k |x_k w_k| of the decoded values.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import qdt_workloads as W
+from qdt_testutil import bits_equal, sample_rows, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+qdt = pytest.importorskip("quantized_diffusion_transformer_amd")
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def check_quant(X, colmul=None, ldx=None):
+    M, K = X.shape
+    Xh = X
+    if ldx is not None:
+        Xh = np.full((M, ldx), 0x7FC0, np.uint16)  # NaN padding: must never be read
+        Xh[:, :K] = X
+    Xd = to_dev(Xh)[:, :K] if ldx is not None else to_dev(Xh)
+    Q, S = qdt.mxfp4_quantize(Xd, None if colmul is None else to_dev(colmul))
+    torch.cuda.synchronize()
+    Qr, Sr = oracle.mxfp4_quantize(X, colmul)
+    Qg, Sg = to_host(Q), to_host(S)
+    assert bits_equal(Sg, Sr), f"exponents: {np.sum(Sg != Sr)} differ"
+    assert bits_equal(Qg, Qr), f"codes: {np.sum(Qg != Qr)} bytes differ"
+    return Q, S
+
+
+@pytest.mark.parametrize("M,K", [(1, 64), (37, 256), (300, 4608), (5, 53248)])
+def test_mxfp4_quantize_parity(M, K):
+    announce(f"mxfp4_quantize M={M} K={K}")
+    X = W.activations(M, K, 4000 + K, "pct1")
+    check_quant(X)
+    inv = (np.random.default_rng(K).uniform(0.05, 3.0, K)).astype(np.float32)
+    check_quant(X, inv)
+
+
+def test_mxfp4_quantize_special_blocks_and_stride():
+    announce("mxfp4_quantize special blocks, ldx > K")
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((8, 512)).astype(np.float32)
+    x[0, :32] = 0.0                                   # zero block
+    x[1, 32:64] = 1e-39 * rng.standard_normal(32)     # subnormal block maximum
+    x[2, 64:96] = 3e38 * np.sign(rng.standard_normal(32))  # exponent near the top
+    x[3, :32] = [4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5, 7.75, -0.25, -0.1, -5.0] + [0.0] * 19
+    x[4] = -1e-3 * np.abs(rng.standard_normal(512))   # negative values, some rounding to zero
+    x[4, ::32] = -1.0
+    check_quant(W.f32_to_bf16_bits(x), ldx=512 + 40)
+
+
+def exact_operands(rows, K, seed):
+    """Random codes with block exponents in {-2, -1, 0}: every product is a multiple of 2^-6
+    below 36, so sums over K <= 1024 stay exact in fp32."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 16, (rows, K))
+    codes[codes == 8] = 0  # canonical zero
+    Q = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    S = rng.integers(125, 128, (rows, K // 32)).astype(np.uint8)
+    return Q, S
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 16, 256), (300, 272, 512), (513, 256, 1024)])
+def test_mxfp4_gemm_exact_accumulators(M, N, K):
+    announce(f"mxfp4_linear exact M={M} N={N} K={K}")
+    Xq, Xs = exact_operands(M, K, 50 + M)
+    Wq, Ws = exact_operands(N, K, 60 + N)
+    _, acc = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, want_acc=True)
+    Y = to_host(qdt.mxfp4_linear(to_dev(Xq), to_dev(Xs), to_dev(Wq), to_dev(Ws), None, "acc_f32"))
+    assert np.array_equal(Y.astype(np.float64), acc), f"{np.sum(Y != acc)} accumulators differ"
+
+
+def within_bound(Y, Xq, Xs, Wq, Ws, bias, rows):
+    Y_ref, acc = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, rows, want_acc=True)
+    xd = oracle.mxfp4_dequantize(Xq[rows], Xs[rows])
+    wd = oracle.mxfp4_dequantize(Wq, Ws)
+    K = xd.shape[1]
+    gam = K * 2.0 ** -24 / (1 - K * 2.0 ** -24)
+    b = 0.0 if bias is None else W.bf16_bits_to_f32(bias).astype(np.float64)
+    ref = acc + b
+    bound = gam * (np.abs(xd) @ np.abs(wd).T) + 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    got = W.bf16_bits_to_f32(Y[rows]).astype(np.float64)
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), f"worst error / bound {np.max(err / bound):.3f}"
+    return float(np.mean(Y[rows] == Y_ref))
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 128, 256), (300, 4608, 4608)])
+def test_mxfp4_linear_bias_within_bound(M, N, K):
+    announce(f"mxfp4_linear bias M={M} N={N} K={K}")
+    d = W.make_linear(M, N, K, seed=4100 + M, x_kind="pct1", w_sigma=0.015, bias=True)
+    Xq, Xs = check_quant(d["X"])
+    Wq, Ws = check_quant(d["W"])
+    Y = to_host(qdt.mxfp4_linear(Xq, Xs, Wq, Ws, to_dev(d["bias"]), "bias"))
+    rows = np.arange(M) if M <= 64 else sample_rows(M, 24, 5)
+    exact = within_bound(Y, to_host(Xq), to_host(Xs), to_host(Wq), to_host(Ws), d["bias"], rows)
+    assert exact > 0.9, f"only {exact:.3f} of the outputs equal the correctly rounded result"
+
+
+def test_mxfp4_attention_projection_4608():
+    """The headline shape in block-scaled FP4, sampled rows, in the benchmark's launch."""
+    announce("mxfp4 4608x4608x4608")
+    d = W.make_workload("dit_attn_proj_4608x4608x4608")
+    Xq, Xs = qdt.mxfp4_quantize(to_dev(d["X"]))
+    Wq, Ws = qdt.mxfp4_quantize(to_dev(d["W"]))
+    Y = to_host(qdt.mxfp4_linear(Xq, Xs, Wq, Ws, to_dev(d["bias"]), "bias"))
+    rows = sample_rows(4608, 16, 6)
+    Qr, Sr = oracle.mxfp4_quantize(d["X"][rows])
+    assert bits_equal(to_host(Xq)[rows], Qr) and bits_equal(to_host(Xs)[rows], Sr)
+    Wqr, Wsr = oracle.mxfp4_quantize(d["W"])
+    assert bits_equal(to_host(Wq), Wqr) and bits_equal(to_host(Ws), Wsr)
+    Xqh, Xsh = to_host(Xq), to_host(Xs)
+    within_bound(Y, Xqh, Xsh, Wqr, Wsr, d["bias"], rows)

@@ -90,6 +90,18 @@ def time_loop(fn_step, sets, steps, warmup):
     return (t1 - t0) * 1e3 / steps, ph1, ph2
 
 
+def time_loop_best(fn_step, steps, warmup, reps=2):
+    """time_loop on one buffer set, repeated: the repetition with the lowest wall time (context
+    numbers of the other workloads; a one-off stall of the device then costs a repetition, not
+    the number)."""
+    best = None
+    for r in range(reps):
+        res = time_loop(fn_step, [None], steps, warmup if r == 0 else max(1, warmup // 4))
+        if best is None or res[0] < best[0]:
+            best = res
+    return best
+
+
 def stats(xs):
     import numpy as np
     a = np.asarray(xs, dtype=np.float64)
@@ -340,7 +352,7 @@ def extra_workloads(args, only=None):
             if ev is not None:
                 ev[2].record()
         steps, warm = counts(step)
-        ms, tq, tg = time_loop(step, [None], steps, warm)
+        ms, tq, tg = time_loop_best(step, steps, warm)
         ops = 2.0 * M * N * K
         g = stats(tg)["mean"]
         r = {"M": M, "N": N, "K": K, "epilogue": epi, "plan": plan, "steps": steps, "warmup": warm,
@@ -370,7 +382,7 @@ def extra_workloads(args, only=None):
             if ev is not None:
                 ev[2].record()
         steps, warm = counts(step)
-        _, _, tg = time_loop(step, [None], steps, warm)
+        _, _, tg = time_loop_best(step, steps, warm)
         g = stats(tg)["mean"]
         fl = 2.0 * H.shape[0] * Wd.shape[0] * H.shape[1]
         return {"bf16_down_proj": {"M": H.shape[0], "N": Wd.shape[0], "K": H.shape[1], "ms": round(g, 4),
@@ -431,7 +443,7 @@ def mxfp4_workload(src, counts):
         if ev is not None:
             ev[2].record()
     steps, warm = counts(step)
-    ms, tq, tg = time_loop(step, [None], steps, warm)
+    ms, tq, tg = time_loop_best(step, steps, warm)
     ops = 2.0 * M * N * K
     g = stats(tg)["mean"]
     qb = 2 * M * K + M * K // 2 + M * K // 32
@@ -481,8 +493,8 @@ def adaln_producer(M, K, counts):
         if ev is not None:
             ev[2].record()
     steps, warm = counts(fused)
-    tf, _, _ = time_loop(fused, [None], steps, warm)
-    tu, t_ln, t_q = time_loop(unfused, [None], steps, warm)
+    tf, _, _ = time_loop_best(fused, steps, warm)
+    tu, t_ln, t_q = time_loop_best(unfused, steps, warm)
     b = 3 * M * K + 4 * M + 4 * K + 4 * K
     return {"M": M, "K": K, "steps": steps, "warmup": warm, "fused_ms": round(tf, 4),
             "fused_gbs": round(b / (tf * 1e-3) / 1e9, 1), "fused_frac_hbm": round(b / (tf * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

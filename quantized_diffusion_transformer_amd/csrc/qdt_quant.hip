@@ -10,6 +10,8 @@
 // The quantizer is HBM-bound: one read of the bf16 row, one write of the int8 row.  A row is
 // owned by one wavefront (K <= 8192) or one workgroup (larger K) and held in registers
 // between the max-abs reduction and the quantization, so X is read once.
+#include <atomic>
+
 #include "qdt_device.h"
 #include "qdt_internal.h"
 
@@ -263,15 +265,17 @@ static hipError_t launch_quant_cfg(const uint16_t* X, int64_t ldx, const float* 
     static_assert(WPR > 1 || C * 64 * 8 <= kQuantMaxLdsK, "column multipliers fit in LDS");
     const int threads = WPR == 1 ? 256 : WPR * 64;
     const size_t lds = (WPR == 1 && colmul) ? (size_t)K * sizeof(float) : 0;
-    // cached per configuration, for the largest LDS request of the configuration (K = 512 C)
-    static int per_cu_cache[2] = {0, 0};
-    int& per_cu = per_cu_cache[lds ? 1 : 0];
+    // cached per configuration (one architecture per process), for the largest LDS request of the
+    // configuration (K = 512 C); concurrent first calls compute the same value
+    static std::atomic<int> per_cu_cache[2] = {0, 0};
+    int per_cu = per_cu_cache[lds ? 1 : 0].load(std::memory_order_relaxed);
     if (per_cu == 0) {
         int v = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, quant_rows_kernel<WPR, C>, threads,
                                                                     lds ? (size_t)C * 512 * sizeof(float) : 0);
         if (e != hipSuccess) return e;
         per_cu = max(v, 1);
+        per_cu_cache[lds ? 1 : 0].store(per_cu, std::memory_order_relaxed);
     }
     const int64_t units = WPR == 1 ? (M + 3) / 4 : M;  // blocks for one row per wave
     const int64_t blocks = min(units, (int64_t)per_cu * kNumCU);
@@ -458,13 +462,16 @@ static hipError_t launch_adaln_cfg(const uint16_t* X, int64_t ldx, const uint16_
                                    uint16_t* H, hipStream_t st) {
     const int threads = kAdalnWaves * 64;
     const size_t lds = (size_t)K * 12;
-    static int per_cu = 0;  // for the largest LDS request of the configuration (K = 512 C)
+    // cached like launch_quant_cfg's, for the largest LDS request of the configuration (K = 512 C)
+    static std::atomic<int> per_cu_cache{0};
+    int per_cu = per_cu_cache.load(std::memory_order_relaxed);
     if (per_cu == 0) {
         int v = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, adaln_quant_kernel<C, QUANT>, threads,
                                                                     (size_t)C * 512 * 12);
         if (e != hipSuccess) return e;
         per_cu = max(v, 1);
+        per_cu_cache.store(per_cu, std::memory_order_relaxed);
     }
     const int64_t units = (M + kAdalnWaves - 1) / kAdalnWaves;
     const int64_t blocks = min(units, (int64_t)per_cu * kNumCU);

@@ -298,7 +298,7 @@ def cpu_baseline(d):
 EXTRA_WORKLOADS = ("dit_ffn_gate_up_4608x24576x4608", "text_cond_proj_512x4608x53248",
                    "text_cond_proj_padded_4608x4608x53248", "qk_proj_headnorm_16896x4608x4608",
                    "qk_proj_headnorm_6037x4608x4608", "adaln_quantize_4608x4608", "adaln_quantize_16896x4608",
-                   "mxfp4_attn_proj_4608x4608x4608", "mxfp4_ffn_up_4608x24576x4608")
+                   "mxfp4_attn_proj_4608x4608x4608", "mxfp4_ffn_gate_up_4608x24576x4608")
 
 
 def extra_workloads(args, only=None):
@@ -409,17 +409,17 @@ def extra_workloads(args, only=None):
         name = f"adaln_quantize_{M}x4608"
         if want(name):
             res[name] = adaln_producer(M, 4608, counts)
-    for name, src in (("mxfp4_attn_proj_4608x4608x4608", "dit_attn_proj_4608x4608x4608"),
-                      ("mxfp4_ffn_up_4608x24576x4608", "dit_ffn_gate_up_4608x24576x4608")):
+    for name, src, epi in (("mxfp4_attn_proj_4608x4608x4608", "dit_attn_proj_4608x4608x4608", "bias"),
+                           ("mxfp4_ffn_gate_up_4608x24576x4608", "dit_ffn_gate_up_4608x24576x4608", "silu_gate")):
         if want(name):
-            res[name] = mxfp4_workload(src, counts)
+            res[name] = mxfp4_workload(src, epi, counts)
     torch.cuda.empty_cache()
     return res
 
 
-def mxfp4_workload(src, counts):
+def mxfp4_workload(src, epi, counts):
     """Block-scaled FP4 on a workload's shapes and inputs: per step the activations are quantized
-    (qdt_mxfp4_quantize) and multiplied (qdt_mxfp4_linear, bias epilogue); weights offline."""
+    (qdt_mxfp4_quantize) and multiplied (qdt_mxfp4_linear with epilogue `epi`); weights offline."""
     import torch
 
     import qdt_workloads as W
@@ -431,7 +431,7 @@ def mxfp4_workload(src, counts):
     b = None if d.get("bias") is None else to_dev(d["bias"])
     Xq = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
     Xs = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
-    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    Y = torch.empty((M, N // 2 if epi == "silu_gate" else N), dtype=torch.bfloat16, device="cuda")
 
     def step(_, ev):
         if ev is not None:
@@ -439,7 +439,7 @@ def mxfp4_workload(src, counts):
         qdt.mxfp4_quantize(X, None, Xq, Xs)
         if ev is not None:
             ev[1].record()
-        qdt.mxfp4_linear(Xq, Xs, Wq, Ws, b, out=Y)
+        qdt.mxfp4_linear(Xq, Xs, Wq, Ws, b, epi, out=Y)
         if ev is not None:
             ev[2].record()
     steps, warm = counts(step)
@@ -447,7 +447,7 @@ def mxfp4_workload(src, counts):
     ops = 2.0 * M * N * K
     g = stats(tg)["mean"]
     qb = 2 * M * K + M * K // 2 + M * K // 32
-    return {"M": M, "N": N, "K": K, "format": "MXFP4 (32-element blocks, E8M0 scales)", "epilogue": "bias",
+    return {"M": M, "N": N, "K": K, "format": "MXFP4 (32-element blocks, E8M0 scales)", "epilogue": epi,
             "steps": steps, "warmup": warm, "ms_per_step": round(ms, 4),
             "eff_tops": round(ops / (ms * 1e-3) / 1e12, 1), "gemm_ms": round(g, 4),
             "gemm_tops": round(ops / (g * 1e-3) / 1e12, 1),

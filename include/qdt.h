@@ -197,6 +197,9 @@ qdt_status qdt_mxfp4_quantize(const uint16_t* X, const float* colmul, int64_t M,
  *   acc[m][n] = sum_k dec(Xq, Xs)[m][k] * dec(Wq, Ws)[n][k], dec = code value * 2^(exponent - 127),
  *   accumulated in fp32 (order unspecified: within the fp32 summation bound of the exact sum);
  *   QDT_EPI_BIAS: Y bf16 [M, ldy], Y[m][n] = bf16_rne(acc + (float)bias[n]) (bias NULL = 0);
+ *   QDT_EPI_SILU_GATE: W rows [gate(0..F-1); up(F..2F-1)], N = 2F (N % 32 == 0), Y bf16 [M, ldy >= F]:
+ *     g = acc[m][f] + bias[f], u = acc[m][F+f] + bias[F+f], Y[m][f] = bf16_rne((g / (1 + exp(-g))) * u)
+ *     ([FAL] gated-SiLU epilogue; the exponential and reciprocal as in the W8A8 SILU epilogue);
  *   QDT_EPI_ACC_F32: Y fp32 [M, ldy], the accumulators.
  *   Xq / Xs: qdt_mxfp4_quantize of the activations ([M, K/2] codes, [M, K/32] exponents); Wq / Ws
  *   the same of the weights ([N, K/2], [N, K/32]).  K % 256 == 0 (whole 128-byte stages of codes),

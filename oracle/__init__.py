@@ -56,7 +56,7 @@ def lib():
             "oracle_adaln_modulate": ([P, I64, I64, I64, P, P, F, P], None),
             "oracle_fp4_value": ([I], C.c_double),
             "oracle_mxfp4_quantize_rows": ([P, P, I64, I64, I64, P, P], None),
-            "oracle_mxfp4_gemm_rows": ([P, P, P, P, P, P, I64, I64, I64, P, P], None),
+            "oracle_mxfp4_gemm_rows": ([P, P, P, P, P, P, I64, I64, I64, I, P, P], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -241,14 +241,16 @@ def mxfp4_dequantize(Q, S) -> np.ndarray:
     return table[codes] * np.ldexp(1.0, np.repeat(S.astype(np.int64) - 127, 32, axis=1))
 
 
-def mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias=None, rows=None, want_acc=False):
-    """fp64 accumulators of the decoded product and Y = bf16((float)acc + bias) for the given rows."""
+def mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias=None, rows=None, want_acc=False, epi="bias"):
+    """fp64 accumulators of the decoded product and the bf16 output of epilogue ``epi`` ("bias":
+    bf16((float)acc + bias); "silu_gate": W rows [gate; up], bf16(silu(g) * u)) for the given rows."""
+    e = _EPI[epi]
     Xq, Xs, Wq, Ws = (_c(a, np.uint8) for a in (Xq, Xs, Wq, Ws))
     N, K = Wq.shape[0], Wq.shape[1] * 2
     r = None if rows is None else _c(rows, np.int64)
     nr = Xq.shape[0] if r is None else r.size
-    Y = np.empty((nr, N), np.uint16)
+    Y = np.empty((nr, _n_out(N, e)), np.uint16)
     acc = np.empty((nr, N), np.float64) if want_acc else None
-    lib().oracle_mxfp4_gemm_rows(_p(Xq), _p(Xs), _p(Wq), _p(Ws), _p(_c(bias, np.uint16)), _p(r), nr, N, K, _p(acc),
-                                 _p(Y))
+    lib().oracle_mxfp4_gemm_rows(_p(Xq), _p(Xs), _p(Wq), _p(Ws), _p(_c(bias, np.uint16)), _p(r), nr, N, K, e,
+                                 _p(acc), _p(Y))
     return (Y, acc) if want_acc else Y

@@ -488,11 +488,12 @@ static double mx_elem(const uint8_t* q, const uint8_t* s, int64_t j) {
 
 typedef struct {
     const uint8_t* Xq; const uint8_t* Xs; const uint8_t* Wq; const uint8_t* Ws; const uint16_t* bias;
-    const int64_t* rows; int64_t N, K; double* acc; uint16_t* Y;
+    const int64_t* rows; int64_t N, K; int epi; double* acc; uint16_t* Y;
 } mxg_ctx;
 
 static void mxg_rows(void* p, int64_t i0, int64_t i1) {
     mxg_ctx* c = (mxg_ctx*)p;
+    double* a = (double*)malloc(sizeof(double) * (size_t)c->N);
     for (int64_t i = i0; i < i1; ++i) {
         int64_t m = c->rows ? c->rows[i] : i;
         const uint8_t* xq = c->Xq + m * (c->K / 2);
@@ -500,22 +501,36 @@ static void mxg_rows(void* p, int64_t i0, int64_t i1) {
         for (int64_t n = 0; n < c->N; ++n) {
             const uint8_t* wq = c->Wq + n * (c->K / 2);
             const uint8_t* ws = c->Ws + n * (c->K / 32);
-            double a = 0.0; /* products are exact; the fp64 sum rounds far below fp32 */
-            for (int64_t k = 0; k < c->K; ++k) a += mx_elem(xq, xs, k) * mx_elem(wq, ws, k);
-            if (c->acc) c->acc[i * c->N + n] = a;
-            if (c->Y) {
+            double s = 0.0; /* products are exact; the fp64 sum rounds far below fp32 */
+            for (int64_t k = 0; k < c->K; ++k) s += mx_elem(xq, xs, k) * mx_elem(wq, ws, k);
+            a[n] = s;
+            if (c->acc) c->acc[i * c->N + n] = s;
+        }
+        if (!c->Y) continue;
+        if (c->epi == ORACLE_EPI_SILU_GATE) {
+            int64_t F = c->N / 2;
+            for (int64_t f = 0; f < F; ++f) {
+                float g = (float)a[f] + (c->bias ? oracle_bf16_to_f32(c->bias[f]) : 0.0f);
+                float u = (float)a[F + f] + (c->bias ? oracle_bf16_to_f32(c->bias[F + f]) : 0.0f);
+                c->Y[i * F + f] = oracle_f32_to_bf16((g / (1.0f + expf(-g))) * u);
+            }
+        } else {
+            for (int64_t n = 0; n < c->N; ++n) {
                 float b = c->bias ? oracle_bf16_to_f32(c->bias[n]) : 0.0f;
-                c->Y[i * c->N + n] = oracle_f32_to_bf16((float)a + b);
+                c->Y[i * c->N + n] = oracle_f32_to_bf16((float)a[n] + b);
             }
         }
     }
+    free(a);
 }
 
-/* acc[i][n] = sum_k dec(X row rows[i], k) * dec(W row n, k) (fp64) and Y = bf16((float)acc + bias).
+/* acc[i][n] = sum_k dec(X row rows[i], k) * dec(W row n, k) (fp64), then for epi BIAS
+ * Y[i][n] = bf16((float)acc + bias[n]) and for SILU_GATE (W rows [gate; up], N = 2F)
+ * Y[i][f] = bf16((g / (1 + expf(-g))) * u) with g, u the gate and up outputs in fp32.
  * rows == NULL computes every row; acc or Y may be NULL. */
 void oracle_mxfp4_gemm_rows(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
-                            const uint16_t* bias, const int64_t* rows, int64_t nrows, int64_t N, int64_t K,
+                            const uint16_t* bias, const int64_t* rows, int64_t nrows, int64_t N, int64_t K, int epi,
                             double* acc, uint16_t* Y) {
-    mxg_ctx c = {Xq, Xs, Wq, Ws, bias, rows, N, K, acc, Y};
+    mxg_ctx c = {Xq, Xs, Wq, Ws, bias, rows, N, K, epi, acc, Y};
     parallel_rows(nrows, mxg_rows, &c);
 }

@@ -211,7 +211,8 @@ def mxfp4_quantize(X: torch.Tensor, colmul: torch.Tensor | None = None, Q=None, 
 
 def mxfp4_linear(Xq: torch.Tensor, Xs: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor,
                  bias: torch.Tensor | None = None, epilogue: str = "bias", out=None, stream=None) -> torch.Tensor:
-    """Block-scaled FP4 linear: bf16 [M, N] = acc + bias ("bias"), or the fp32 accumulators ("acc_f32").
+    """Block-scaled FP4 linear: bf16 [M, N] = acc + bias ("bias"), bf16 [M, N/2] = silu(gate) * up
+    ("silu_gate", W rows [gate; up]), or the fp32 accumulators ("acc_f32").
     Xq uint8 [M, K/2] and Xs uint8 [M, K/32] from mxfp4_quantize of the activations; Wq, Ws the
     same of the weights."""
     for t, n in ((Xq, "Xq"), (Xs, "Xs"), (Wq, "Wq"), (Ws, "Ws")):
@@ -221,9 +222,10 @@ def mxfp4_linear(Xq: torch.Tensor, Xs: torch.Tensor, Wq: torch.Tensor, Ws: torch
     M, N, K = Xq.shape[0], Wq.shape[0], Xq.shape[1] * 2
     if Wq.shape[1] * 2 != K or Xs.shape != (M, K // 32) or Ws.shape != (N, K // 32):
         raise ValueError("mxfp4_linear: inconsistent operand shapes")
-    epi = {"bias": QDT_EPI_BIAS, "acc_f32": QDT_EPI_ACC_F32}[epilogue]
+    epi = {"bias": QDT_EPI_BIAS, "silu_gate": QDT_EPI_SILU_GATE, "acc_f32": QDT_EPI_ACC_F32}[epilogue]
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32 if epi == QDT_EPI_ACC_F32 else torch.bfloat16,
+        nout = N // 2 if epi == QDT_EPI_SILU_GATE else N
+        out = torch.empty((M, nout), dtype=torch.float32 if epi == QDT_EPI_ACC_F32 else torch.bfloat16,
                           device=Xq.device)
     out, ldy = _rows(out, "out")
     _check(qdt_mxfp4_linear(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(bias), M, N, K, epi, _ptr(out), ldy,

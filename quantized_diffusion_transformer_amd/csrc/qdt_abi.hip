@@ -208,6 +208,7 @@ static int epi_kind(qdt_epilogue e) {
         case QDT_EPI_SILU_GATE: return EPI_SILU;
         case QDT_EPI_HEAD_RMSNORM: return EPI_RMSNORM;
         case QDT_EPI_ACC_I32: return EPI_ACC;
+        default: break;  // QDT_EPI_ACC_F32 belongs to the FP4 linear only
     }
     return -1;
 }
@@ -372,21 +373,23 @@ qdt_status qdt_bf16_linear(const uint16_t* X, const uint16_t* W, const uint16_t*
 qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
                             const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi, void* Y,
                             int64_t ldy, void* stream) {
-    if (epi != QDT_EPI_BIAS && epi != QDT_EPI_ACC_F32) return QDT_EINVAL;
+    if (epi != QDT_EPI_BIAS && epi != QDT_EPI_SILU_GATE && epi != QDT_EPI_ACC_F32) return QDT_EINVAL;
     if (M < 0 || M > INT32_MAX / 2 || N <= 0 || N > INT32_MAX / 2 || N % 16 != 0) return QDT_ESHAPE;
-    if (K <= 0 || K % 256 != 0 || K > QDT_MAX_K || ldy < N) return QDT_ESHAPE;
+    if (epi == QDT_EPI_SILU_GATE && N % 32 != 0) return QDT_ESHAPE;
+    const int64_t nout = epi == QDT_EPI_SILU_GATE ? N / 2 : N;
+    if (K <= 0 || K % 256 != 0 || K > QDT_MAX_K || ldy < nout) return QDT_ESHAPE;
     if (M == 0) return QDT_OK;
     if (!Xq || !Xs || !Wq || !Ws || !Y) return QDT_EINVAL;
     if (!aligned16(Xq) || !aligned16(Wq) || !aligned16(bias) || !aligned16(Y) || ldy % 8 != 0 ||
         (reinterpret_cast<uintptr_t>(Xs) & 3u) != 0 || (reinterpret_cast<uintptr_t>(Ws) & 3u) != 0)
         return QDT_EALIGN;
     const int64_t es = epi == QDT_EPI_ACC_F32 ? 4 : 2;
-    const int64_t ybytes = ((M - 1) * ldy + N) * es;
+    const int64_t ybytes = ((M - 1) * ldy + nout) * es;
     if (overlap(Y, ybytes, Xq, M * K / 2) || overlap(Y, ybytes, Xs, M * K / 32) || overlap(Y, ybytes, Wq, N * K / 2) ||
         overlap(Y, ybytes, Ws, N * K / 32) || overlap(Y, ybytes, bias, bias ? N * 2 : 0))
         return QDT_EALIAS;
     Plan p;
-    qdt_status r = make_plan(M, N, K / 2, EPI_F32BIAS, 1, QDT_TILE_256, 1, &p);
+    qdt_status r = make_plan(M, N, K / 2, epi == QDT_EPI_SILU_GATE ? EPI_SILU : EPI_F32BIAS, 1, QDT_TILE_256, 1, &p);
     if (r != QDT_OK) return r;
     GemmArgs a;
     memset(&a, 0, sizeof(a));
@@ -398,7 +401,7 @@ qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t*
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
-    a.epi = epi == QDT_EPI_ACC_F32 ? EPI_ACC : EPI_F32BIAS;
+    a.epi = epi == QDT_EPI_ACC_F32 ? EPI_ACC : epi == QDT_EPI_SILU_GATE ? EPI_F32SILU : EPI_F32BIAS;
     return hip_status(launch_gemm_mx(a, Xs, Ws, p, reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -173,10 +173,10 @@ gemm_kernel(KArgs p) {
     // (8 bytes per row: the stage's 256 elements are 8 blocks)
     constexpr int NSC = MX ? 4 : 0;
     constexpr int NDMA = NI + NSC;
-    static_assert(!MX || (BM == 256 && BN == 256 && !BF16 && (EPI == EPI_F32BIAS || EPI == EPI_ACC)),
+    static_assert(!MX || (BM == 256 && BN == 256 && !BF16 && (EPI == EPI_F32BIAS || EPI == EPI_F32SILU || EPI == EPI_ACC)),
                   "FP4: 256 x 256 tiles, fp32-accumulator epilogues");
     constexpr int NACC_A = 64;             // accumulator tuples held in AGPRs (the rest in VGPRs)
-    constexpr bool SILU = EPI == EPI_SILU;
+    constexpr bool SILU = EPI == EPI_SILU || EPI == EPI_F32SILU;
     static_assert(WM == 2 && WN == 2 && NBW % 2 == 0 && NBX % 2 == 0, "two waves per operand region");
     static_assert(!SILU || (NIW * 8 == BN / 2 && FN % 2 == 0), "one weight wave per gate / up half");
     constexpr int SP = 4;                  // MFMA slots between consecutive reads of sub-step 0
@@ -194,7 +194,7 @@ gemm_kernel(KArgs p) {
     // w_scale per tile weight row, x_scale per tile token row, bias per weight row (bf16 pairs),
     // gamma per head column (bf16 pairs).
     constexpr bool HAS_SCALE = EPI == EPI_BIAS || EPI == EPI_SILU || EPI == EPI_RMSNORM;
-    constexpr bool HAS_BIAS = HAS_SCALE || EPI == EPI_F32BIAS;
+    constexpr bool HAS_BIAS = HAS_SCALE || EPI == EPI_F32BIAS || EPI == EPI_F32SILU;
     constexpr int P_SW = 0, N_SW = HAS_SCALE ? (BN + 63) / 64 * 64 : 0;
     constexpr int P_SX = P_SW + N_SW, N_SX = HAS_SCALE ? (BM + 63) / 64 * 64 : 0;
     constexpr int P_B = P_SX + N_SX, N_B = HAS_BIAS ? (BN / 2 + 63) / 64 * 64 : 0;
@@ -277,7 +277,8 @@ gemm_kernel(KArgs p) {
     uint32_t ldss = 0;
     if constexpr (MX) {
         const int64_t scb = Kb / 16;  // exponent bytes per row: K / 32 = 2 Kb / 32
-        scbase = uniform_ptr((wwave ? p.wsc + (int64_t)n0 * scb : p.xsc + (int64_t)m0 * scb) + (int64_t)kta * 8);
+        const int wrow0 = (SILU && wave == 1 ? p.F : 0) + n0;  // the up half's rows for SILU
+        scbase = uniform_ptr((wwave ? p.wsc + (int64_t)wrow0 * scb : p.xsc + (int64_t)m0 * scb) + (int64_t)kta * 8);
 #pragma unroll
         for (int i = 0; i < NSC; ++i)
             scvoffs[i] = (uint32_t)(min(rlocal0 + i * 32 + (lane >> 1), rlast) * scb) + (lane & 1) * 4;
@@ -660,6 +661,28 @@ gemm_kernel(KArgs p) {
                 return make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
             });
         }
+    } else if constexpr (EPI == EPI_F32SILU) {
+        // fp32 accumulators (block-scaled FP4): g = acc_g + b_g, u = acc_u + b_u, y = silu(g) u
+        float bg[NF][4], bu[NF][4];
+#pragma unroll
+        for (int fn = 0; fn < NF; ++fn) {
+            const int rl = ncol0 + fn * 16;
+            prm_b4(rl, bg[fn]);
+            prm_b4(BN / 2 + rl, bu[fn]);
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            put_strip(fm, [&](int fn) {
+                float g[4], u[4], y[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    g[r] = (float)acc[fn][fm][r] + bg[fn][r];
+                    u[r] = (float)acc[fn + NF][fm][r] + bu[fn][r];
+                }
+                silu_gate4(g, u, y);
+                return make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+            });
+        }
     } else if constexpr (EPI == EPI_RMSNORM) {
         // The workgroup's BN = 256 columns are exactly one head; each wave holds FN*16 of
         // them, so a head spans the fragments of WN waves.  Row sums of y^2: in-lane over
@@ -897,6 +920,7 @@ hipError_t launch_gemm_mx(const GemmArgs& a, const uint8_t* xsc, const uint8_t* 
     k.wsc = wsc;
     if (pl.tile != QDT_TILE_256 || pl.split_k != 1) return hipErrorInvalidValue;
     if (a.epi == EPI_F32BIAS) return go<8, 8, false, EPI_F32BIAS, true>(k, pl.grid, st);
+    if (a.epi == EPI_F32SILU) return go<8, 8, false, EPI_F32SILU, true>(k, pl.grid, st);
     if (a.epi == EPI_ACC) return go<8, 8, false, EPI_ACC, true>(k, pl.grid, st);
     return hipErrorInvalidValue;
 }

@@ -93,8 +93,10 @@ def test_mxfp4_validation():
         return f(A(0x100000), A(xs), A(0x300000), A(ws), None, M, N, K, epi, A(Y), N if ldy is None else ldy, None)
     assert lin(K=128) == qdt.QDT_ESHAPE                 # whole 256-element stages
     assert lin(N=120) == qdt.QDT_ESHAPE
-    assert lin(epi=1) == qdt.QDT_EINVAL                 # bias or fp32 accumulators only
+    assert lin(epi=2) == qdt.QDT_EINVAL                 # bias, gated SiLU or fp32 accumulators only
     assert lin(epi=3) == qdt.QDT_EINVAL
+    assert lin(epi=1, N=48) == qdt.QDT_ESHAPE           # gate and up halves of whole 16-row fragments
+    assert lin(epi=1, N=128, ldy=32) == qdt.QDT_ESHAPE  # ldy >= F = N / 2
     assert lin(ldy=64) == qdt.QDT_ESHAPE
     assert lin(xs=0x200002) == qdt.QDT_EALIGN           # exponent rows read as dwords
     assert lin(Y=0x300000 + 64) == qdt.QDT_EALIAS        # Y over Wq

@@ -4,14 +4,14 @@ The quantizer's codes and block exponents are gated bit for bit.  The GEMM is ga
 on inputs whose partial sums are exact in fp32 (any summation order gives the exact sum), which
 pins the fragment layout, the nibble order and the placement of every block exponent.  On
 general inputs its bf16 output is gated by 1 bf16 ulp plus the fp32 summation bound
-gamma_K * sum_k |x_k w_k| of the decoded values.
+gamma_K * sum_k |x_k w_k| of the decoded values (carried through silu(g) u for the gated SiLU).
 """
 import numpy as np
 import pytest
 
 import oracle
 import qdt_workloads as W
-from qdt_testutil import bits_equal, sample_rows, to_dev, to_host
+from qdt_testutil import bits_equal, sample_rows, to_dev, to_host, ulp_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -125,3 +125,47 @@ def test_mxfp4_attention_projection_4608():
     assert bits_equal(to_host(Wq), Wqr) and bits_equal(to_host(Ws), Wsr)
     Xqh, Xsh = to_host(Xq), to_host(Xs)
     within_bound(Y, Xqh, Xsh, Wqr, Wsr, d["bias"], rows)
+
+
+@pytest.mark.parametrize("M,F,K", [(300, 272, 512), (64, 128, 1024)])
+def test_mxfp4_silu_gate_exact_sums_within_one_ulp(M, F, K):
+    """With sums exact in fp32, g and u equal the oracle's, so only the exponential and the
+    reciprocal can differ: the output is gated at 1 bf16 ulp, like the W8A8 gate."""
+    announce(f"mxfp4_linear silu_gate exact sums M={M} F={F} K={K}")
+    Xq, Xs = exact_operands(M, K, 70 + M)
+    Wq, Ws = exact_operands(2 * F, K, 80 + F)
+    bias = W.f32_to_bf16_bits(np.random.default_rng(F).standard_normal(2 * F).astype(np.float32) * 4)
+    Y_ref = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, epi="silu_gate")
+    Y = to_host(qdt.mxfp4_linear(to_dev(Xq), to_dev(Xs), to_dev(Wq), to_dev(Ws), to_dev(bias), "silu_gate"))
+    assert Y.shape == (M, F)
+    u = ulp_bf16(Y, Y_ref)
+    assert u.max() <= 1, f"max ulp {u.max()}"
+
+
+@pytest.mark.parametrize("M,F,K", [(300, 1024, 4608)])
+def test_mxfp4_silu_gate_within_bound(M, F, K):
+    """General inputs: the fp32 accumulation error of g and u carried through silu(g) u
+    (|silu'| <= 1.1), plus the fast exponential's relative error and one bf16 ulp."""
+    announce(f"mxfp4_linear silu_gate M={M} F={F} K={K}")
+    d = W.make_linear(M, 2 * F, K, seed=4200 + M, x_kind="pct1", w_sigma=0.015, bias=True)
+    Xq, Xs = check_quant(d["X"])
+    Wq, Ws = check_quant(d["W"])
+    Y = to_host(qdt.mxfp4_linear(Xq, Xs, Wq, Ws, to_dev(d["bias"]), "silu_gate"))
+    rows = sample_rows(M, 24, 8)
+    Xqh, Xsh, Wqh, Wsh = to_host(Xq), to_host(Xs), to_host(Wq), to_host(Ws)
+    Y_ref, acc = oracle.mxfp4_gemm_rows(Xqh, Xsh, Wqh, Wsh, d["bias"], rows, want_acc=True, epi="silu_gate")
+    xd = np.abs(oracle.mxfp4_dequantize(Xqh[rows], Xsh[rows]))
+    wd = np.abs(oracle.mxfp4_dequantize(Wqh, Wsh))
+    gam = K * 2.0 ** -24 / (1 - K * 2.0 ** -24)
+    b = W.bf16_bits_to_f32(d["bias"]).astype(np.float64)
+    ga, ua = acc[:, :F] + b[:F], acc[:, F:] + b[F:]
+    dg = gam * (xd @ wd[:F].T) + np.abs(ga) * 2.0 ** -23
+    du = gam * (xd @ wd[F:].T) + np.abs(ua) * 2.0 ** -23
+    silu = ga / (1.0 + np.exp(-ga))
+    ref = silu * ua
+    bound = 1.1 * dg * (np.abs(ua) + du) + np.abs(silu) * du + 1e-5 * np.abs(ref) \
+        + 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    got = W.bf16_bits_to_f32(Y[rows]).astype(np.float64)
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), f"worst error / bound {np.max(err / bound):.3f}"
+    assert np.mean(Y[rows] == Y_ref) > 0.9

@@ -298,7 +298,8 @@ def cpu_baseline(d):
 EXTRA_WORKLOADS = ("dit_ffn_gate_up_4608x24576x4608", "text_cond_proj_512x4608x53248",
                    "text_cond_proj_padded_4608x4608x53248", "qk_proj_headnorm_16896x4608x4608",
                    "qk_proj_headnorm_6037x4608x4608", "adaln_quantize_4608x4608", "adaln_quantize_16896x4608",
-                   "mxfp4_attn_proj_4608x4608x4608", "mxfp4_ffn_gate_up_4608x24576x4608")
+                   "mxfp4_attn_proj_4608x4608x4608", "mxfp4_ffn_gate_up_4608x24576x4608",
+                   "mxfp4_qk_proj_headnorm_16896x4608x4608")
 
 
 def extra_workloads(args, only=None):
@@ -410,7 +411,9 @@ def extra_workloads(args, only=None):
         if want(name):
             res[name] = adaln_producer(M, 4608, counts)
     for name, src, epi in (("mxfp4_attn_proj_4608x4608x4608", "dit_attn_proj_4608x4608x4608", "bias"),
-                           ("mxfp4_ffn_gate_up_4608x24576x4608", "dit_ffn_gate_up_4608x24576x4608", "silu_gate")):
+                           ("mxfp4_ffn_gate_up_4608x24576x4608", "dit_ffn_gate_up_4608x24576x4608", "silu_gate"),
+                           ("mxfp4_qk_proj_headnorm_16896x4608x4608", "qk_proj_headnorm_16896x4608x4608",
+                            "head_rmsnorm")):
         if want(name):
             res[name] = mxfp4_workload(src, epi, counts)
     torch.cuda.empty_cache()
@@ -432,6 +435,7 @@ def mxfp4_workload(src, epi, counts):
     Xq = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
     Xs = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
     Y = torch.empty((M, N // 2 if epi == "silu_gate" else N), dtype=torch.bfloat16, device="cuda")
+    g = to_dev(d["gamma"]) if epi == "head_rmsnorm" else None
 
     def step(_, ev):
         if ev is not None:
@@ -439,7 +443,7 @@ def mxfp4_workload(src, epi, counts):
         qdt.mxfp4_quantize(X, None, Xq, Xs)
         if ev is not None:
             ev[1].record()
-        qdt.mxfp4_linear(Xq, Xs, Wq, Ws, b, epi, out=Y)
+        qdt.mxfp4_linear(Xq, Xs, Wq, Ws, b, epi, gamma=g, eps=d.get("eps", 1e-6), out=Y)
         if ev is not None:
             ev[2].record()
     steps, warm = counts(step)

@@ -200,6 +200,8 @@ qdt_status qdt_mxfp4_quantize(const uint16_t* X, const float* colmul, int64_t M,
  *   QDT_EPI_SILU_GATE: W rows [gate(0..F-1); up(F..2F-1)], N = 2F (N % 32 == 0), Y bf16 [M, ldy >= F]:
  *     g = acc[m][f] + bias[f], u = acc[m][F+f] + bias[F+f], Y[m][f] = bf16_rne((g / (1 + exp(-g))) * u)
  *     ([FAL] gated-SiLU epilogue; the exponential and reciprocal as in the W8A8 SILU epilogue);
+ *   QDT_EPI_HEAD_RMSNORM: y = acc + bias; per row and head of 256 columns r = 1/sqrtf(mean(y^2) + eps),
+ *     Y = bf16_rne((y * r) * gamma[n mod 256]) (epi_params: qdt_rmsnorm_params, as for qdt_w8a8_linear);
  *   QDT_EPI_ACC_F32: Y fp32 [M, ldy], the accumulators.
  *   Xq / Xs: qdt_mxfp4_quantize of the activations ([M, K/2] codes, [M, K/32] exponents); Wq / Ws
  *   the same of the weights ([N, K/2], [N, K/32]).  K % 256 == 0 (whole 128-byte stages of codes),
@@ -208,8 +210,8 @@ qdt_status qdt_mxfp4_quantize(const uint16_t* X, const float* colmul, int64_t M,
  *   The scales of the block exponents are powers of two, so they take no rounding of their own.
  */
 qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
-                            const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi, void* Y,
-                            int64_t ldy, void* stream);
+                            const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi,
+                            const void* epi_params, void* Y, int64_t ldy, void* stream);
 
 /* The plan qdt_w8a8_linear uses for this problem (pure host computation, no device call). */
 qdt_status qdt_w8a8_linear_plan(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, qdt_linear_plan* plan);

@@ -56,7 +56,7 @@ def lib():
             "oracle_adaln_modulate": ([P, I64, I64, I64, P, P, F, P], None),
             "oracle_fp4_value": ([I], C.c_double),
             "oracle_mxfp4_quantize_rows": ([P, P, I64, I64, I64, P, P], None),
-            "oracle_mxfp4_gemm_rows": ([P, P, P, P, P, P, I64, I64, I64, I, P, P], None),
+            "oracle_mxfp4_gemm_rows": ([P, P, P, P, P, P, I64, I64, I64, I, P, F, P, P], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -241,9 +241,10 @@ def mxfp4_dequantize(Q, S) -> np.ndarray:
     return table[codes] * np.ldexp(1.0, np.repeat(S.astype(np.int64) - 127, 32, axis=1))
 
 
-def mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias=None, rows=None, want_acc=False, epi="bias"):
+def mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias=None, rows=None, want_acc=False, epi="bias", gamma=None, eps=1e-6):
     """fp64 accumulators of the decoded product and the bf16 output of epilogue ``epi`` ("bias":
-    bf16((float)acc + bias); "silu_gate": W rows [gate; up], bf16(silu(g) * u)) for the given rows."""
+    bf16((float)acc + bias); "silu_gate": W rows [gate; up], bf16(silu(g) * u); "head_rmsnorm":
+    per 256-column head with gamma) for the given rows."""
     e = _EPI[epi]
     Xq, Xs, Wq, Ws = (_c(a, np.uint8) for a in (Xq, Xs, Wq, Ws))
     N, K = Wq.shape[0], Wq.shape[1] * 2
@@ -252,5 +253,5 @@ def mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias=None, rows=None, want_acc=False, epi="b
     Y = np.empty((nr, _n_out(N, e)), np.uint16)
     acc = np.empty((nr, N), np.float64) if want_acc else None
     lib().oracle_mxfp4_gemm_rows(_p(Xq), _p(Xs), _p(Wq), _p(Ws), _p(_c(bias, np.uint16)), _p(r), nr, N, K, e,
-                                 _p(acc), _p(Y))
+                                 _p(_c(gamma, np.uint16)), eps, _p(acc), _p(Y))
     return (Y, acc) if want_acc else Y

@@ -488,7 +488,7 @@ static double mx_elem(const uint8_t* q, const uint8_t* s, int64_t j) {
 
 typedef struct {
     const uint8_t* Xq; const uint8_t* Xs; const uint8_t* Wq; const uint8_t* Ws; const uint16_t* bias;
-    const int64_t* rows; int64_t N, K; int epi; double* acc; uint16_t* Y;
+    const int64_t* rows; int64_t N, K; int epi; const uint16_t* gamma; float eps; double* acc; uint16_t* Y;
 } mxg_ctx;
 
 static void mxg_rows(void* p, int64_t i0, int64_t i1) {
@@ -514,6 +514,19 @@ static void mxg_rows(void* p, int64_t i0, int64_t i1) {
                 float u = (float)a[F + f] + (c->bias ? oracle_bf16_to_f32(c->bias[F + f]) : 0.0f);
                 c->Y[i * F + f] = oracle_f32_to_bf16((g / (1.0f + expf(-g))) * u);
             }
+        } else if (c->epi == ORACLE_EPI_HEAD_RMSNORM) {
+            for (int64_t h0 = 0; h0 < c->N; h0 += 256) {
+                float y[256];
+                double ss = 0.0;
+                for (int d = 0; d < 256; ++d) {
+                    y[d] = (float)a[h0 + d] + (c->bias ? oracle_bf16_to_f32(c->bias[h0 + d]) : 0.0f);
+                    ss += (double)y[d] * (double)y[d];
+                }
+                float ms = (float)ss / 256.0f;
+                float r = 1.0f / sqrtf(ms + c->eps);
+                for (int d = 0; d < 256; ++d)
+                    c->Y[i * c->N + h0 + d] = oracle_f32_to_bf16((y[d] * r) * oracle_bf16_to_f32(c->gamma[d]));
+            }
         } else {
             for (int64_t n = 0; n < c->N; ++n) {
                 float b = c->bias ? oracle_bf16_to_f32(c->bias[n]) : 0.0f;
@@ -524,13 +537,14 @@ static void mxg_rows(void* p, int64_t i0, int64_t i1) {
     free(a);
 }
 
-/* acc[i][n] = sum_k dec(X row rows[i], k) * dec(W row n, k) (fp64), then for epi BIAS
- * Y[i][n] = bf16((float)acc + bias[n]) and for SILU_GATE (W rows [gate; up], N = 2F)
- * Y[i][f] = bf16((g / (1 + expf(-g))) * u) with g, u the gate and up outputs in fp32.
+/* acc[i][n] = sum_k dec(X row rows[i], k) * dec(W row n, k) (fp64), then with y = (float)acc + bias
+ * (fp32): BIAS Y = bf16(y); SILU_GATE (W rows [gate; up], N = 2F) Y[i][f] = bf16((g / (1 + expf(-g)))
+ * * u) with g, u the gate and up values of y; HEAD_RMSNORM per 256-column head as the W8A8 epilogue
+ * (fp64 sum of y^2, r = 1 / sqrtf(ms + eps), Y = bf16((y * r) * gamma)).
  * rows == NULL computes every row; acc or Y may be NULL. */
 void oracle_mxfp4_gemm_rows(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
                             const uint16_t* bias, const int64_t* rows, int64_t nrows, int64_t N, int64_t K, int epi,
-                            double* acc, uint16_t* Y) {
-    mxg_ctx c = {Xq, Xs, Wq, Ws, bias, rows, N, K, epi, acc, Y};
+                            const uint16_t* gamma, float eps, double* acc, uint16_t* Y) {
+    mxg_ctx c = {Xq, Xs, Wq, Ws, bias, rows, N, K, epi, gamma, eps, acc, Y};
     parallel_rows(nrows, mxg_rows, &c);
 }

@@ -57,7 +57,7 @@ _SIGS = {
     "qdt_quantize_per_token": ([_P, _P, _I64, _I64, _I64, _P, _P, _P], _I),
     "qdt_adaln_quantize": ([_P, _I64, _P, _P, _F, _P, _I64, _I64, _P, _P, _P, _P], _I),
     "qdt_mxfp4_quantize": ([_P, _P, _I64, _I64, _I64, _P, _P, _P], _I),
-    "qdt_mxfp4_linear": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _P], _I),
+    "qdt_mxfp4_linear": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P], _I),
     "qdt_w8a8_linear_plan": ([_I64, _I64, _I64, _I, C.POINTER(qdt_linear_plan)], _I),
     "qdt_w8a8_linear_plan_for": ([_I64, _I64, _I64, _I, C.c_int32, C.c_int32, C.POINTER(qdt_linear_plan)], _I),
     "qdt_w8a8_linear_workspace_size": ([_I64, _I64, _I64, _I, C.POINTER(_SZ)], _I),
@@ -210,9 +210,11 @@ def mxfp4_quantize(X: torch.Tensor, colmul: torch.Tensor | None = None, Q=None, 
 
 
 def mxfp4_linear(Xq: torch.Tensor, Xs: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor,
-                 bias: torch.Tensor | None = None, epilogue: str = "bias", out=None, stream=None) -> torch.Tensor:
+                 bias: torch.Tensor | None = None, epilogue: str = "bias", gamma=None, eps: float = 1e-6, out=None,
+                 stream=None) -> torch.Tensor:
     """Block-scaled FP4 linear: bf16 [M, N] = acc + bias ("bias"), bf16 [M, N/2] = silu(gate) * up
-    ("silu_gate", W rows [gate; up]), or the fp32 accumulators ("acc_f32").
+    ("silu_gate", W rows [gate; up]), RMSNorm of acc + bias over 256-wide heads with gamma
+    ("head_rmsnorm"), or the fp32 accumulators ("acc_f32").
     Xq uint8 [M, K/2] and Xs uint8 [M, K/32] from mxfp4_quantize of the activations; Wq, Ws the
     same of the weights."""
     for t, n in ((Xq, "Xq"), (Xs, "Xs"), (Wq, "Wq"), (Ws, "Ws")):
@@ -222,13 +224,21 @@ def mxfp4_linear(Xq: torch.Tensor, Xs: torch.Tensor, Wq: torch.Tensor, Ws: torch
     M, N, K = Xq.shape[0], Wq.shape[0], Xq.shape[1] * 2
     if Wq.shape[1] * 2 != K or Xs.shape != (M, K // 32) or Ws.shape != (N, K // 32):
         raise ValueError("mxfp4_linear: inconsistent operand shapes")
-    epi = {"bias": QDT_EPI_BIAS, "silu_gate": QDT_EPI_SILU_GATE, "acc_f32": QDT_EPI_ACC_F32}[epilogue]
+    epi = {"bias": QDT_EPI_BIAS, "silu_gate": QDT_EPI_SILU_GATE, "head_rmsnorm": QDT_EPI_HEAD_RMSNORM,
+           "acc_f32": QDT_EPI_ACC_F32}[epilogue]
+    params = None
+    if epi == QDT_EPI_HEAD_RMSNORM:
+        if gamma is None:
+            raise ValueError("head_rmsnorm needs gamma (bf16 [256])")
+        _dev(gamma, torch.bfloat16, "gamma")
+        params = qdt_rmsnorm_params(gamma.data_ptr(), 256, float(eps))
     if out is None:
         nout = N // 2 if epi == QDT_EPI_SILU_GATE else N
         out = torch.empty((M, nout), dtype=torch.float32 if epi == QDT_EPI_ACC_F32 else torch.bfloat16,
                           device=Xq.device)
     out, ldy = _rows(out, "out")
-    _check(qdt_mxfp4_linear(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(bias), M, N, K, epi, _ptr(out), ldy,
+    _check(qdt_mxfp4_linear(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(bias), M, N, K, epi,
+                            None if params is None else C.cast(C.byref(params), C.c_void_p), _ptr(out), ldy,
                             _stream(stream)), "qdt_mxfp4_linear")
     return out
 

@@ -371,11 +371,20 @@ qdt_status qdt_bf16_linear(const uint16_t* X, const uint16_t* W, const uint16_t*
 }
 
 qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
-                            const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi, void* Y,
-                            int64_t ldy, void* stream) {
-    if (epi != QDT_EPI_BIAS && epi != QDT_EPI_SILU_GATE && epi != QDT_EPI_ACC_F32) return QDT_EINVAL;
+                            const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi,
+                            const void* epi_params, void* Y, int64_t ldy, void* stream) {
+    if (epi != QDT_EPI_BIAS && epi != QDT_EPI_SILU_GATE && epi != QDT_EPI_HEAD_RMSNORM && epi != QDT_EPI_ACC_F32)
+        return QDT_EINVAL;
     if (M < 0 || M > INT32_MAX / 2 || N <= 0 || N > INT32_MAX / 2 || N % 16 != 0) return QDT_ESHAPE;
     if (epi == QDT_EPI_SILU_GATE && N % 32 != 0) return QDT_ESHAPE;
+    const qdt_rmsnorm_params* rp = reinterpret_cast<const qdt_rmsnorm_params*>(epi_params);
+    if (epi == QDT_EPI_HEAD_RMSNORM) {
+        if (N % 256 != 0) return QDT_ESHAPE;
+        if (!rp || !rp->gamma) return QDT_EINVAL;
+        if (rp->head_dim != 256) return QDT_ESHAPE;
+        if (!(rp->eps >= 0.0f) || rp->eps > 3.0e38f) return QDT_EINVAL;
+        if (!aligned16(rp->gamma)) return QDT_EALIGN;
+    }
     const int64_t nout = epi == QDT_EPI_SILU_GATE ? N / 2 : N;
     if (K <= 0 || K % 256 != 0 || K > QDT_MAX_K || ldy < nout) return QDT_ESHAPE;
     if (M == 0) return QDT_OK;
@@ -386,10 +395,12 @@ qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t*
     const int64_t es = epi == QDT_EPI_ACC_F32 ? 4 : 2;
     const int64_t ybytes = ((M - 1) * ldy + nout) * es;
     if (overlap(Y, ybytes, Xq, M * K / 2) || overlap(Y, ybytes, Xs, M * K / 32) || overlap(Y, ybytes, Wq, N * K / 2) ||
-        overlap(Y, ybytes, Ws, N * K / 32) || overlap(Y, ybytes, bias, bias ? N * 2 : 0))
+        overlap(Y, ybytes, Ws, N * K / 32) || overlap(Y, ybytes, bias, bias ? N * 2 : 0) ||
+        overlap(Y, ybytes, epi == QDT_EPI_HEAD_RMSNORM ? rp->gamma : nullptr, 512))
         return QDT_EALIAS;
     Plan p;
-    qdt_status r = make_plan(M, N, K / 2, epi == QDT_EPI_SILU_GATE ? EPI_SILU : EPI_F32BIAS, 1, QDT_TILE_256, 1, &p);
+    const int pk = epi == QDT_EPI_SILU_GATE ? EPI_SILU : epi == QDT_EPI_HEAD_RMSNORM ? EPI_RMSNORM : EPI_F32BIAS;
+    qdt_status r = make_plan(M, N, K / 2, pk, 1, QDT_TILE_256, 1, &p);
     if (r != QDT_OK) return r;
     GemmArgs a;
     memset(&a, 0, sizeof(a));
@@ -401,7 +412,12 @@ qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t*
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
-    a.epi = epi == QDT_EPI_ACC_F32 ? EPI_ACC : epi == QDT_EPI_SILU_GATE ? EPI_F32SILU : EPI_F32BIAS;
+    a.gamma = epi == QDT_EPI_HEAD_RMSNORM ? rp->gamma : nullptr;
+    a.eps = epi == QDT_EPI_HEAD_RMSNORM ? rp->eps : 0.0f;
+    a.epi = epi == QDT_EPI_ACC_F32         ? EPI_ACC
+            : epi == QDT_EPI_SILU_GATE     ? EPI_F32SILU
+            : epi == QDT_EPI_HEAD_RMSNORM  ? EPI_F32RMSNORM
+                                           : EPI_F32BIAS;
     return hip_status(launch_gemm_mx(a, Xs, Ws, p, reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -173,10 +173,12 @@ gemm_kernel(KArgs p) {
     // (8 bytes per row: the stage's 256 elements are 8 blocks)
     constexpr int NSC = MX ? 4 : 0;
     constexpr int NDMA = NI + NSC;
-    static_assert(!MX || (BM == 256 && BN == 256 && !BF16 && (EPI == EPI_F32BIAS || EPI == EPI_F32SILU || EPI == EPI_ACC)),
+    static_assert(!MX || (BM == 256 && BN == 256 && !BF16 &&
+                          (EPI == EPI_F32BIAS || EPI == EPI_F32SILU || EPI == EPI_F32RMSNORM || EPI == EPI_ACC)),
                   "FP4: 256 x 256 tiles, fp32-accumulator epilogues");
     constexpr int NACC_A = 64;             // accumulator tuples held in AGPRs (the rest in VGPRs)
     constexpr bool SILU = EPI == EPI_SILU || EPI == EPI_F32SILU;
+    constexpr bool RMS = EPI == EPI_RMSNORM || EPI == EPI_F32RMSNORM;
     static_assert(WM == 2 && WN == 2 && NBW % 2 == 0 && NBX % 2 == 0, "two waves per operand region");
     static_assert(!SILU || (NIW * 8 == BN / 2 && FN % 2 == 0), "one weight wave per gate / up half");
     constexpr int SP = 4;                  // MFMA slots between consecutive reads of sub-step 0
@@ -189,16 +191,16 @@ gemm_kernel(KArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * STAGE];
     constexpr int SCST = ROWS * 8;  // block-exponent bytes per stage (FP4)
     __shared__ __attribute__((aligned(16))) uint8_t smem_sc[MX ? NB * SCST : 16];
-    __shared__ float red[EPI == EPI_RMSNORM ? WN * BM : 1];
+    __shared__ float red[RMS ? WN * BM : 1];
     // Epilogue parameters staged in LDS (dwords, each array padded to whole 64-lane DMA chunks):
     // w_scale per tile weight row, x_scale per tile token row, bias per weight row (bf16 pairs),
     // gamma per head column (bf16 pairs).
     constexpr bool HAS_SCALE = EPI == EPI_BIAS || EPI == EPI_SILU || EPI == EPI_RMSNORM;
-    constexpr bool HAS_BIAS = HAS_SCALE || EPI == EPI_F32BIAS || EPI == EPI_F32SILU;
+    constexpr bool HAS_BIAS = HAS_SCALE || EPI == EPI_F32BIAS || EPI == EPI_F32SILU || EPI == EPI_F32RMSNORM;
     constexpr int P_SW = 0, N_SW = HAS_SCALE ? (BN + 63) / 64 * 64 : 0;
     constexpr int P_SX = P_SW + N_SW, N_SX = HAS_SCALE ? (BM + 63) / 64 * 64 : 0;
     constexpr int P_B = P_SX + N_SX, N_B = HAS_BIAS ? (BN / 2 + 63) / 64 * 64 : 0;
-    constexpr int P_G = P_B + N_B, N_G = EPI == EPI_RMSNORM ? 128 : 0;
+    constexpr int P_G = P_B + N_B, N_G = RMS ? 128 : 0;
     constexpr int P_BF = P_G + N_G, N_BF = HAS_BIAS ? (BN + 63) / 64 * 64 : 0;  // bias as fp32 (epilogue)
     constexpr int NPRM = P_BF + N_BF;
     __shared__ __attribute__((aligned(16))) uint32_t prm[NPRM > 0 ? NPRM : 1];
@@ -683,29 +685,39 @@ gemm_kernel(KArgs p) {
                 return make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
             });
         }
-    } else if constexpr (EPI == EPI_RMSNORM) {
+    } else if constexpr (RMS) {
         // The workgroup's BN = 256 columns are exactly one head; each wave holds FN*16 of
         // them, so a head spans the fragments of WN waves.  Row sums of y^2: in-lane over
         // fragments, across the 4 lane groups with shuffles, across waves through LDS, in a
         // fixed order.
         static_assert(BN == 256, "one head per tile");
+        // y: the dequantized output plus bias (int8), or the fp32 accumulator plus bias (FP4)
+        constexpr bool F32 = EPI == EPI_F32RMSNORM;
         float sxv[FM], ss[FM];
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-            sxv[fm] = prm_sxf(fm);
+            sxv[fm] = F32 ? 0.0f : prm_sxf(fm);
             ss[fm] = 0.0f;
         }
         float swv[FN][4], bv[FN][4];
+        auto yv = [&](int fn, int fm, int r) __attribute__((always_inline)) {
+            if constexpr (F32)
+                return (float)acc[fn][fm][r] + bv[fn][r];
+            else
+                return dequant(acc[fn][fm][r], sxv[fm], swv[fn][r], bv[fn][r]);
+        };
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            const float4 sw = prm_sw4(ncol0 + fn * 16);
-            swv[fn][0] = sw.x; swv[fn][1] = sw.y; swv[fn][2] = sw.z; swv[fn][3] = sw.w;
+            if constexpr (!F32) {
+                const float4 sw = prm_sw4(ncol0 + fn * 16);
+                swv[fn][0] = sw.x; swv[fn][1] = sw.y; swv[fn][2] = sw.z; swv[fn][3] = sw.w;
+            }
             prm_b4(ncol0 + fn * 16, bv[fn]);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float y = dequant(acc[fn][fm][r], sxv[fm], swv[fn][r], bv[fn][r]);
+                    const float y = yv(fn, fm, r);
                     ss[fm] += y * y;
                 }
         }
@@ -739,7 +751,7 @@ gemm_kernel(KArgs p) {
                 float o[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float y = dequant(acc[fn][fm][r], sxv[fm], swv[fn][r], bv[fn][r]);
+                    const float y = yv(fn, fm, r);
                     o[r] = (y * rinv[fm]) * g[fn][r];
                 }
                 return make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
@@ -921,6 +933,7 @@ hipError_t launch_gemm_mx(const GemmArgs& a, const uint8_t* xsc, const uint8_t* 
     if (pl.tile != QDT_TILE_256 || pl.split_k != 1) return hipErrorInvalidValue;
     if (a.epi == EPI_F32BIAS) return go<8, 8, false, EPI_F32BIAS, true>(k, pl.grid, st);
     if (a.epi == EPI_F32SILU) return go<8, 8, false, EPI_F32SILU, true>(k, pl.grid, st);
+    if (a.epi == EPI_F32RMSNORM) return go<8, 8, false, EPI_F32RMSNORM, true>(k, pl.grid, st);
     if (a.epi == EPI_ACC) return go<8, 8, false, EPI_ACC, true>(k, pl.grid, st);
     return hipErrorInvalidValue;
 }

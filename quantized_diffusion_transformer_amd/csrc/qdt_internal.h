@@ -27,10 +27,10 @@ hipError_t launch_mx_quant(const uint16_t* X, int64_t ldx, const float* colmul, 
                            uint8_t* S, hipStream_t st);
 
 // ------------------------------------------------------------------ GEMM
-// F32BIAS / F32SILU: the fp32-accumulator forms (bf16 and block-scaled FP4 GEMMs) of BIAS / SILU,
-// with no scales: y = acc + bias.
+// F32BIAS / F32SILU / F32RMSNORM: the fp32-accumulator forms (bf16 and block-scaled FP4 GEMMs) of
+// BIAS / SILU / RMSNORM, with no scales: y = acc + bias.
 enum EpiKind { EPI_BIAS = 0, EPI_SILU = 1, EPI_RMSNORM = 2, EPI_ACC = 3, EPI_PARTIAL = 4, EPI_F32BIAS = 5,
-               EPI_F32SILU = 6 };
+               EPI_F32SILU = 6, EPI_F32RMSNORM = 7 };
 
 struct Plan {
     int tile;       // qdt_tile
@@ -61,8 +61,8 @@ struct GemmArgs {
 hipError_t launch_gemm_i8(const GemmArgs& a, const Plan& p, hipStream_t st);
 hipError_t launch_gemm_bf16(const GemmArgs& a, const Plan& p, hipStream_t st);
 // Block-scaled FP4 GEMM (256 x 256 tiles, no K split): a.K is the element count; xsc / wsc the
-// biased block exponents [M][K/32] / [N][K/32]; a.epi EPI_F32BIAS, EPI_F32SILU or EPI_ACC (fp32
-// accumulators).
+// biased block exponents [M][K/32] / [N][K/32]; a.epi EPI_F32BIAS, EPI_F32SILU, EPI_F32RMSNORM or
+// EPI_ACC (fp32 accumulators).
 hipError_t launch_gemm_mx(const GemmArgs& a, const uint8_t* xsc, const uint8_t* wsc, const Plan& p, hipStream_t st);
 // Sum of the S int32 partial slices followed by epilogue `epi` (BIAS, SILU, RMSNORM, ACC).
 hipError_t launch_splitk_epilogue(const GemmArgs& a, int split_k, int epi, hipStream_t st);

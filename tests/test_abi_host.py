@@ -90,11 +90,13 @@ def test_mxfp4_validation():
     f = qdt.qdt_mxfp4_linear
 
     def lin(M=64, N=128, K=256, epi=0, Y=0x900000, ldy=None, xs=0x200000, ws=0x400000):
-        return f(A(0x100000), A(xs), A(0x300000), A(ws), None, M, N, K, epi, A(Y), N if ldy is None else ldy, None)
+        return f(A(0x100000), A(xs), A(0x300000), A(ws), None, M, N, K, epi, None, A(Y), N if ldy is None else ldy,
+                 None)
     assert lin(K=128) == qdt.QDT_ESHAPE                 # whole 256-element stages
     assert lin(N=120) == qdt.QDT_ESHAPE
-    assert lin(epi=2) == qdt.QDT_EINVAL                 # bias, gated SiLU or fp32 accumulators only
-    assert lin(epi=3) == qdt.QDT_EINVAL
+    assert lin(epi=2, N=512) == qdt.QDT_EINVAL          # head RMSNorm without its parameters
+    assert lin(epi=2, N=384) == qdt.QDT_ESHAPE          # whole 256-column heads
+    assert lin(epi=3) == qdt.QDT_EINVAL                 # int32 accumulators are the W8A8 linear's
     assert lin(epi=1, N=48) == qdt.QDT_ESHAPE           # gate and up halves of whole 16-row fragments
     assert lin(epi=1, N=128, ldy=32) == qdt.QDT_ESHAPE  # ldy >= F = N / 2
     assert lin(ldy=64) == qdt.QDT_ESHAPE

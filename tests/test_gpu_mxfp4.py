@@ -169,3 +169,53 @@ def test_mxfp4_silu_gate_within_bound(M, F, K):
     err = np.abs(got - ref)
     assert np.all(err <= bound), f"worst error / bound {np.max(err / bound):.3f}"
     assert np.mean(Y[rows] == Y_ref) > 0.9
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 512, 512), (64, 256, 1024)])
+def test_mxfp4_head_rmsnorm_exact_sums_within_one_ulp(M, N, K):
+    """With sums exact in fp32 the per-head statistics differ only in summation order."""
+    announce(f"mxfp4_linear head_rmsnorm exact sums M={M} N={N} K={K}")
+    Xq, Xs = exact_operands(M, K, 90 + M)
+    Wq, Ws = exact_operands(N, K, 100 + N)
+    rng = np.random.default_rng(N)
+    bias = W.f32_to_bf16_bits(rng.standard_normal(N).astype(np.float32))
+    gamma = W.f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(256)).astype(np.float32))
+    Y_ref = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, epi="head_rmsnorm", gamma=gamma, eps=1e-6)
+    Y = to_host(qdt.mxfp4_linear(to_dev(Xq), to_dev(Xs), to_dev(Wq), to_dev(Ws), to_dev(bias), "head_rmsnorm",
+                                 gamma=to_dev(gamma), eps=1e-6))
+    u = ulp_bf16(Y, Y_ref)
+    assert u.max() <= 1, f"max ulp {u.max()}"
+
+
+def test_mxfp4_head_rmsnorm_within_bound():
+    """General inputs: the fp32 accumulation error of y carried through the per-head normalization."""
+    M, N, K = 300, 4608, 4608
+    announce(f"mxfp4_linear head_rmsnorm M={M} N={N} K={K}")
+    d = W.make_linear(M, N, K, seed=4300, x_kind="pct1", w_sigma=0.015, bias=True, epi="head_rmsnorm")
+    Xq, Xs = check_quant(d["X"])
+    Wq, Ws = check_quant(d["W"])
+    Y = to_host(qdt.mxfp4_linear(Xq, Xs, Wq, Ws, to_dev(d["bias"]), "head_rmsnorm", gamma=to_dev(d["gamma"]),
+                                 eps=d["eps"]))
+    rows = sample_rows(M, 16, 10)
+    Xqh, Xsh, Wqh, Wsh = to_host(Xq), to_host(Xs), to_host(Wq), to_host(Ws)
+    Y_ref, acc = oracle.mxfp4_gemm_rows(Xqh, Xsh, Wqh, Wsh, d["bias"], rows, want_acc=True, epi="head_rmsnorm",
+                                        gamma=d["gamma"], eps=d["eps"])
+    xd = np.abs(oracle.mxfp4_dequantize(Xqh[rows], Xsh[rows]))
+    wd = np.abs(oracle.mxfp4_dequantize(Wqh, Wsh))
+    gam = K * 2.0 ** -24 / (1 - K * 2.0 ** -24)
+    y = acc + W.bf16_bits_to_f32(d["bias"]).astype(np.float64)
+    dy = gam * (xd @ wd.T) + np.abs(y) * 2.0 ** -23
+    g = W.bf16_bits_to_f32(d["gamma"]).astype(np.float64)
+    got = W.bf16_bits_to_f32(Y[rows]).astype(np.float64)
+    for h in range(N // 256):
+        sl = slice(h * 256, (h + 1) * 256)
+        yh, dyh = y[:, sl], dy[:, sl]
+        ms = (yh ** 2).mean(axis=1, keepdims=True) + d["eps"]
+        r = 1.0 / np.sqrt(ms)
+        ref = yh * r * g
+        dr = r * (np.abs(yh) * dyh).mean(axis=1, keepdims=True) / ms + r * 2.0 ** -21  # first order, plus fp32 ops
+        bound = 2.0 * np.abs(g) * (dyh * r + np.abs(yh) * dr) \
+            + 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+        err = np.abs(got[:, sl] - ref)
+        assert np.all(err <= bound), f"head {h}: worst error / bound {np.max(err / bound):.3f}"
+    assert np.mean(Y[rows] == Y_ref) > 0.9

@@ -513,6 +513,23 @@ def test_mx_column_multiplier_is_applied_first():
     assert not np.array_equal(oracle.mxfp4_quantize(X, mul)[0], oracle.mxfp4_quantize(X)[0])
 
 
+def test_mx_head_rmsnorm_normalizes_each_head():
+    rng = np.random.default_rng(35)
+    M, N, K = 3, 512, 256
+    Xq, Xs = oracle.mxfp4_quantize(bf(rng.standard_normal((M, K))))
+    Wq, Ws = oracle.mxfp4_quantize(bf(rng.standard_normal((N, K)) * 0.05))
+    gamma = bf(1.0 + 0.1 * rng.standard_normal(256))
+    bias = bf(0.01 * rng.standard_normal(N))
+    Y, acc = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, want_acc=True, epi="head_rmsnorm", gamma=gamma, eps=1e-6)
+    g = f32(gamma).astype(np.float64)
+    y = acc + f32(bias).astype(np.float64)
+    for h in range(N // 256):
+        yh = y[:, h * 256:(h + 1) * 256]
+        want = yh / np.sqrt((yh ** 2).mean(axis=1, keepdims=True) + 1e-6) * g
+        got = f32(Y[:, h * 256:(h + 1) * 256]).astype(np.float64)
+        assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -7 + 1e-30)
+
+
 def test_mx_gemm_exact_against_rationals():
     from fractions import Fraction
     rng = np.random.default_rng(33)

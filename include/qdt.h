@@ -205,13 +205,21 @@ qdt_status qdt_mxfp4_quantize(const uint16_t* X, const float* colmul, int64_t M,
  *   QDT_EPI_ACC_F32: Y fp32 [M, ldy], the accumulators.
  *   Xq / Xs: qdt_mxfp4_quantize of the activations ([M, K/2] codes, [M, K/32] exponents); Wq / Ws
  *   the same of the weights ([N, K/2], [N, K/32]).  K % 256 == 0 (whole 128-byte stages of codes),
- *   N % 16 == 0, ldy >= N, ldy % 8 == 0; code and Y pointers 16-byte aligned, exponent rows
- *   4-byte aligned (K % 128 == 0 gives that).  Y must not overlap an input.  M = 0 is a no-op.
+ *   N % 16 == 0, ldy >= N (F for the gated SiLU), ldy % 8 == 0; code and Y pointers 16-byte aligned,
+ *   exponent rows 4-byte aligned (K % 128 == 0 gives that).  Y must not overlap an input.
+ *   When the plan splits K (deep K, few output tiles: qdt_mxfp4_linear_plan), the slices write fp32
+ *   partial sums to `workspace` (plan.workspace_bytes = split_k * M * N * 4, 16-byte aligned, caller
+ *   owned) and a second kernel adds them in slice order before the epilogue; otherwise workspace may
+ *   be NULL.  QDT_EWORKSPACE if it is missing or too small.  M = 0 is a no-op.
  *   The scales of the block exponents are powers of two, so they take no rounding of their own.
  */
 qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
                             const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi,
-                            const void* epi_params, void* Y, int64_t ldy, void* stream);
+                            const void* epi_params, void* Y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* The plan qdt_mxfp4_linear uses (tile, K split, workspace bytes).  Pure host computation. */
+qdt_status qdt_mxfp4_linear_plan(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, qdt_linear_plan* plan);
 
 /* The plan qdt_w8a8_linear uses for this problem (pure host computation, no device call). */
 qdt_status qdt_w8a8_linear_plan(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, qdt_linear_plan* plan);

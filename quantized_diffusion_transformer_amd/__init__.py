@@ -57,7 +57,8 @@ _SIGS = {
     "qdt_quantize_per_token": ([_P, _P, _I64, _I64, _I64, _P, _P, _P], _I),
     "qdt_adaln_quantize": ([_P, _I64, _P, _P, _F, _P, _I64, _I64, _P, _P, _P, _P], _I),
     "qdt_mxfp4_quantize": ([_P, _P, _I64, _I64, _I64, _P, _P, _P], _I),
-    "qdt_mxfp4_linear": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P], _I),
+    "qdt_mxfp4_linear": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P, _SZ, _P], _I),
+    "qdt_mxfp4_linear_plan": ([_I64, _I64, _I64, _I, C.POINTER(qdt_linear_plan)], _I),
     "qdt_w8a8_linear_plan": ([_I64, _I64, _I64, _I, C.POINTER(qdt_linear_plan)], _I),
     "qdt_w8a8_linear_plan_for": ([_I64, _I64, _I64, _I, C.c_int32, C.c_int32, C.POINTER(qdt_linear_plan)], _I),
     "qdt_w8a8_linear_workspace_size": ([_I64, _I64, _I64, _I, C.POINTER(_SZ)], _I),
@@ -209,9 +210,19 @@ def mxfp4_quantize(X: torch.Tensor, colmul: torch.Tensor | None = None, Q=None, 
     return Q, S
 
 
+_MX_EPI = {"bias": QDT_EPI_BIAS, "silu_gate": QDT_EPI_SILU_GATE, "head_rmsnorm": QDT_EPI_HEAD_RMSNORM,
+           "acc_f32": QDT_EPI_ACC_F32}
+
+
+def mxfp4_linear_plan(M: int, N: int, K: int, epilogue: str = "bias") -> dict:
+    p = qdt_linear_plan()
+    _check(qdt_mxfp4_linear_plan(M, N, K, _MX_EPI[epilogue], C.byref(p)), "qdt_mxfp4_linear_plan")
+    return p.as_dict()
+
+
 def mxfp4_linear(Xq: torch.Tensor, Xs: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor,
                  bias: torch.Tensor | None = None, epilogue: str = "bias", gamma=None, eps: float = 1e-6, out=None,
-                 stream=None) -> torch.Tensor:
+                 workspace=None, stream=None) -> torch.Tensor:
     """Block-scaled FP4 linear: bf16 [M, N] = acc + bias ("bias"), bf16 [M, N/2] = silu(gate) * up
     ("silu_gate", W rows [gate; up]), RMSNorm of acc + bias over 256-wide heads with gamma
     ("head_rmsnorm"), or the fp32 accumulators ("acc_f32").
@@ -224,8 +235,7 @@ def mxfp4_linear(Xq: torch.Tensor, Xs: torch.Tensor, Wq: torch.Tensor, Ws: torch
     M, N, K = Xq.shape[0], Wq.shape[0], Xq.shape[1] * 2
     if Wq.shape[1] * 2 != K or Xs.shape != (M, K // 32) or Ws.shape != (N, K // 32):
         raise ValueError("mxfp4_linear: inconsistent operand shapes")
-    epi = {"bias": QDT_EPI_BIAS, "silu_gate": QDT_EPI_SILU_GATE, "head_rmsnorm": QDT_EPI_HEAD_RMSNORM,
-           "acc_f32": QDT_EPI_ACC_F32}[epilogue]
+    epi = _MX_EPI[epilogue]
     params = None
     if epi == QDT_EPI_HEAD_RMSNORM:
         if gamma is None:
@@ -237,8 +247,12 @@ def mxfp4_linear(Xq: torch.Tensor, Xs: torch.Tensor, Wq: torch.Tensor, Ws: torch
         out = torch.empty((M, nout), dtype=torch.float32 if epi == QDT_EPI_ACC_F32 else torch.bfloat16,
                           device=Xq.device)
     out, ldy = _rows(out, "out")
+    need = mxfp4_linear_plan(M, N, K, epilogue)["workspace_bytes"]
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Xq.device)
     _check(qdt_mxfp4_linear(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(bias), M, N, K, epi,
                             None if params is None else C.cast(C.byref(params), C.c_void_p), _ptr(out), ldy,
+                            _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
                             _stream(stream)), "qdt_mxfp4_linear")
     return out
 

@@ -370,23 +370,43 @@ qdt_status qdt_bf16_linear(const uint16_t* X, const uint16_t* W, const uint16_t*
     return hip_status(launch_gemm_bf16(a, p, reinterpret_cast<hipStream_t>(stream)));
 }
 
-qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
-                            const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi,
-                            const void* epi_params, void* Y, int64_t ldy, void* stream) {
+// The planner's view of an FP4 problem: K/2 code bytes per row, 256 x 256 tiles (the only FP4
+// tile), the epilogue's tile constraints, K split chosen by the planner.
+static qdt_status mx_plan(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, Plan* p) {
     if (epi != QDT_EPI_BIAS && epi != QDT_EPI_SILU_GATE && epi != QDT_EPI_HEAD_RMSNORM && epi != QDT_EPI_ACC_F32)
         return QDT_EINVAL;
     if (M < 0 || M > INT32_MAX / 2 || N <= 0 || N > INT32_MAX / 2 || N % 16 != 0) return QDT_ESHAPE;
     if (epi == QDT_EPI_SILU_GATE && N % 32 != 0) return QDT_ESHAPE;
+    if (epi == QDT_EPI_HEAD_RMSNORM && N % 256 != 0) return QDT_ESHAPE;
+    if (K <= 0 || K % 256 != 0 || K > QDT_MAX_K) return QDT_ESHAPE;
+    const int pk = epi == QDT_EPI_SILU_GATE ? EPI_SILU : epi == QDT_EPI_HEAD_RMSNORM ? EPI_RMSNORM : EPI_BIAS;
+    return make_plan(M, N, K / 2, pk, 1, QDT_TILE_256, 0, p);
+}
+
+qdt_status qdt_mxfp4_linear_plan(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, qdt_linear_plan* plan) {
+    if (!plan) return QDT_EINVAL;
+    Plan p;
+    qdt_status r = mx_plan(M, N, K, epi, &p);
+    if (r == QDT_OK) export_plan(p, plan);
+    return r;
+}
+
+qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                            const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi,
+                            const void* epi_params, void* Y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    Plan p;
+    qdt_status r = mx_plan(M, N, K, epi, &p);
+    if (r != QDT_OK) return r;
     const qdt_rmsnorm_params* rp = reinterpret_cast<const qdt_rmsnorm_params*>(epi_params);
     if (epi == QDT_EPI_HEAD_RMSNORM) {
-        if (N % 256 != 0) return QDT_ESHAPE;
         if (!rp || !rp->gamma) return QDT_EINVAL;
         if (rp->head_dim != 256) return QDT_ESHAPE;
         if (!(rp->eps >= 0.0f) || rp->eps > 3.0e38f) return QDT_EINVAL;
         if (!aligned16(rp->gamma)) return QDT_EALIGN;
     }
     const int64_t nout = epi == QDT_EPI_SILU_GATE ? N / 2 : N;
-    if (K <= 0 || K % 256 != 0 || K > QDT_MAX_K || ldy < nout) return QDT_ESHAPE;
+    if (ldy < nout) return QDT_ESHAPE;
     if (M == 0) return QDT_OK;
     if (!Xq || !Xs || !Wq || !Ws || !Y) return QDT_EINVAL;
     if (!aligned16(Xq) || !aligned16(Wq) || !aligned16(bias) || !aligned16(Y) || ldy % 8 != 0 ||
@@ -394,31 +414,38 @@ qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t*
         return QDT_EALIGN;
     const int64_t es = epi == QDT_EPI_ACC_F32 ? 4 : 2;
     const int64_t ybytes = ((M - 1) * ldy + nout) * es;
-    if (overlap(Y, ybytes, Xq, M * K / 2) || overlap(Y, ybytes, Xs, M * K / 32) || overlap(Y, ybytes, Wq, N * K / 2) ||
-        overlap(Y, ybytes, Ws, N * K / 32) || overlap(Y, ybytes, bias, bias ? N * 2 : 0) ||
-        overlap(Y, ybytes, epi == QDT_EPI_HEAD_RMSNORM ? rp->gamma : nullptr, 512))
-        return QDT_EALIAS;
-    Plan p;
-    const int pk = epi == QDT_EPI_SILU_GATE ? EPI_SILU : epi == QDT_EPI_HEAD_RMSNORM ? EPI_RMSNORM : EPI_F32BIAS;
-    qdt_status r = make_plan(M, N, K / 2, pk, 1, QDT_TILE_256, 1, &p);
-    if (r != QDT_OK) return r;
+    const void* ins[6] = {Xq, Xs, Wq, Ws, bias, epi == QDT_EPI_HEAD_RMSNORM ? rp->gamma : nullptr};
+    const int64_t inb[6] = {M * K / 2, M * K / 32, N * K / 2, N * K / 32, bias ? N * 2 : 0, 512};
+    for (int i = 0; i < 6; ++i)
+        if (overlap(Y, ybytes, ins[i], inb[i])) return QDT_EALIAS;
+    if (p.ws_bytes > 0) {
+        if (!workspace || (int64_t)workspace_bytes < p.ws_bytes) return QDT_EWORKSPACE;
+        if (!aligned16(workspace)) return QDT_EALIGN;
+        if (overlap(Y, ybytes, workspace, p.ws_bytes)) return QDT_EALIAS;
+        for (int i = 0; i < 6; ++i)
+            if (overlap(workspace, p.ws_bytes, ins[i], inb[i])) return QDT_EALIAS;
+    }
     GemmArgs a;
     memset(&a, 0, sizeof(a));
     a.X = Xq;
     a.W = Wq;
     a.bias = bias;
+    a.gamma = epi == QDT_EPI_HEAD_RMSNORM ? rp->gamma : nullptr;
+    a.eps = epi == QDT_EPI_HEAD_RMSNORM ? rp->eps : 0.0f;
     a.Y = Y;
     a.ldy = ldy;
+    a.ws = reinterpret_cast<int32_t*>(workspace);
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
-    a.gamma = epi == QDT_EPI_HEAD_RMSNORM ? rp->gamma : nullptr;
-    a.eps = epi == QDT_EPI_HEAD_RMSNORM ? rp->eps : 0.0f;
     a.epi = epi == QDT_EPI_ACC_F32         ? EPI_ACC
             : epi == QDT_EPI_SILU_GATE     ? EPI_F32SILU
             : epi == QDT_EPI_HEAD_RMSNORM  ? EPI_F32RMSNORM
                                            : EPI_F32BIAS;
-    return hip_status(launch_gemm_mx(a, Xs, Ws, p, reinterpret_cast<hipStream_t>(stream)));
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if ((r = hip_status(launch_gemm_mx(a, Xs, Ws, p, st))) != QDT_OK) return r;
+    if (p.split_k > 1) return hip_status(launch_splitk_f32_epilogue(a, p.split_k, a.epi, st));
+    return QDT_OK;
 }
 
 }  // extern "C"

@@ -174,7 +174,8 @@ gemm_kernel(KArgs p) {
     constexpr int NSC = MX ? 4 : 0;
     constexpr int NDMA = NI + NSC;
     static_assert(!MX || (BM == 256 && BN == 256 && !BF16 &&
-                          (EPI == EPI_F32BIAS || EPI == EPI_F32SILU || EPI == EPI_F32RMSNORM || EPI == EPI_ACC)),
+                          (EPI == EPI_F32BIAS || EPI == EPI_F32SILU || EPI == EPI_F32RMSNORM || EPI == EPI_ACC ||
+                           EPI == EPI_PARTIAL)),
                   "FP4: 256 x 256 tiles, fp32-accumulator epilogues");
     constexpr int NACC_A = 64;             // accumulator tuples held in AGPRs (the rest in VGPRs)
     constexpr bool SILU = EPI == EPI_SILU || EPI == EPI_F32SILU;
@@ -930,12 +931,110 @@ hipError_t launch_gemm_mx(const GemmArgs& a, const uint8_t* xsc, const uint8_t* 
     k.Kb = a.K / 2;  // two FP4 codes per byte
     k.xsc = xsc;
     k.wsc = wsc;
-    if (pl.tile != QDT_TILE_256 || pl.split_k != 1) return hipErrorInvalidValue;
+    if (pl.tile != QDT_TILE_256) return hipErrorInvalidValue;
+    if (pl.split_k > 1) return go<8, 8, false, EPI_PARTIAL, true>(k, pl.grid, st);
     if (a.epi == EPI_F32BIAS) return go<8, 8, false, EPI_F32BIAS, true>(k, pl.grid, st);
     if (a.epi == EPI_F32SILU) return go<8, 8, false, EPI_F32SILU, true>(k, pl.grid, st);
     if (a.epi == EPI_F32RMSNORM) return go<8, 8, false, EPI_F32RMSNORM, true>(k, pl.grid, st);
     if (a.epi == EPI_ACC) return go<8, 8, false, EPI_ACC, true>(k, pl.grid, st);
     return hipErrorInvalidValue;
+}
+
+// Block-scaled FP4 split-K: sums the S fp32 partial slices in slice order and applies the
+// fp32-accumulator epilogues to y = sum + bias (the same functions as the fused kernel).
+// F32BIAS / F32SILU / ACC: one thread per 4 output columns; F32RMSNORM: one wave per (row, head).
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_f32_epi_kernel(KArgs p) {
+    const int64_t MN = (int64_t)p.M * p.N;
+    const float* ws = reinterpret_cast<const float*>(p.ws);
+    auto sum4 = [&](int64_t off) __attribute__((always_inline)) {
+        v4f a = *reinterpret_cast<const v4f*>(ws + off);
+        for (int s = 1; s < p.split_k; ++s) a += *reinterpret_cast<const v4f*>(ws + s * MN + off);
+        return a;
+    };
+    auto bias4 = [&](int n, float (&b)[4]) __attribute__((always_inline)) {
+        b[0] = b[1] = b[2] = b[3] = 0.0f;
+        if (p.bias) {
+            const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
+            b[0] = bf16_to_f32(bb.x & 0xFFFFu); b[1] = bf16_to_f32(bb.x >> 16);
+            b[2] = bf16_to_f32(bb.y & 0xFFFFu); b[3] = bf16_to_f32(bb.y >> 16);
+        }
+    };
+    uint16_t* Y = reinterpret_cast<uint16_t*>(p.Y);
+    if constexpr (EPI == EPI_F32RMSNORM) {
+        const int heads = p.N / p.head_dim;
+        const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+        if (item >= (int64_t)p.M * heads) return;
+        const int lane = threadIdx.x & 63;
+        const int m = (int)(item / heads), h = (int)(item % heads);
+        const int d = lane * 4, n = h * p.head_dim + d;
+        const v4f a = sum4((int64_t)m * p.N + n);
+        float b[4], y[4], ss = 0.0f;
+        bias4(n, b);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            y[r] = a[r] + b[r];
+            ss += y[r] * y[r];
+        }
+        ss = wave_sum(ss);
+        const float rinv = 1.0f / sqrtf(ss / (float)p.head_dim + p.eps);
+        const uint2 gg = *reinterpret_cast<const uint2*>(p.gamma + d);
+        const float g[4] = {bf16_to_f32(gg.x & 0xFFFFu), bf16_to_f32(gg.x >> 16), bf16_to_f32(gg.y & 0xFFFFu),
+                            bf16_to_f32(gg.y >> 16)};
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = (y[r] * rinv) * g[r];
+        *reinterpret_cast<uint2*>(Y + (int64_t)m * p.ldy + n) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+    } else {
+        const int nout = EPI == EPI_F32SILU ? p.F : p.N;
+        const int q = nout / 4;
+        const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+        if (idx >= (int64_t)p.M * q) return;
+        const int m = (int)(idx / q);
+        const int n = (int)(idx % q) * 4;
+        const v4f a = sum4((int64_t)m * p.N + n);
+        if constexpr (EPI == EPI_ACC) {
+            *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.Y) + (int64_t)m * p.ldy + n) = a;
+            return;
+        }
+        float b[4], y[4];
+        bias4(n, b);
+        if constexpr (EPI == EPI_F32SILU) {
+            const v4f u = sum4((int64_t)m * p.N + p.F + n);
+            float bu[4], g[4], uu[4];
+            bias4(p.F + n, bu);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                g[r] = a[r] + b[r];
+                uu[r] = u[r] + bu[r];
+            }
+            silu_gate4(g, uu, y);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = a[r] + b[r];
+        }
+        *reinterpret_cast<uint2*>(Y + (int64_t)m * p.ldy + n) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+    }
+}
+
+hipError_t launch_splitk_f32_epilogue(const GemmArgs& a, int split_k, int epi, hipStream_t st) {
+    Plan dummy{};
+    dummy.split_k = split_k;
+    KArgs k = make_kargs(a, dummy, 1);
+    if (epi == EPI_F32RMSNORM) {
+        const int64_t items = (int64_t)a.M * (a.N / 256);
+        hipLaunchKernelGGL(splitk_f32_epi_kernel<EPI_F32RMSNORM>, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, k);
+        return hipGetLastError();
+    }
+    const int nout = epi == EPI_F32SILU ? a.N / 2 : a.N;
+    const unsigned blocks = (unsigned)(((int64_t)a.M * (nout / 4) + 255) / 256);
+    switch (epi) {
+        case EPI_F32BIAS: hipLaunchKernelGGL(splitk_f32_epi_kernel<EPI_F32BIAS>, dim3(blocks), dim3(256), 0, st, k); break;
+        case EPI_F32SILU: hipLaunchKernelGGL(splitk_f32_epi_kernel<EPI_F32SILU>, dim3(blocks), dim3(256), 0, st, k); break;
+        case EPI_ACC: hipLaunchKernelGGL(splitk_f32_epi_kernel<EPI_ACC>, dim3(blocks), dim3(256), 0, st, k); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_splitk_epilogue(const GemmArgs& a, int split_k, int epi, hipStream_t st) {

@@ -60,11 +60,14 @@ struct GemmArgs {
 
 hipError_t launch_gemm_i8(const GemmArgs& a, const Plan& p, hipStream_t st);
 hipError_t launch_gemm_bf16(const GemmArgs& a, const Plan& p, hipStream_t st);
-// Block-scaled FP4 GEMM (256 x 256 tiles, no K split): a.K is the element count; xsc / wsc the
+// Block-scaled FP4 GEMM (256 x 256 tiles; a K split writes fp32 partials to a.ws): a.K is the element count; xsc / wsc the
 // biased block exponents [M][K/32] / [N][K/32]; a.epi EPI_F32BIAS, EPI_F32SILU, EPI_F32RMSNORM or
 // EPI_ACC (fp32 accumulators).
 hipError_t launch_gemm_mx(const GemmArgs& a, const uint8_t* xsc, const uint8_t* wsc, const Plan& p, hipStream_t st);
 // Sum of the S int32 partial slices followed by epilogue `epi` (BIAS, SILU, RMSNORM, ACC).
 hipError_t launch_splitk_epilogue(const GemmArgs& a, int split_k, int epi, hipStream_t st);
+// Sum of the S fp32 partial slices of the FP4 GEMM, then epilogue `epi` (F32BIAS, F32SILU,
+// F32RMSNORM, ACC).
+hipError_t launch_splitk_f32_epilogue(const GemmArgs& a, int split_k, int epi, hipStream_t st);
 
 }  // namespace qdt

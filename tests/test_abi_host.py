@@ -91,7 +91,7 @@ def test_mxfp4_validation():
 
     def lin(M=64, N=128, K=256, epi=0, Y=0x900000, ldy=None, xs=0x200000, ws=0x400000):
         return f(A(0x100000), A(xs), A(0x300000), A(ws), None, M, N, K, epi, None, A(Y), N if ldy is None else ldy,
-                 None)
+                 None, 0, None)
     assert lin(K=128) == qdt.QDT_ESHAPE                 # whole 256-element stages
     assert lin(N=120) == qdt.QDT_ESHAPE
     assert lin(epi=2, N=512) == qdt.QDT_EINVAL          # head RMSNorm without its parameters
@@ -103,6 +103,13 @@ def test_mxfp4_validation():
     assert lin(xs=0x200002) == qdt.QDT_EALIGN           # exponent rows read as dwords
     assert lin(Y=0x300000 + 64) == qdt.QDT_EALIAS        # Y over Wq
     assert lin(M=0) == qdt.QDT_OK
+    # deep K with few output tiles splits K and needs a workspace for the fp32 partials
+    p = qdt.mxfp4_linear_plan(512, 4608, 53248)
+    assert p["split_k"] > 1 and p["tile_m"] == 256 and p["workspace_bytes"] == p["split_k"] * 512 * 4608 * 4
+    big = 0x10000000000
+    assert f(A(big), A(2 * big), A(3 * big), A(4 * big), None, 512, 4608, 53248, 0, None, A(5 * big), 4608,
+             None, 0, None) == qdt.QDT_EWORKSPACE
+    assert qdt.mxfp4_linear_plan(4608, 4608, 4608)["split_k"] == 1
 
 
 def test_smooth_prepare_validation():

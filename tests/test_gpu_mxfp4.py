@@ -219,3 +219,48 @@ def test_mxfp4_head_rmsnorm_within_bound():
         err = np.abs(got[:, sl] - ref)
         assert np.all(err <= bound), f"head {h}: worst error / bound {np.max(err / bound):.3f}"
     assert np.mean(Y[rows] == Y_ref) > 0.9
+
+
+def small_operands(rows, K, seed):
+    """Codes of magnitude <= 1 with block exponents in {-1, 0}: every product is a multiple of 2^-4
+    at most 1, so sums over K <= 53248 (and any split of them) stay exact in fp32."""
+    rng = np.random.default_rng(seed)
+    codes = rng.choice(np.array([0, 1, 2, 9, 10]), (rows, K))
+    Q = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    S = rng.integers(126, 128, (rows, K // 32)).astype(np.uint8)
+    return Q, S
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 512, 16384), (64, 256, 53248)])
+def test_mxfp4_split_k_exact(M, N, K):
+    """Deep K: the planner splits K, the slices write fp32 partials and a second kernel sums them.
+    With exact sums every epilogue must match the oracle (bias bit for bit, SiLU / RMSNorm 1 ulp)."""
+    plan = qdt.mxfp4_linear_plan(M, N, K)
+    assert plan["split_k"] > 1
+    announce(f"mxfp4_linear split-K {plan['split_k']} M={M} N={N} K={K}")
+    Xq, Xs = small_operands(M, K, 110 + M)
+    Wq, Ws = small_operands(N, K, 120 + N)
+    rng = np.random.default_rng(K)
+    bias = W.f32_to_bf16_bits(rng.standard_normal(N).astype(np.float32))
+    gamma = W.f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(256)).astype(np.float32))
+    dX, dXs, dW, dWs, db = (to_dev(a) for a in (Xq, Xs, Wq, Ws, bias))
+    Y_ref, acc = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, want_acc=True)
+    Yacc = to_host(qdt.mxfp4_linear(dX, dXs, dW, dWs, None, "acc_f32"))
+    assert np.array_equal(Yacc.astype(np.float64), acc), f"{np.sum(Yacc != acc)} accumulators differ"
+    assert bits_equal(to_host(qdt.mxfp4_linear(dX, dXs, dW, dWs, db, "bias")), Y_ref)
+    Ys = to_host(qdt.mxfp4_linear(dX, dXs, dW, dWs, db, "silu_gate"))
+    assert ulp_bf16(Ys, oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, epi="silu_gate")).max() <= 1
+    Yr = to_host(qdt.mxfp4_linear(dX, dXs, dW, dWs, db, "head_rmsnorm", gamma=to_dev(gamma), eps=1e-6))
+    Yr_ref = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, epi="head_rmsnorm", gamma=gamma, eps=1e-6)
+    assert ulp_bf16(Yr, Yr_ref).max() <= 1
+
+
+def test_mxfp4_text_projection_shape():
+    """The deep-K text projection (512 x 4608 x 53248) in FP4 with its K split, sampled rows."""
+    d = W.make_workload("text_cond_proj_512x4608x53248")
+    plan = qdt.mxfp4_linear_plan(512, 4608, 53248)
+    announce(f"mxfp4 text projection, split-K {plan['split_k']}")
+    Xq, Xs = check_quant(d["X"])
+    Wq, Ws = qdt.mxfp4_quantize(to_dev(d["W"]))
+    Y = to_host(qdt.mxfp4_linear(Xq, Xs, Wq, Ws, to_dev(d["bias"]), "bias"))
+    within_bound(Y, to_host(Xq), to_host(Xs), to_host(Wq), to_host(Ws), d["bias"], sample_rows(512, 4, 11))

@@ -299,7 +299,7 @@ EXTRA_WORKLOADS = ("dit_ffn_gate_up_4608x24576x4608", "text_cond_proj_512x4608x5
                    "text_cond_proj_padded_4608x4608x53248", "qk_proj_headnorm_16896x4608x4608",
                    "qk_proj_headnorm_6037x4608x4608", "adaln_quantize_4608x4608", "adaln_quantize_16896x4608",
                    "mxfp4_attn_proj_4608x4608x4608", "mxfp4_ffn_gate_up_4608x24576x4608",
-                   "mxfp4_qk_proj_headnorm_16896x4608x4608")
+                   "mxfp4_qk_proj_headnorm_16896x4608x4608", "mxfp4_text_cond_proj_512x4608x53248")
 
 
 def extra_workloads(args, only=None):
@@ -413,7 +413,8 @@ def extra_workloads(args, only=None):
     for name, src, epi in (("mxfp4_attn_proj_4608x4608x4608", "dit_attn_proj_4608x4608x4608", "bias"),
                            ("mxfp4_ffn_gate_up_4608x24576x4608", "dit_ffn_gate_up_4608x24576x4608", "silu_gate"),
                            ("mxfp4_qk_proj_headnorm_16896x4608x4608", "qk_proj_headnorm_16896x4608x4608",
-                            "head_rmsnorm")):
+                            "head_rmsnorm"),
+                           ("mxfp4_text_cond_proj_512x4608x53248", "text_cond_proj_512x4608x53248", "bias")):
         if want(name):
             res[name] = mxfp4_workload(src, epi, counts)
     torch.cuda.empty_cache()
@@ -436,6 +437,8 @@ def mxfp4_workload(src, epi, counts):
     Xs = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
     Y = torch.empty((M, N // 2 if epi == "silu_gate" else N), dtype=torch.bfloat16, device="cuda")
     g = to_dev(d["gamma"]) if epi == "head_rmsnorm" else None
+    plan = qdt.mxfp4_linear_plan(M, N, K, epi)
+    ws = torch.empty(max(plan["workspace_bytes"], 16), dtype=torch.uint8, device="cuda")
 
     def step(_, ev):
         if ev is not None:
@@ -443,7 +446,7 @@ def mxfp4_workload(src, epi, counts):
         qdt.mxfp4_quantize(X, None, Xq, Xs)
         if ev is not None:
             ev[1].record()
-        qdt.mxfp4_linear(Xq, Xs, Wq, Ws, b, epi, gamma=g, eps=d.get("eps", 1e-6), out=Y)
+        qdt.mxfp4_linear(Xq, Xs, Wq, Ws, b, epi, gamma=g, eps=d.get("eps", 1e-6), out=Y, workspace=ws)
         if ev is not None:
             ev[2].record()
     steps, warm = counts(step)
@@ -452,7 +455,7 @@ def mxfp4_workload(src, epi, counts):
     g = stats(tg)["mean"]
     qb = 2 * M * K + M * K // 2 + M * K // 32
     return {"M": M, "N": N, "K": K, "format": "MXFP4 (32-element blocks, E8M0 scales)", "epilogue": epi,
-            "steps": steps, "warmup": warm, "ms_per_step": round(ms, 4),
+            "split_k": plan["split_k"], "steps": steps, "warmup": warm, "ms_per_step": round(ms, 4),
             "eff_tops": round(ops / (ms * 1e-3) / 1e12, 1), "gemm_ms": round(g, 4),
             "gemm_tops": round(ops / (g * 1e-3) / 1e12, 1),
             "gemm_frac_fp4_peak": round(ops / (g * 1e-3) / 1e12 / PEAK_FP4_TOPS, 4),

@@ -57,6 +57,10 @@ def lib():
             "oracle_fp4_value": ([I], C.c_double),
             "oracle_mxfp4_quantize_rows": ([P, P, I64, I64, I64, P, P], None),
             "oracle_mxfp4_gemm_rows": ([P, P, P, P, P, P, I64, I64, I64, I, P, F, P, P], None),
+            "oracle_f32_to_f16": ([F], C.c_uint16),
+            "oracle_f16_to_f64": ([C.c_uint16], C.c_double),
+            "oracle_wo_quantize": ([P, I64, I64, I64, I, P, P], None),
+            "oracle_wo_dequantize": ([P, P, I64, I64, I, P], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -255,3 +259,48 @@ def mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias=None, rows=None, want_acc=False, epi="b
     lib().oracle_mxfp4_gemm_rows(_p(Xq), _p(Xs), _p(Wq), _p(Ws), _p(_c(bias, np.uint16)), _p(r), nr, N, K, e,
                                  _p(_c(gamma, np.uint16)), eps, _p(acc), _p(Y))
     return (Y, acc) if want_acc else Y
+
+
+def f32_to_f16(x) -> np.ndarray:
+    """IEEE half bits of fp32 values: round half to even, saturating at 65504."""
+    a = np.asarray(x, np.float32).ravel()
+    L = lib()
+    return np.array([L.oracle_f32_to_f16(float(v)) for v in a], np.uint16).reshape(np.shape(x))
+
+
+def f16_to_f64(h) -> np.ndarray:
+    a = np.asarray(h, np.uint16).ravel()
+    L = lib()
+    return np.array([L.oracle_f16_to_f64(int(v)) for v in a], np.float64).reshape(np.shape(h))
+
+
+def wo_quantize(W, bits: int = 4):
+    """Weight-only blocks of W [N, K] bf16 (K % 32 == 0): codes (int8 [N, K] for 8 bits, nibbles
+    uint8 [N, K/2] for 4 bits) and half-precision scale bits uint16 [N, K/32]."""
+    assert bits in (4, 8)
+    W = np.asarray(W, np.uint16)
+    N, K = W.shape
+    ldw = W.strides[0] // 2
+    Q = np.zeros((N, K if bits == 8 else K // 2), np.int8 if bits == 8 else np.uint8)
+    D = np.empty((N, K // 32), np.uint16)
+    if W.strides[1] != 2:
+        W = np.ascontiguousarray(W)
+        ldw = K
+    lib().oracle_wo_quantize(_p(W), N, K, ldw, bits, _p(Q), _p(D))
+    return Q, D
+
+
+def wo_dequantize(Q, D, bits: int) -> np.ndarray:
+    """bf16 [N, K] = bf16(q * d) of weight-only blocks."""
+    Q = _c(Q, np.int8 if bits == 8 else np.uint8)
+    D = _c(D, np.uint16)
+    N = Q.shape[0]
+    K = D.shape[1] * 32
+    Wd = np.empty((N, K), np.uint16)
+    lib().oracle_wo_dequantize(_p(Q), _p(D), N, K, bits, _p(Wd))
+    return Wd
+
+
+def wo_linear_rows(X, Q, D, bits: int, bias=None, rows=None, want_f32=False):
+    """The weight-only linear: the bf16 GEMM of X with the dequantized weights (plus bias)."""
+    return bf16_gemm_rows(X, wo_dequantize(Q, D, bits), bias, rows, want_f32)

@@ -50,6 +50,16 @@
  *     0, 0.5, 1, 1.5, 2, 3, 4, 6 (ties to the even 1-bit mantissa), magnitudes above 6 saturate
  *     to 6, and the 4-bit code is sign << 3 | index with zero always +0.  Two codes per byte,
  *     the even element in the low nibble.  The GEMM sums exact products of the decoded values.
+ *   - Weight-only block formats ([PTQ] GGUF paragraph: an 8-bit round-to-nearest format at 8.5
+ *     bits per weight, and a 4-bit one at 4.5 bits per weight; [ZC] "The NF4 Exactness
+ *     Problem": the text projection multiplies bf16 activations by dequantized weights).  Blocks
+ *     of 32 consecutive weights of a row share a 16-bit IEEE half-precision scale
+ *     d = half(amax / qmax) (qmax = 127 for 8 bits, 7 for 4 bits; round half to even, half
+ *     subnormals kept, magnitudes from 65520 up saturate to 65504), and each weight becomes
+ *     q = clamp(rint(w / d), -qmax, qmax) with the fp32 division against the stored scale
+ *     (q = 0 when d = 0).  8-bit codes are int8; 4-bit codes are stored as q + 8 in a nibble,
+ *     the even element in the low nibble.  The dequantized weight is bf16(q * d) (the product is
+ *     exact in fp32), and the GEMM is the bf16 GEMM below on those weights.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math (no intrinsics, no SIMD pragmas).
  * Floating point: every fp32 operation is IEEE round-to-nearest-even, as written.
@@ -547,4 +557,94 @@ void oracle_mxfp4_gemm_rows(const uint8_t* Xq, const uint8_t* Xs, const uint8_t*
                             const uint16_t* gamma, float eps, double* acc, uint16_t* Y) {
     mxg_ctx c = {Xq, Xs, Wq, Ws, bias, rows, N, K, epi, gamma, eps, acc, Y};
     parallel_rows(nrows, mxg_rows, &c);
+}
+
+/* ---------------------------------------------------------------- O11: weight-only blocks */
+/* fp32 -> IEEE binary16 bits, round half to even, subnormal halves kept; magnitudes that would
+ * round to infinity (from 65520 up) saturate to the largest finite half, 65504.  Finite input. */
+uint16_t oracle_f32_to_f16(float f) {
+    uint16_t sign = signbit(f) ? 0x8000 : 0;
+    double a = fabs((double)f);
+    if (a >= 65520.0) return sign | 0x7BFF;
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: units of 2^-24 (1024 units = 2^-14 is the smallest normal, whose
+         * encoding 0x0400 continues the same count) */
+        double units = nearbyint(a * ldexp(1.0, 24));
+        return sign | (uint16_t)units;
+    }
+    int e2;
+    frexp(a, &e2);               /* a = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;              /* a in [2^e, 2^(e+1)) */
+    double m = nearbyint(ldexp(a, 10 - e));  /* 11-bit significand in [1024, 2048] */
+    if (m == 2048.0) { m = 1024.0; e += 1; }
+    return sign | (uint16_t)(((e + 15) << 10) | ((int)m - 1024));
+}
+
+/* IEEE binary16 bits -> value (exact in fp32 and fp64). */
+double oracle_f16_to_f64(uint16_t h) {
+    int e = (h >> 10) & 31, m = h & 1023;
+    double v = e == 0 ? ldexp((double)m, -24) : ldexp((double)(1024 + m), e - 25);
+    return (h & 0x8000) ? -v : v;
+}
+
+typedef struct {
+    const uint16_t* W; int64_t K, ldw; int bits; uint8_t* Q; uint16_t* D;
+} wo_ctx;
+
+static void wo_rows(void* p, int64_t r0, int64_t r1) {
+    wo_ctx* c = (wo_ctx*)p;
+    const int qmax = c->bits == 8 ? 127 : 7;
+    for (int64_t n = r0; n < r1; ++n) {
+        const uint16_t* w = c->W + n * c->ldw;
+        for (int64_t b = 0; b < c->K / 32; ++b) {
+            float amax = 0.0f;
+            for (int j = 0; j < 32; ++j) {
+                float v = fabsf(oracle_bf16_to_f32(w[b * 32 + j]));
+                if (v > amax) amax = v;
+            }
+            uint16_t dh = oracle_f32_to_f16(amax / (float)qmax);
+            float d = (float)oracle_f16_to_f64(dh);
+            c->D[n * (c->K / 32) + b] = dh;
+            for (int j = 0; j < 32; ++j) {
+                int64_t k = b * 32 + j;
+                int q = 0;
+                if (d > 0.0f) {
+                    float t = rintf(oracle_bf16_to_f32(w[k]) / d);
+                    if (t > (float)qmax) t = (float)qmax;
+                    if (t < (float)-qmax) t = (float)-qmax;
+                    q = (int)t;
+                }
+                if (c->bits == 8) {
+                    c->Q[n * c->K + k] = (uint8_t)(int8_t)q;
+                } else {
+                    uint8_t* byte = &c->Q[n * (c->K / 2) + k / 2];
+                    *byte = (k % 2 == 0) ? (uint8_t)((*byte & 0xF0) | (q + 8)) : (uint8_t)((*byte & 0x0F) | ((q + 8) << 4));
+                }
+            }
+        }
+    }
+}
+
+/* Weight-only quantization of W [N, ldw] (first K columns, K % 32 == 0): codes Q ([N, K] int8
+ * for bits = 8, [N, K/2] nibbles for bits = 4) and half scales D [N, K/32]. */
+void oracle_wo_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, int bits, uint8_t* Q, uint16_t* D) {
+    wo_ctx c = {W, K, ldw, bits, Q, D};
+    parallel_rows(N, wo_rows, &c);
+}
+
+/* Signed code of element k of a quantized row. */
+static int wo_code(const uint8_t* q, int64_t k, int bits) {
+    if (bits == 8) return (int)(int8_t)q[k];
+    int nib = (k % 2 == 0) ? (q[k / 2] & 15) : (q[k / 2] >> 4);
+    return nib - 8;
+}
+
+/* Dequantized weights Wd [N, K] bf16: Wd[n][k] = bf16(q * d) (the product is exact). */
+void oracle_wo_dequantize(const uint8_t* Q, const uint16_t* D, int64_t N, int64_t K, int bits, uint16_t* Wd) {
+    const int64_t qrow = bits == 8 ? K : K / 2;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            double v = (double)wo_code(Q + n * qrow, k, bits) * oracle_f16_to_f64(D[n * (K / 32) + k / 32]);
+            Wd[n * K + k] = oracle_f32_to_bf16((float)v);
+        }
 }

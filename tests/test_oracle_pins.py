@@ -599,3 +599,163 @@ def test_generator_is_deterministic_and_prefix_stable():
     # outlier channels: 4 channels x20 in the tiny case
     fac = W.outlier_factors(256, 1000, "four20")
     assert sorted(np.unique(fac).tolist()) == [1.0, 20.0] and (fac == 20).sum() == 4
+
+
+# ---------------------------------------------------------------- weight-only block formats
+def test_f16_conversion_matches_numpy_and_saturates():
+    """Round half to even with subnormals, checked against numpy's half conversion; from 65520
+    up (where IEEE rounds to infinity) the reading saturates to 65504."""
+    rng = np.random.default_rng(40)
+    e = rng.integers(-30, 16, 4000)
+    x = (rng.uniform(1, 2, 4000) * np.ldexp(1.0, e) * rng.choice([-1, 1], 4000)).astype(np.float32)
+    # exact midpoints between neighbouring halves, normal and subnormal
+    h = rng.integers(1, 0x7BFE, 500).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    mid = ((lo + hi) / 2).astype(np.float32)
+    assert np.array_equal(mid.astype(np.float64), (lo + hi) / 2)
+    x = np.concatenate([x, mid, np.float32([0.0, -0.0, 65504, 65519.99, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26])])
+    got = oracle.f32_to_f16(x)
+    assert np.array_equal(got, x.astype(np.float16).view(np.uint16))
+    sat = oracle.f32_to_f16(np.float32([65520, -70000, 3e38]))
+    assert list(sat) == [0x7BFF, 0xFBFF, 0x7BFF]
+
+
+def test_f16_decode_every_finite_pattern():
+    h = np.arange(0, 0x10000, dtype=np.uint16)
+    h = h[(h & 0x7C00) != 0x7C00][::7]
+    assert np.array_equal(oracle.f16_to_f64(h), h.view(np.float16).astype(np.float64))
+
+
+def _wo_codes(Q, bits):
+    """Signed codes [N, K] of weight-only blocks (test-side decoding of the documented layout)."""
+    if bits == 8:
+        return Q.astype(np.int64)
+    q = np.empty((Q.shape[0], Q.shape[1] * 2), np.int64)
+    q[:, 0::2] = (Q & 15).astype(np.int64) - 8
+    q[:, 1::2] = (Q >> 4).astype(np.int64) - 8
+    return q
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_wo_scale_rule_and_special_blocks(bits):
+    qmax = 127 if bits == 8 else 7
+    K = 32 * 6
+    w = np.zeros((1, K), np.float32)
+    rng = np.random.default_rng(41)
+    # block 0: on the grid of d = 2^-7, with +-qmax present: exact codes
+    g = rng.integers(-qmax, qmax + 1, 32)
+    g[5] = -qmax
+    w[0, :32] = g * 2.0 ** -7
+    # block 1: all zero; block 2: amax / qmax underflows the half format (scale 0, codes 0)
+    w[0, 64:96] = 1e-9 * rng.standard_normal(32)
+    # block 3: amax / qmax is a half subnormal
+    w[0, 96:128] = 3e-6 * rng.standard_normal(32)
+    # block 4: amax / qmax above the half range: scale saturates, codes clamp
+    w[0, 128:160] = 1e7 * rng.standard_normal(32)
+    # block 5: one nonzero element
+    w[0, 170] = -0.3
+    Wb = bf(w)
+    Q, D = oracle.wo_quantize(Wb, bits)
+    q, d = _wo_codes(Q, bits), oracle.f16_to_f64(D)
+    wv = f32(Wb).astype(np.float64)
+    assert d[0, 0] == 2.0 ** -7 and np.array_equal(q[0, :32], g)
+    assert d[0, 1] == 0 and np.all(q[0, 32:64] == 0)
+    assert d[0, 2] == 0 and np.all(q[0, 64:96] == 0)
+    assert 0 < d[0, 3] < 2.0 ** -14
+    assert D[0, 4] == 0x7BFF and np.abs(q[0, 128:160]).max() == qmax
+    # past the representable range every code saturates to +-qmax
+    big = np.abs(wv[0, 128:160]) >= (qmax + 0.5) * 65504
+    assert big.sum() >= 8 and np.array_equal(q[0, 128:160][big], qmax * np.sign(wv[0, 128:160][big]).astype(np.int64))
+    assert q[0, 170] == -qmax and np.count_nonzero(q[0, 160:192]) == 1
+    amax = np.abs(wv.reshape(6, 32)).max(axis=1)
+    want = oracle.f32_to_f16((amax.astype(np.float32) / np.float32(qmax)).astype(np.float32))
+    assert np.array_equal(D[0], want)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_wo_codes_are_nearest_by_brute_force(bits):
+    """Each code is the nearest grid point q * d (ties to even q) among all codes, away from
+    exact-tie neighbourhoods where the fp32 division decides."""
+    qmax = 127 if bits == 8 else 7
+    rng = np.random.default_rng(42 + bits)
+    Wb = bf(rng.standard_normal((16, 256)) * np.ldexp(1.0, rng.integers(-12, 2, (16, 1))))
+    Q, D = oracle.wo_quantize(Wb, bits)
+    q, d = _wo_codes(Q, bits), np.repeat(oracle.f16_to_f64(D), 32, axis=1)
+    w = f32(Wb).astype(np.float64)
+    grid = np.arange(-qmax, qmax + 1)
+    dist = np.abs(w[..., None] - grid * d[..., None])
+    best = dist.min(axis=-1, keepdims=True)
+    cand = np.where(dist <= best * (1 + 1e-12), grid, 10 ** 6)
+    even = np.where(cand % 2 == 0, cand, 10 ** 6).min(axis=-1)
+    nearest = np.where((dist <= best * (1 + 1e-12)).sum(-1) > 1, even, grid[dist.argmin(-1)])
+    t = w / d
+    safe = np.abs(np.abs(t - np.floor(t)) - 0.5) > 1e-5
+    assert np.array_equal(q[safe], nearest[safe])
+    assert safe.mean() > 0.99
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_wo_exact_ties_round_to_even(bits):
+    """Weights exactly halfway between grid points (d = 2^-6) take the even code."""
+    qmax = 127 if bits == 8 else 7
+    t = np.array([0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5, -5.5] * 4)
+    t[0] = qmax                                   # sets d = 2^-6
+    Q, D = oracle.wo_quantize(bf(t * 2.0 ** -6)[None, :], bits)
+    assert oracle.f16_to_f64(D)[0, 0] == 2.0 ** -6
+    want = np.array([0, 2, 2, 0, -2, -2, 4, -6] * 4)
+    want[0] = qmax
+    assert np.array_equal(_wo_codes(Q, bits)[0], want)
+
+
+def test_wo_nibble_order_and_int8_layout():
+    K = 64
+    codes = (np.arange(K) % 15) - 7          # -7 .. 7
+    w = bf(codes * 2.0 ** -4)                # block max 7 * 2^-4: d = 2^-4 for 4 bits
+    Q4, D4 = oracle.wo_quantize(w[None, :], 4)
+    assert list(D4[0]) == [0x2C00, 0x2C00]   # half 2^-4
+    assert Q4[0, 0] == ((codes[0] + 8) | ((codes[1] + 8) << 4)) and Q4[0, 20] == ((codes[40] + 8) | ((codes[41] + 8) << 4))
+    w8 = bf(((np.arange(K) * 37) % 255 - 127) * 2.0 ** -9)
+    Q8, D8 = oracle.wo_quantize(w8[None, :], 8)
+    assert Q8.dtype == np.int8 and np.array_equal(Q8[0].astype(np.int64), (np.arange(K) * 37) % 255 - 127)
+    assert list(oracle.wo_dequantize(Q8, D8, 8)[0]) == list(w8)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_wo_error_bound_and_dequant_rounding(bits):
+    qmax = 127 if bits == 8 else 7
+    rng = np.random.default_rng(44 + bits)
+    Wb = bf(0.02 * rng.standard_normal((32, 512)))
+    Q, D = oracle.wo_quantize(Wb, bits)
+    w = f32(Wb).astype(np.float64)
+    d = np.repeat(oracle.f16_to_f64(D), 32, axis=1)
+    q = _wo_codes(Q, bits)
+    amax = np.repeat(np.abs(w).reshape(32, 16, 32).max(axis=2), 32, axis=1)
+    # half a grid step, or the clamp excess when the rounded scale fell below amax / qmax
+    assert np.all(np.abs(w - q * d) <= np.maximum(d / 2, amax - qmax * d) * (1 + 1e-12))
+    Wd = oracle.wo_dequantize(Q, D, bits)
+    exact = q * d
+    assert np.array_equal(Wd, bf(exact.astype(np.float32)))            # one rounding of the exact product
+    assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_wo_linear_exact_against_integer_matmul(bits):
+    """On power-of-two scales the GEMM is an integer matmul times 2^-k: pins the operand
+    layout (rows of W are output columns) and the bias."""
+    qmax = 127 if bits == 8 else 7
+    rng = np.random.default_rng(46 + bits)
+    M, N, K = 5, 7, 128
+    qi = rng.integers(-qmax, qmax + 1, (N, K))
+    qi[:, ::32] = qmax                        # every block holds +qmax: d = 2^-6 exactly
+    Q, D = oracle.wo_quantize(bf(qi * 2.0 ** -6), bits)
+    assert np.array_equal(_wo_codes(Q, bits), qi)
+    xi = rng.integers(-3, 4, (M, K))
+    X = bf(xi * 0.5)
+    bias = bf(rng.integers(-8, 9, N) * 0.25)
+    Z, Zf = oracle.wo_linear_rows(X, Q, D, bits, bias, want_f32=True)
+    want = (xi @ qi.T) * 2.0 ** -7 + f32(bias).astype(np.float64)
+    assert np.array_equal(Zf.astype(np.float64), want)
+    assert np.array_equal(Z, bf(want.astype(np.float32)))
+    rows = np.array([4, 1])
+    assert np.array_equal(oracle.wo_linear_rows(X, Q, D, bits, bias, rows), Z[rows])

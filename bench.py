@@ -299,7 +299,8 @@ EXTRA_WORKLOADS = ("dit_ffn_gate_up_4608x24576x4608", "text_cond_proj_512x4608x5
                    "text_cond_proj_padded_4608x4608x53248", "qk_proj_headnorm_16896x4608x4608",
                    "qk_proj_headnorm_6037x4608x4608", "adaln_quantize_4608x4608", "adaln_quantize_16896x4608",
                    "mxfp4_attn_proj_4608x4608x4608", "mxfp4_ffn_gate_up_4608x24576x4608",
-                   "mxfp4_qk_proj_headnorm_16896x4608x4608", "mxfp4_text_cond_proj_512x4608x53248")
+                   "mxfp4_qk_proj_headnorm_16896x4608x4608", "mxfp4_text_cond_proj_512x4608x53248",
+                   "wo4_text_cond_proj_512x4608x53248", "wo8_text_cond_proj_512x4608x53248")
 
 
 def extra_workloads(args, only=None):
@@ -417,8 +418,58 @@ def extra_workloads(args, only=None):
                            ("mxfp4_text_cond_proj_512x4608x53248", "text_cond_proj_512x4608x53248", "bias")):
         if want(name):
             res[name] = mxfp4_workload(src, epi, counts)
+    for bits in (4, 8):
+        name = f"wo{bits}_text_cond_proj_512x4608x53248"
+        if want(name):
+            res[name] = weight_only_workload(bits, counts)
     torch.cuda.empty_cache()
     return res
+
+
+def weight_only_workload(bits, counts):
+    """The deep-K text projection with weight-only 4- or 8-bit weights (bf16 activations, half
+    scales per block of 32): per step one qdt_wo_linear (GEMM over 7 fixed K slices, then the
+    slice sum + bias).  Also timed: the same rows repeated to 4608, the padded call the reference
+    needed for bit-exact outputs (here the 512-row call already gives the same bits)."""
+    import torch
+
+    import qdt_workloads as W
+    import quantized_diffusion_transformer_amd as qdt
+    d = W.make_workload("text_cond_proj_512x4608x53248")
+    M, N, K = d["M"], d["N"], d["K"]
+    X = to_dev(d["X"])
+    Wq, Wd = qdt.wo_quantize(to_dev(d["W"]), bits)
+    b = to_dev(d["bias"])
+
+    def make_step(Xs):
+        plan = qdt.wo_linear_plan(Xs.shape[0], N, K)
+        ws = torch.empty(max(plan["workspace_bytes"], 16), dtype=torch.uint8, device="cuda")
+        Y = torch.empty((Xs.shape[0], N), dtype=torch.bfloat16, device="cuda")
+
+        def step(_, ev):
+            if ev is not None:
+                ev[0].record()
+            qdt.wo_linear(Xs, Wq, Wd, b, out=Y, workspace=ws)
+            if ev is not None:
+                ev[1].record()
+                ev[2].record()
+        return step, plan
+    step, plan = make_step(X)
+    steps, warm = counts(step)
+    ms, tl, _ = time_loop_best(step, steps, warm)
+    Xp = X.repeat(9, 1)
+    step_p, _ = make_step(Xp)
+    steps_p, warm_p = counts(step_p)
+    ms_p, _, _ = time_loop_best(step_p, steps_p, warm_p)
+    ops = 2.0 * M * N * K
+    wbytes = N * K * bits // 8 + N * (K // 32) * 2
+    lin = stats(tl)["mean"]
+    return {"M": M, "N": N, "K": K, "format": f"weight-only {bits}-bit, half scale per 32 ({bits + 0.5} bits/weight)",
+            "split_k": plan["split_k"], "steps": steps, "warmup": warm, "ms_per_step": round(ms, 4),
+            "linear_ms": round(lin, 4), "tflops": round(ops / (lin * 1e-3) / 1e12, 1),
+            "frac_bf16_peak": round(ops / (lin * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "weight_gbs": round(wbytes / (lin * 1e-3) / 1e9, 1),
+            "padded_4608_rows_ms": round(ms_p, 4), "padded_over_512_rows": round(ms_p / ms, 2)}
 
 
 def mxfp4_workload(src, epi, counts):

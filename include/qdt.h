@@ -69,7 +69,7 @@ typedef enum qdt_epilogue {
     QDT_EPI_HEAD_RMSNORM = 2,
     /* Y is int32 [M, N]: the raw accumulators sum_k Xq[m][k] * Wq[n][k] (for testing). */
     QDT_EPI_ACC_I32 = 3,
-    /* Y is fp32 [M, N]: the raw accumulators of qdt_mxfp4_linear (for testing). */
+    /* Y is fp32 [M, N]: the raw accumulators of qdt_mxfp4_linear or qdt_wo_linear (for testing). */
     QDT_EPI_ACC_F32 = 4
 } qdt_epilogue;
 
@@ -220,6 +220,51 @@ qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t*
 
 /* The plan qdt_mxfp4_linear uses (tile, K split, workspace bytes).  Pure host computation. */
 qdt_status qdt_mxfp4_linear_plan(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, qdt_linear_plan* plan);
+
+/*
+ * Weight-only block formats ([PTQ] GGUF paragraph: an 8-bit round-to-nearest format at 8.5 bits
+ * per weight and a 4-bit one at 4.5 bits per weight; [ZC] "The NF4 Exactness Problem": the text
+ * projection is a linear with dequantized 4-bit weights).  Per block of 32 consecutive weights
+ * of a row (amax = max |w| of the block, qmax = 127 for bits = 8, 7 for bits = 4):
+ *   Wd[n][b] = IEEE half of amax / qmax (round half to even, subnormal halves kept; from 65520 up
+ *              saturated to 65504), d its value;
+ *   q = clamp(rint(w / d), -qmax, qmax) with a correctly rounded fp32 division, q = 0 when d = 0;
+ *   bits = 8: Wq int8 [N, K] holds q;  bits = 4: Wq uint8 [N, K/2] holds q + 8 in a nibble, the
+ *   even element in the low nibble.
+ * W bf16 [N, ldw] (first K columns, finite), K % 32 == 0, ldw >= K, ldw % 8 == 0; W and Wq
+ * 16-byte aligned, Wd 2-byte aligned; no output may overlap an input or the other output.
+ * Bit-exact.  N = 0 is a no-op.  Runs once per weight matrix (offline).
+ */
+#define QDT_WO_KSLICE 8192
+qdt_status qdt_wo_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, int bits, uint8_t* Wq, uint16_t* Wd,
+                           void* stream);
+
+/*
+ * Weight-only linear on the bf16 matrix cores: with w~[n][k] = bf16_rne(q * d) (q * d is exact),
+ *   acc[m][n] = sum_k X[m][k] * w~[n][k], fp32 accumulation of exact products;
+ *   QDT_EPI_BIAS: Y bf16 [M, ldy], Y[m][n] = bf16_rne(acc + (float)bias[n]) (bias NULL = 0);
+ *   QDT_EPI_ACC_F32: Y fp32 [M, ldy], the accumulators.
+ * Batch invariance ([ZC] "The NF4 Exactness Problem": a kernel whose reduction order follows the
+ * row count changes the outputs when fewer rows are projected): K is summed in slices of
+ * QDT_WO_KSLICE elements by the same instruction sequence for every tile, the slice sums are
+ * added in slice order, then the bias.  Y[m][n] depends only on X's row m, the weights of row n,
+ * bias[n] and K: it is bit-identical whatever M is, whichever other rows are in the call and
+ * wherever row m sits in it.
+ *   X bf16 [M, ldx] (first K columns), Wq / Wd from qdt_wo_quantize with the same bits (4 or 8).
+ *   K % 256 == 0, N % 16 == 0, ldx >= K, ldx % 8 == 0, ldy >= N, ldy % 8 == 0; X, Wq, bias, Y
+ *   16-byte aligned, Wd 2-byte aligned; Y must not overlap an input.
+ *   When K > QDT_WO_KSLICE the slices write fp32 partial sums to `workspace`
+ *   (qdt_wo_linear_plan: workspace_bytes = split_k * M * N * 4, 16-byte aligned, caller owned, not
+ *   overlapping anything else) and a second kernel adds them; otherwise workspace may be NULL.
+ *   QDT_EWORKSPACE if it is missing or too small.  M = 0 is a no-op.
+ */
+qdt_status qdt_wo_linear(const uint16_t* X, int64_t ldx, const uint8_t* Wq, const uint16_t* Wd, int bits,
+                         const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi, void* Y,
+                         int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The plan qdt_wo_linear uses: 256 x 256 tiles, split_k = ceil(K / QDT_WO_KSLICE) for every M.
+ * Pure host computation. */
+qdt_status qdt_wo_linear_plan(int64_t M, int64_t N, int64_t K, qdt_linear_plan* plan);
 
 /* The plan qdt_w8a8_linear uses for this problem (pure host computation, no device call). */
 qdt_status qdt_w8a8_linear_plan(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, qdt_linear_plan* plan);

@@ -59,6 +59,9 @@ _SIGS = {
     "qdt_mxfp4_quantize": ([_P, _P, _I64, _I64, _I64, _P, _P, _P], _I),
     "qdt_mxfp4_linear": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P, _SZ, _P], _I),
     "qdt_mxfp4_linear_plan": ([_I64, _I64, _I64, _I, C.POINTER(qdt_linear_plan)], _I),
+    "qdt_wo_quantize": ([_P, _I64, _I64, _I64, _I, _P, _P, _P], _I),
+    "qdt_wo_linear": ([_P, _I64, _P, _P, _I, _P, _I64, _I64, _I64, _I, _P, _I64, _P, _SZ, _P], _I),
+    "qdt_wo_linear_plan": ([_I64, _I64, _I64, C.POINTER(qdt_linear_plan)], _I),
     "qdt_w8a8_linear_plan": ([_I64, _I64, _I64, _I, C.POINTER(qdt_linear_plan)], _I),
     "qdt_w8a8_linear_plan_for": ([_I64, _I64, _I64, _I, C.c_int32, C.c_int32, C.POINTER(qdt_linear_plan)], _I),
     "qdt_w8a8_linear_workspace_size": ([_I64, _I64, _I64, _I, C.POINTER(_SZ)], _I),
@@ -256,6 +259,66 @@ def mxfp4_linear(Xq: torch.Tensor, Xs: torch.Tensor, Wq: torch.Tensor, Ws: torch
                             _stream(stream)), "qdt_mxfp4_linear")
     return out
 
+
+QDT_WO_KSLICE = 8192
+
+
+def wo_quantize(W: torch.Tensor, bits: int = 4, Wq=None, Wd=None, stream=None):
+    """Weight-only blocks of bf16 W [N, K] (offline): codes (int8 [N, K] for 8 bits, uint8 [N, K/2]
+    nibbles for 4 bits) and half-precision scale bits (int16 [N, K/32])."""
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    _dev(W, torch.bfloat16, "W")
+    W, ldw = _rows(W, "W")
+    N, K = W.shape
+    if Wq is None:
+        Wq = torch.empty((N, K if bits == 8 else K // 2), dtype=torch.int8 if bits == 8 else torch.uint8,
+                         device=W.device)
+    if Wd is None:
+        Wd = torch.empty((N, K // 32), dtype=torch.int16, device=W.device)
+    _check(qdt_wo_quantize(_ptr(W), N, K, ldw, bits, _ptr(Wq), _ptr(Wd), _stream(stream)), "qdt_wo_quantize")
+    return Wq, Wd
+
+
+def wo_linear_plan(M: int, N: int, K: int) -> dict:
+    p = qdt_linear_plan()
+    _check(qdt_wo_linear_plan(M, N, K, C.byref(p)), "qdt_wo_linear_plan")
+    return p.as_dict()
+
+
+def wo_linear(X: torch.Tensor, Wq: torch.Tensor, Wd: torch.Tensor, bias: torch.Tensor | None = None,
+              epilogue: str = "bias", out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Weight-only linear: bf16 [M, N] = X . dequant(W)^T + bias ("bias"), or the fp32 accumulators
+    ("acc_f32").  X bf16 [M, K]; Wq / Wd from wo_quantize (the code width gives the bit count).
+    Every output row is bit-identical whatever M is."""
+    _dev(X, torch.bfloat16, "X")
+    X, ldx = _rows(X, "X")
+    M, K = X.shape
+    N = Wq.shape[0]
+    if Wq.dtype == torch.int8 and Wq.shape == (N, K):
+        bits = 8
+    elif Wq.dtype == torch.uint8 and Wq.shape == (N, K // 2):
+        bits = 4
+    else:
+        raise ValueError("wo_linear: Wq must be int8 [N, K] or uint8 [N, K/2]")
+    _dev(Wd, torch.int16, "Wd")
+    if Wd.shape != (N, K // 32):
+        raise ValueError("wo_linear: Wd must be [N, K/32]")
+    if bias is not None:
+        _dev(bias, torch.bfloat16, "bias")
+    if epilogue not in ("bias", "acc_f32"):
+        raise ValueError("wo_linear: epilogue must be 'bias' or 'acc_f32'")
+    epi = QDT_EPI_ACC_F32 if epilogue == "acc_f32" else QDT_EPI_BIAS
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32 if epilogue == "acc_f32" else torch.bfloat16, device=X.device)
+    out, ldy = _rows(out, "out")
+    need = wo_linear_plan(M, N, K)["workspace_bytes"]
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    _check(qdt_wo_linear(_ptr(X), ldx, _ptr(Wq), _ptr(Wd), bits, _ptr(bias), M, N, K, epi, _ptr(out), ldy,
+                         _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+                         _stream(stream)), "qdt_wo_linear")
+    return out
 
 def linear_plan(M: int, N: int, K: int, epilogue: str = "bias", tile: int | None = None,
                 split_k: int | None = None) -> dict:

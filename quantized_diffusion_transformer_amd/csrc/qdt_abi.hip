@@ -448,4 +448,93 @@ qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t*
     return QDT_OK;
 }
 
+// The weight-only linear's plan: 256 x 256 tiles and K slices of QDT_WO_KSLICE elements,
+// whatever M is (the fixed reduction structure makes every output independent of M).
+static qdt_status wo_plan(int64_t M, int64_t N, int64_t K, Plan* p) {
+    if (M < 0 || M > INT32_MAX / 2 || N <= 0 || N > INT32_MAX / 2 || N % 16 != 0) return QDT_ESHAPE;
+    if (K <= 0 || K % 256 != 0 || K > QDT_MAX_K) return QDT_ESHAPE;
+    memset(p, 0, sizeof(*p));
+    p->tile = QDT_TILE_256;
+    p->bm = p->bn = 256;
+    p->tiles_m = (int)cdiv(M, 256);
+    p->tiles_n = (int)cdiv(N, 256);
+    p->kt_total = (int)(K / 128);
+    p->kt_per_split = QDT_WO_KSLICE / 128;
+    p->split_k = (int)cdiv(p->kt_total, p->kt_per_split);
+    p->group_m = 1;
+    const int64_t grid = (int64_t)p->tiles_m * p->tiles_n * p->split_k;
+    if (grid > INT32_MAX) return QDT_ESHAPE;
+    p->grid = (int)grid;
+    p->ws_bytes = p->split_k > 1 ? (int64_t)p->split_k * M * N * 4 : 0;
+    return QDT_OK;
+}
+
+qdt_status qdt_wo_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, int bits, uint8_t* Wq, uint16_t* Wd,
+                           void* stream) {
+    if (bits != 4 && bits != 8) return QDT_EINVAL;
+    if (N < 0 || N > INT32_MAX) return QDT_ESHAPE;
+    if (N > 0 && (!W || !Wq || !Wd)) return QDT_EINVAL;
+    if (K <= 0 || K % 32 != 0 || K > QDT_MAX_K || ldw < K) return QDT_ESHAPE;
+    if (!aligned16(W) || !aligned16(Wq) || (reinterpret_cast<uintptr_t>(Wd) & 1u) != 0 || ldw % 8 != 0)
+        return QDT_EALIGN;
+    if (N == 0) return QDT_OK;
+    const int64_t wb = ((N - 1) * ldw + K) * 2, qb = N * K * bits / 8, db = N * (K / 32) * 2;
+    if (overlap(Wq, qb, W, wb) || overlap(Wd, db, W, wb) || overlap(Wd, db, Wq, qb)) return QDT_EALIAS;
+    return hip_status(launch_wo_quant(W, ldw, N, K, bits, Wq, Wd, reinterpret_cast<hipStream_t>(stream)));
+}
+
+qdt_status qdt_wo_linear_plan(int64_t M, int64_t N, int64_t K, qdt_linear_plan* plan) {
+    if (!plan) return QDT_EINVAL;
+    Plan p;
+    qdt_status r = wo_plan(M, N, K, &p);
+    if (r == QDT_OK) export_plan(p, plan);
+    return r;
+}
+
+qdt_status qdt_wo_linear(const uint16_t* X, int64_t ldx, const uint8_t* Wq, const uint16_t* Wd, int bits,
+                         const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi, void* Y,
+                         int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+    if (bits != 4 && bits != 8) return QDT_EINVAL;
+    if (epi != QDT_EPI_BIAS && epi != QDT_EPI_ACC_F32) return QDT_EINVAL;
+    Plan p;
+    qdt_status r = wo_plan(M, N, K, &p);
+    if (r != QDT_OK) return r;
+    if (ldx < K || ldy < N) return QDT_ESHAPE;
+    if (M == 0) return QDT_OK;
+    if (!X || !Wq || !Wd || !Y) return QDT_EINVAL;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(bias) || !aligned16(Y) || ldx % 8 != 0 || ldy % 8 != 0 ||
+        (reinterpret_cast<uintptr_t>(Wd) & 1u) != 0)
+        return QDT_EALIGN;
+    const int64_t es = epi == QDT_EPI_ACC_F32 ? 4 : 2;
+    const int64_t ybytes = ((M - 1) * ldy + N) * es;
+    const void* ins[4] = {X, Wq, Wd, bias};
+    const int64_t inb[4] = {((M - 1) * ldx + K) * 2, N * K * bits / 8, N * (K / 32) * 2, bias ? N * 2 : 0};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(Y, ybytes, ins[i], inb[i])) return QDT_EALIAS;
+    if (p.ws_bytes > 0) {
+        if (!workspace || (int64_t)workspace_bytes < p.ws_bytes) return QDT_EWORKSPACE;
+        if (!aligned16(workspace)) return QDT_EALIGN;
+        if (overlap(Y, ybytes, workspace, p.ws_bytes)) return QDT_EALIAS;
+        for (int i = 0; i < 4; ++i)
+            if (overlap(workspace, p.ws_bytes, ins[i], inb[i])) return QDT_EALIAS;
+    }
+    const int e = epi == QDT_EPI_ACC_F32 ? EPI_ACC : EPI_F32BIAS;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if ((r = hip_status(launch_wo_gemm(X, ldx, Wq, Wd, bits, bias, (int)M, (int)N, (int)K, e, Y, ldy,
+                                       reinterpret_cast<float*>(workspace), p, st))) != QDT_OK)
+        return r;
+    if (p.split_k == 1) return QDT_OK;
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.bias = bias;
+    a.Y = Y;
+    a.ldy = ldy;
+    a.ws = reinterpret_cast<int32_t*>(workspace);
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.epi = e;
+    return hip_status(launch_splitk_f32_epilogue(a, p.split_k, e, st));
+}
+
 }  // extern "C"

@@ -64,6 +64,14 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, const Plan& p, hipStream_t st);
 // biased block exponents [M][K/32] / [N][K/32]; a.epi EPI_F32BIAS, EPI_F32SILU, EPI_F32RMSNORM or
 // EPI_ACC (fp32 accumulators).
 hipError_t launch_gemm_mx(const GemmArgs& a, const uint8_t* xsc, const uint8_t* wsc, const Plan& p, hipStream_t st);
+// Weight-only block formats: quantizer of W [N, ldw] (first K columns) into codes Q and half
+// scales D, and the linear Y = X * dequant(W)^T (+ bias) on bf16 matrix cores.  epi: EPI_F32BIAS
+// (bf16 Y) or EPI_ACC (fp32 Y); a K split (pl.split_k > 1) writes fp32 partials to ws.
+hipError_t launch_wo_quant(const uint16_t* W, int64_t ldw, int64_t N, int64_t K, int bits, uint8_t* Q, uint16_t* D,
+                           hipStream_t st);
+hipError_t launch_wo_gemm(const uint16_t* X, int64_t ldx, const uint8_t* Wq, const uint16_t* Wd, int bits,
+                          const uint16_t* bias, int M, int N, int K, int epi, void* Y, int64_t ldy, float* ws,
+                          const Plan& pl, hipStream_t st);
 // Sum of the S int32 partial slices followed by epilogue `epi` (BIAS, SILU, RMSNORM, ACC).
 hipError_t launch_splitk_epilogue(const GemmArgs& a, int split_k, int epi, hipStream_t st);
 // Sum of the S fp32 partial slices of the FP4 GEMM, then epilogue `epi` (F32BIAS, F32SILU,

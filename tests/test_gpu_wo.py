@@ -1,0 +1,184 @@
+"""Parity of the weight-only block formats (qdt_wo_quantize, qdt_wo_linear) against the oracle.
+
+Codes and half-precision scales are bit-exact.  The linear accumulates exact bf16 products in
+fp32: on inputs whose sums are exact in fp32 (in any order) the accumulators and the bias output
+are bit-exact; on general inputs the output is within one bf16 rounding plus the fp32 summation
+bound of the exact sum.  Batch invariance is checked bit for bit: a row's output does not depend
+on how many rows the call has, which other rows it has, or where the row sits.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import qdt_workloads as W
+from qdt_testutil import bits_equal, sample_rows, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+qdt = pytest.importorskip("quantized_diffusion_transformer_amd")
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def scales_dev(D):
+    return torch.from_numpy(np.ascontiguousarray(D).view(np.int16)).cuda()
+
+
+def scales_host(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def quantize_and_check(Wb, bits, ldw=None):
+    """GPU quantizer on bf16 bits Wb [N, K] (optionally stored with row stride ldw and NaN
+    padding), checked bit for bit against the oracle; returns the device codes and scales."""
+    N, K = Wb.shape
+    if ldw is not None:
+        Wp = np.full((N, ldw), 0x7FC0, np.uint16)
+        Wp[:, :K] = Wb
+        Wdev = to_dev(Wp)[:, :K]
+    else:
+        Wdev = to_dev(Wb)
+    Q, D = qdt.wo_quantize(Wdev, bits)
+    Q_ref, D_ref = oracle.wo_quantize(Wb, bits)
+    Qh, Dh = to_host(Q), scales_host(D)
+    assert bits_equal(Dh, D_ref), f"{np.sum(Dh != D_ref)} scales differ"
+    assert bits_equal(Qh, Q_ref), f"{np.sum(Qh != Q_ref)} code bytes differ"
+    return Q, D, Q_ref, D_ref
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("N,K", [(1, 32), (37, 64), (256, 4608), (300, 53248)])
+def test_wo_quantize_parity(bits, N, K):
+    announce(f"wo_quantize bits={bits} N={N} K={K}")
+    rng = np.random.default_rng(700 + N + bits)
+    w = rng.standard_normal((N, K)) * np.exp(rng.normal(-4.5, 1.0, (N, 1)))
+    quantize_and_check(W.f32_to_bf16_bits(w.astype(np.float32)), bits)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_wo_quantize_special_blocks_and_row_stride(bits):
+    """Zero blocks, scales that underflow the half format or land in its subnormals, scales
+    that saturate, exact ties, one-element blocks; rows stored with ldw > K (NaN padding)."""
+    announce(f"wo_quantize special blocks bits={bits}")
+    qmax = 127 if bits == 8 else 7
+    rng = np.random.default_rng(710 + bits)
+    K = 32 * 8
+    w = np.zeros((6, K), np.float32)
+    w[0] = rng.standard_normal(K) * 1e-9                 # scale rounds to 0
+    w[1] = rng.standard_normal(K) * 3e-6                 # half subnormal scales
+    w[2] = rng.standard_normal(K) * 1e7                  # saturated scales
+    t = np.tile([0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5, -5.5], K // 8)
+    t[::32] = qmax
+    w[3] = t * 2.0 ** -6                                 # exact ties
+    w[4, ::32] = -0.25                                   # one element per block
+    w[5] = rng.standard_normal(K)                        # ordinary
+    quantize_and_check(W.f32_to_bf16_bits(w), bits, ldw=K + 40)
+
+
+def exact_weights(N, K, bits, rng):
+    """Weights on the grid of d = 2^-6 with +-qmax in every block: exact codes, w~ = q 2^-6."""
+    qmax = 127 if bits == 8 else 7
+    qi = rng.integers(-qmax, qmax + 1, (N, K))
+    qi[:, ::32] = qmax * rng.choice([-1, 1], (N, K // 32))
+    return W.f32_to_bf16_bits((qi * 2.0 ** -6).astype(np.float32))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M,N,K", [(1, 16, 256), (300, 272, 1024), (64, 256, 16384), (37, 48, 8448)])
+def test_wo_linear_exact_sums(bits, M, N, K):
+    """X in {-1, 0, 1} / 4 and w~ = q 2^-6: every partial sum is a multiple of 2^-8 below 2^15,
+    exact in fp32 in any order, so accumulators and bias outputs are bit-exact (ragged M and N
+    tiles, K split into QDT_WO_KSLICE slices with a short last slice)."""
+    plan = qdt.wo_linear_plan(M, N, K)
+    announce(f"wo_linear exact bits={bits} M={M} N={N} K={K} split={plan['split_k']}")
+    rng = np.random.default_rng(720 + M + K + bits)
+    Wb = exact_weights(N, K, bits, rng)
+    X = W.f32_to_bf16_bits((rng.integers(-1, 2, (M, K)) * 0.25).astype(np.float32))
+    bias = W.f32_to_bf16_bits((rng.integers(-64, 65, N) * 2.0 ** -5).astype(np.float32))
+    Q, D, Q_ref, D_ref = quantize_and_check(Wb, bits)
+    Xd = to_dev(X)
+    acc = to_host(qdt.wo_linear(Xd, Q, D, None, "acc_f32"))
+    _, acc_ref = oracle.wo_linear_rows(X, Q_ref, D_ref, bits, None, want_f32=True)
+    assert bits_equal(acc, acc_ref), f"{np.sum(acc != acc_ref)} accumulators differ"
+    Y = to_host(qdt.wo_linear(Xd, Q, D, to_dev(bias)))
+    assert bits_equal(Y, oracle.wo_linear_rows(X, Q_ref, D_ref, bits, bias))
+
+
+def within_bound(Y, X, Q_ref, D_ref, bits, bias, rows):
+    """|Y - (acc + b)| <= gamma_K sum |x w~| + half a bf16 ulp of the result (plus the fp32
+    rounding of acc + b), with acc the exact fp64 sum; returns the fraction of outputs equal to
+    the oracle's correctly rounded result."""
+    Wd = oracle.wo_dequantize(Q_ref, D_ref, bits)
+    x = W.bf16_bits_to_f32(X[rows]).astype(np.float64)
+    w = W.bf16_bits_to_f32(Wd).astype(np.float64)
+    K = x.shape[1]
+    gam = K * 2.0 ** -24 / (1 - K * 2.0 ** -24)
+    b = 0.0 if bias is None else W.bf16_bits_to_f32(bias).astype(np.float64)
+    ref = x @ w.T + b
+    bound = gam * (np.abs(x) @ np.abs(w).T) + 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    got = W.bf16_bits_to_f32(Y[rows]).astype(np.float64)
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), f"worst error / bound {np.max(err / bound):.3f}"
+    Y_ref = oracle.wo_linear_rows(X, Q_ref, D_ref, bits, bias, rows)
+    return float(np.mean(Y[rows] == Y_ref))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_wo_linear_within_bound(bits):
+    announce(f"wo_linear general inputs bits={bits} 300x4608x4608")
+    d = W.make_linear(300, 4608, 4608, seed=730 + bits, x_kind="pct1", w_sigma=0.015, bias=True)
+    Q, D, Q_ref, D_ref = quantize_and_check(d["W"], bits)
+    Y = to_host(qdt.wo_linear(to_dev(d["X"]), Q, D, to_dev(d["bias"])))
+    exact = within_bound(Y, d["X"], Q_ref, D_ref, bits, d["bias"], sample_rows(300, 16, 3))
+    assert exact > 0.9, f"only {exact:.3f} of the outputs equal the correctly rounded result"
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_wo_text_projection_shape_and_batch_invariance(bits):
+    """The deep-K text projection (512 x 4608 x 53248, split into 7 slices): sampled rows within
+    the bound; then the page's exactness case: the 512 real rows projected alone equal the first
+    512 rows of the call padded to 4608 rows (the fillers repeat the real rows), bit for bit."""
+    d = W.make_workload("text_cond_proj_512x4608x53248")
+    plan = qdt.wo_linear_plan(512, 4608, 53248)
+    announce(f"wo_linear text projection bits={bits} split={plan['split_k']}")
+    Q, D, Q_ref, D_ref = quantize_and_check(d["W"], bits)
+    X = to_dev(d["X"])
+    b = to_dev(d["bias"])
+    Y = qdt.wo_linear(X, Q, D, b)
+    Yh = to_host(Y)
+    within_bound(Yh, d["X"], Q_ref, D_ref, bits, d["bias"], sample_rows(512, 3, 4))
+    announce(f"wo_linear 4608 padded rows bits={bits}")
+    Xpad = X.repeat(9, 1)
+    Ypad = to_host(qdt.wo_linear(Xpad, Q, D, b))
+    for r in range(9):
+        assert bits_equal(Ypad[512 * r:512 * (r + 1)], Yh), f"copy {r} of the rows differs"
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_wo_batch_invariance(bits):
+    """A row's output is the same bits whatever the row count, the other rows and the row's
+    position; also with a row stride ldx > K whose padding holds NaN."""
+    M, N, K = 700, 528, 16640
+    announce(f"wo_linear batch invariance bits={bits} M={M} N={N} K={K}")
+    rng = np.random.default_rng(740 + bits)
+    d = W.make_linear(M, N, K, seed=741 + bits, x_kind="pct1", w_sigma=0.015, bias=True)
+    Q, D, _, _ = quantize_and_check(d["W"], bits)
+    b = to_dev(d["bias"])
+    X = to_dev(d["X"])
+    Y = to_host(qdt.wo_linear(X, Q, D, b))
+    for T in (1, 37, 256, 300):
+        assert bits_equal(to_host(qdt.wo_linear(X[:T].contiguous(), Q, D, b)), Y[:T]), f"T={T}"
+    perm = rng.permutation(M)
+    assert bits_equal(to_host(qdt.wo_linear(X[perm].contiguous(), Q, D, b)), Y[perm])
+    other = to_dev(W.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32) * 30))
+    mixed = torch.where(torch.arange(M, device="cuda")[:, None] % 3 == 0, X, other)
+    keep = np.arange(M) % 3 == 0
+    assert bits_equal(to_host(qdt.wo_linear(mixed, Q, D, b))[keep], Y[keep])
+    Xp = np.full((M, K + 24), 0x7FC0, np.uint16)
+    Xp[:, :K] = d["X"]
+    assert bits_equal(to_host(qdt.wo_linear(to_dev(Xp)[:, :K], Q, D, b)), Y)

@@ -251,7 +251,7 @@ qdt_status qdt_wo_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
  * bias[n] and K: it is bit-identical whatever M is, whichever other rows are in the call and
  * wherever row m sits in it.
  *   X bf16 [M, ldx] (first K columns), Wq / Wd from qdt_wo_quantize with the same bits (4 or 8).
- *   K % 256 == 0, N % 16 == 0, ldx >= K, ldx % 8 == 0, ldy >= N, ldy % 8 == 0; X, Wq, bias, Y
+ *   K % 512 == 0, N % 16 == 0, ldx >= K, ldx % 8 == 0, ldy >= N, ldy % 8 == 0; X, Wq, bias, Y
  *   16-byte aligned, Wd 2-byte aligned; Y must not overlap an input.
  *   When K > QDT_WO_KSLICE the slices write fp32 partial sums to `workspace`
  *   (qdt_wo_linear_plan: workspace_bytes = split_k * M * N * 4, 16-byte aligned, caller owned, not

@@ -452,7 +452,7 @@ qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t*
 // whatever M is (the fixed reduction structure makes every output independent of M).
 static qdt_status wo_plan(int64_t M, int64_t N, int64_t K, Plan* p) {
     if (M < 0 || M > INT32_MAX / 2 || N <= 0 || N > INT32_MAX / 2 || N % 16 != 0) return QDT_ESHAPE;
-    if (K <= 0 || K % 256 != 0 || K > QDT_MAX_K) return QDT_ESHAPE;
+    if (K <= 0 || K % 512 != 0 || K > QDT_MAX_K) return QDT_ESHAPE;
     memset(p, 0, sizeof(*p));
     p->tile = QDT_TILE_256;
     p->bm = p->bn = 256;

@@ -121,6 +121,9 @@ struct WoKArgs {
     int tiles_m, tiles_n, split_k, kt_total, kt_per_split;
 };
 
+// Row r mod 16 with its two 2-bit halves swapped: the token LDS swizzle.
+__device__ __forceinline__ int rot4(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 // MFMA with the accumulator tuple tied in place in AGPRs (see the W8A8 GEMM for why asm).
 __device__ __forceinline__ void mfma_bf16_acc(v4f& c, const v4u& a, const v4u& b) {
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
@@ -130,7 +133,7 @@ template <int BITS>
 struct WoRegs {
     static constexpr int NC = BITS == 8 ? 2 : 1;  // 16-byte code chunks per lane and fragment
     v4u c[4][NC];                                 // codes of the lane's block, fragments 0..3
-    uint32_t s[4];                                // half-precision scale bits
+    uint16_t s[4];                                // half-precision scale bits
 };
 
 // EPI: EPI_F32BIAS (bf16 out), EPI_ACC (fp32 accumulators out), EPI_PARTIAL (fp32 slice sums).
@@ -158,15 +161,17 @@ wo_gemm_kernel(WoKArgs p) {
     const int tm = tr % p.tiles_m, split = tr / p.tiles_m;
     const int m0 = tm * BM, n0 = tn * BN;
     const int kt0 = split * p.kt_per_split;
-    // stages of the slice: even and >= 2 (K % 256 == 0, slices of an even number of stages), so
-    // the main loop runs stages in pairs with no conditional stage (a merge of control flow
-    // would make the compiler shuffle all 256 accumulator registers)
+    // stages of the slice: a multiple of 4 (K % 512 == 0, slices of 64 stages), so the main loop
+    // runs stages in fours with no conditional stage (a merge of control flow would make the
+    // compiler shuffle all 256 accumulator registers)
     const int nk = min(p.kt_total - kt0, p.kt_per_split);
 
     // ---- token LDS-DMA: instruction i of wave w fills LDS rows 4 (NDMA w + i) .. + 3 of the
     // stage (1 KiB); lane l moves row r = 4 (NDMA w + i) + l / 16 into LDS chunk slot l % 16, which
-    // holds the row's global 16-byte chunk (l % 16) ^ (r & 15).  Rows past M are clamped to the
-    // last row: their outputs are not stored.
+    // holds the row's global 16-byte chunk (l % 16) ^ rot4(r).  rot4 swaps the two 2-bit halves of
+    // r mod 16, so the 16 rows x 4 chunks of a fragment read land on distinct 16-byte bank groups
+    // whether the LDS serves 16, 32 or 64 lanes per pass.  Rows past M are clamped to the last
+    // row: their outputs are not stored.
     const int xlast = p.M - m0 - 1;
     const uint8_t* xbase =
         uniform_ptr(reinterpret_cast<const uint8_t*>(p.X + (int64_t)m0 * p.ldx + (int64_t)kt0 * BK));
@@ -174,7 +179,7 @@ wo_gemm_kernel(WoKArgs p) {
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
         const int r = 4 * (NDMA * wave + i) + (lane >> 4);
-        xoff[i] = (uint32_t)((int64_t)min(r, xlast) * p.ldx * 2) + (uint32_t)((((lane & 15) ^ (r & 15))) * 16);
+        xoff[i] = (uint32_t)((int64_t)min(r, xlast) * p.ldx * 2) + (uint32_t)(((lane & 15) ^ rot4(r)) * 16);
     }
     const uint32_t ldsx = __builtin_amdgcn_readfirstlane(lds_offset(smem) + wave * NDMA * 1024);
     auto dma_stage = [&](int buf, int j) __attribute__((always_inline)) {
@@ -207,39 +212,59 @@ wo_gemm_kernel(WoKArgs p) {
 #pragma unroll
         for (int f = 0; f < FN; ++f) R.s[f] = sp[soff[f]];
     };
-    // The compiler does not count the asm LDS-DMAs in its load-counter bookkeeping: after the
-    // explicit wait for everything, this makes it take the code registers as complete there.
-    auto touch = [&](const Regs& R) __attribute__((always_inline)) {
+    // Marks the point where a register set is first used: the compiler waits for its loads right
+    // here and cannot move arithmetic on them above it (asm statements keep their order), so no
+    // wait for a set lands where it would also hold back loads issued after it.  (The compiler
+    // does not count the asm LDS-DMAs, so a wait it places early would cover them too.)
+    auto fence = [&](Regs& R) __attribute__((always_inline)) {
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
 #pragma unroll
-            for (int c = 0; c < Regs::NC; ++c) asm volatile("" ::"v"(R.c[f][c]));
-            asm volatile("" ::"v"(R.s[f]));
+            for (int c = 0; c < Regs::NC; ++c) asm volatile("" : "+v"(R.c[f][c]));
+            asm volatile("" : "+v"(R.s[f]));
         }
     };
 
     // ---- dequantization.  Pair p (0..3) of fragment f's 8 elements for K step s: elements
     // 2 p, 2 p + 1 of the lane's 8 (block elements 8 s + 2 p, + 1) as bf16(q * d), computed as
     // fma(code, d, -offset * d), exact in fp32 (the stored code is q + 8, or q + 128 after the
-    // sign flip of the int8 byte).
-    auto deq_pair = [&](const Regs& R, int f, int s, int pr, float d, float nod) __attribute__((always_inline)) {
-        uint32_t lo, hi;
+    // sign flip of the int8 byte).  Split in parts so that each can follow its own MFMA:
+    // deq_src (once per fragment and step for 4 bits, per dword for 8 bits) isolates the codes as
+    // bytes, deq_cvt turns two of them into floats (v_cvt_f32_ubyteN), then fma and pack.
+    auto deq_src = [&](const Regs& R, int f, int s, int pr, uint32_t& lo, uint32_t& hi) __attribute__((always_inline)) {
         if constexpr (BITS == 4) {
             const uint32_t x = R.c[f][0][s];
-            const uint32_t e0 = (x >> (8 * pr)) & 0xFu, e1 = (x >> (8 * pr + 4)) & 0xFu;
-            lo = e0;
-            hi = e1;
+            lo = x & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6 in bytes 0..3
+            hi = (x >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
+            // opaque to the optimizer, so that each element is one v_cvt_f32_ubyteN of these
+            // words instead of a re-derived bit-field extract plus a conversion
+            asm volatile("" : "+v"(lo), "+v"(hi));
         } else {
             const int dw = 2 * s + pr / 2;
-            const uint32_t x = R.c[f][dw / 4][dw % 4] ^ 0x80808080u;
-            lo = (x >> (16 * (pr & 1))) & 0xFFu;
-            hi = (x >> (16 * (pr & 1) + 8)) & 0xFFu;
+            lo = R.c[f][dw / 4][dw % 4] ^ 0x80808080u;  // elements 4 (pr / 2) .. + 3, biased by 128
+            hi = 0u;
+            asm volatile("" : "+v"(lo));
         }
-        return pack_bf16x2(__builtin_fmaf((float)lo, d, nod), __builtin_fmaf((float)hi, d, nod));
+    };
+    auto deq_cvt = [&](uint32_t lo, uint32_t hi, int pr, float& c0, float& c1) __attribute__((always_inline)) {
+        if constexpr (BITS == 4) {
+            c0 = (float)((lo >> (8 * pr)) & 0xFFu);
+            c1 = (float)((hi >> (8 * pr)) & 0xFFu);
+        } else {
+            c0 = (float)((lo >> (16 * (pr & 1))) & 0xFFu);
+            c1 = (float)((lo >> (16 * (pr & 1) + 8)) & 0xFFu);
+        }
+    };
+    auto deq_pair = [&](const Regs& R, int f, int s, int pr, float d, float nod) __attribute__((always_inline)) {
+        uint32_t lo, hi;
+        float c0, c1;
+        deq_src(R, f, s, pr, lo, hi);
+        deq_cvt(lo, hi, pr, c0, c1);
+        return pack_bf16x2(__builtin_fmaf(c0, d, nod), __builtin_fmaf(c1, d, nod));
     };
     constexpr float OFS = BITS == 8 ? -128.0f : -8.0f;
     auto scale_of = [&](const Regs& R, int f) __attribute__((always_inline)) {
-        return (float)__builtin_bit_cast(_Float16, (uint16_t)R.s[f]);
+        return (float)__builtin_bit_cast(_Float16, R.s[f]);
     };
 
     v4f acc[FN][FM];
@@ -252,7 +277,7 @@ wo_gemm_kernel(WoKArgs p) {
     const int frow = (lane & 15) * ROWB;
     auto tok = [&](int buf, int it) __attribute__((always_inline)) {
         const int s = it / FM, fm = it % FM;
-        const int slot = ((4 * (lane >> 4) + s) ^ (lane & 15)) * 16;
+        const int slot = ((4 * (lane >> 4) + s) ^ rot4(lane & 15)) * 16;
         return *reinterpret_cast<const v4u*>(smem + buf * STAGE + fm * 16 * ROWB + frow + slot);
     };
 
@@ -260,16 +285,21 @@ wo_gemm_kernel(WoKArgs p) {
     // stage's loads into the other buffers, then 4 K steps of 16 x 4 MFMAs.  The weight fragments
     // of a K step are formed during the previous one (those of step 0 during step 3 of the
     // previous stage, from the other register set, whose loads were issued a stage earlier).
-    Regs R0, R1;
+    // ---- the weight codes travel in a ring of 4 register sets, loaded two stages ahead: stage j
+    // computes from set j % 4 (and set (j + 1) % 4 for the next stage's step-0 fragments, during
+    // its last K step) while the loads of stage j + 2 fill set (j + 2) % 4.  At the top of a stage
+    // its LDS-DMAs must have landed but the NW code loads issued after them may not have:
+    // vmcnt(NW).  Past the slice end, loads are clamped to its last stage (unused, in bounds),
+    // which keeps the counts fixed and the loop free of branches.
+    constexpr int NW = FN * Regs::NC + FN;  // VMEM instructions per wload
+    Regs S0, S1, S2, S3;
     v4u a[FN];
-    auto stage = [&](int j, Regs& Rc, Regs& Rn, int buf) __attribute__((always_inline)) {
-        wait_vmcnt<0>();
-        touch(Rc);
+    auto stage = [&](int j, Regs& Rc, Regs& Rn, Regs& Rl, int buf) __attribute__((always_inline)) {
+        wait_vmcnt<NW>();
+        fence(Rc);
         __syncthreads();
-        if (j + 1 < nk) {
-            wload(Rn, j + 1);
-            dma_stage(buf ^ 1, j + 1);
-        }
+        dma_stage(buf ^ 1, min(j + 1, nk - 1));
+        wload(Rl, min(j + 2, nk - 1));
         float d[FN], nod[FN], dn[FN], nodn[FN];
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
@@ -279,28 +309,41 @@ wo_gemm_kernel(WoKArgs p) {
         v4u bq[3];
         bq[0] = tok(buf, 0);
         bq[1] = tok(buf, 1);
+        // Each iteration: 4 MFMAs (token fragment it against the 4 weight fragments), one slice of
+        // the next K step's dequantization after each MFMA (so the VALU work runs in the MFMAs'
+        // shadow), and the LDS read of token fragment it + 2.
         v4u an[FN];
+        uint32_t slo = 0u, shi = 0u;
 #pragma unroll
         for (int it = 0; it < 4 * FM; ++it) {
             const int s = it / FM, fm = it % FM;
-            if (it + 2 < 4 * FM) bq[(it + 2) % 3] = tok(buf, it + 2);
-            if (fm == 0) asm volatile("s_nop 1");  // VALU-written fragments -> MFMA source
+            const int f = fm / 4, pr = fm % 4;          // fragment and pair formed in this iteration
+            const bool next = s == 3;                   // forming the next stage's step 0
+            Regs& Rs = next ? Rn : Rc;
+            const int ss = next ? 0 : s + 1;
+            if (next && fm == 0) {
+                fence(Rn);
 #pragma unroll
-            for (int f = 0; f < FN; ++f) mfma_bf16_acc(acc[f][fm], a[f], bq[it % 3]);
-            // form pair (fm % 4) of weight fragment fm / 4 for the next K step
-            const int f = fm / 4, pr = fm % 4;
-            if (s < 3) {
-                an[f][pr] = deq_pair(Rc, f, s + 1, pr, d[f], nod[f]);
-            } else {
-                if (fm == 0) {
-#pragma unroll
-                    for (int g = 0; g < FN; ++g) {
-                        dn[g] = scale_of(Rn, g);
-                        nodn[g] = dn[g] * OFS;
-                    }
+                for (int g = 0; g < FN; ++g) {
+                    dn[g] = scale_of(Rn, g);
+                    nodn[g] = dn[g] * OFS;
                 }
-                an[f][pr] = deq_pair(Rn, f, 0, pr, dn[f], nodn[f]);
             }
+            const float dd = next ? dn[f] : d[f], no = next ? nodn[f] : nod[f];
+            if (fm == 0) asm volatile("s_nop 1");  // VALU-written fragments -> MFMA source
+            mfma_bf16_acc(acc[0][fm], a[0], bq[it % 3]);
+            if (BITS == 4 ? pr == 0 : (pr & 1) == 0) deq_src(Rs, f, ss, pr, slo, shi);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_bf16_acc(acc[1][fm], a[1], bq[it % 3]);
+            float c0, c1;
+            deq_cvt(slo, shi, pr, c0, c1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_bf16_acc(acc[2][fm], a[2], bq[it % 3]);
+            const float w0 = __builtin_fmaf(c0, dd, no), w1 = __builtin_fmaf(c1, dd, no);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_bf16_acc(acc[3][fm], a[3], bq[it % 3]);
+            an[f][pr] = pack_bf16x2(w0, w1);
+            if (it + 2 < 4 * FM) bq[(it + 2) % 3] = tok(buf, it + 2);
             if (fm == FM - 1) {
 #pragma unroll
                 for (int g = 0; g < FN; ++g) a[g] = an[g];
@@ -309,26 +352,25 @@ wo_gemm_kernel(WoKArgs p) {
         }
     };
 
-    // prologue: stage 0's loads, then its step-0 weight fragments.  R1 starts cleared: the last
-    // stage forms (unused) next-stage fragments from whichever set it does not own.
-#pragma unroll
-    for (int f = 0; f < FN; ++f) {
-#pragma unroll
-        for (int c = 0; c < Regs::NC; ++c) R1.c[f][c] = v4u{0u, 0u, 0u, 0u};
-        R1.s[f] = 0u;
-    }
-    wload(R0, 0);
+    // prologue: the codes of stages 0 and 1 around stage 0's LDS-DMAs (the order the stage waits
+    // assume), then stage 0's step-0 weight fragments
+    wload(S0, 0);
     dma_stage(0, 0);
+    wload(S1, 1);
+    fence(S0);
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
-        const float d0 = scale_of(R0, f), n0d = d0 * OFS;
+        const float d0 = scale_of(S0, f), n0d = d0 * OFS;
 #pragma unroll
-        for (int pr = 0; pr < 4; ++pr) a[f][pr] = deq_pair(R0, f, 0, pr, d0, n0d);
+        for (int pr = 0; pr < 4; ++pr) a[f][pr] = deq_pair(S0, f, 0, pr, d0, n0d);
     }
-    for (int j = 0; j < nk; j += 2) {
-        stage(j, R0, R1, 0);
-        stage(j + 1, R1, R0, 1);
+    for (int j = 0; j < nk; j += 4) {
+        stage(j, S0, S1, S2, 0);
+        stage(j + 1, S1, S2, S3, 1);
+        stage(j + 2, S2, S3, S0, 0);
+        stage(j + 3, S3, S0, S1, 1);
     }
+    wait_vmcnt<0>();  // the clamped LDS-DMAs of the last stage land before the workgroup ends
     mfma_drain();
 
     // ---------------------------------------------------------------- epilogue

@@ -125,17 +125,17 @@ def test_weight_only_validation():
     assert q(A(), 0, 64, 64, 8, A(0x200000), A(0x300000), None) == qdt.QDT_OK
     f = qdt.qdt_wo_linear
 
-    def lin(M=64, N=128, K=256, bits=4, epi=0, Y=0x900000, ldy=None, ldx=None, wd=0x400000, ws=None, wsb=0):
+    def lin(M=64, N=128, K=512, bits=4, epi=0, Y=0x900000, ldy=None, ldx=None, wd=0x400000, ws=None, wsb=0):
         return f(A(0x100000), K if ldx is None else ldx, A(0x300000), A(wd), bits, None, M, N, K, epi, A(Y),
                  N if ldy is None else ldy, None if ws is None else A(ws), wsb, None)
     assert lin(bits=6) == qdt.QDT_EINVAL
     assert lin(epi=1) == qdt.QDT_EINVAL                 # bias or fp32 accumulators only
     assert lin(epi=3) == qdt.QDT_EINVAL
-    assert lin(K=128) == qdt.QDT_ESHAPE                 # stages in pairs: K % 256
+    assert lin(K=256) == qdt.QDT_ESHAPE                 # stages in fours: K % 512
     assert lin(N=120) == qdt.QDT_ESHAPE
-    assert lin(ldx=128) == qdt.QDT_ESHAPE
+    assert lin(ldx=256) == qdt.QDT_ESHAPE
     assert lin(ldy=64) == qdt.QDT_ESHAPE
-    assert lin(ldx=260) == qdt.QDT_EALIGN
+    assert lin(ldx=516) == qdt.QDT_EALIGN
     assert lin(wd=0x400001) == qdt.QDT_EALIGN
     assert lin(Y=0x300000 + 64) == qdt.QDT_EALIAS        # Y over Wq
     assert lin(M=0) == qdt.QDT_OK
@@ -144,7 +144,7 @@ def test_weight_only_validation():
     assert {p["split_k"] for p in plans} == {7} and all(p["tile_m"] == 256 for p in plans)
     assert plans[1]["workspace_bytes"] == 7 * 512 * 4608 * 4 and plans[1]["grid"] == 2 * 18 * 7
     assert qdt.wo_linear_plan(300, 4608, 8192)["split_k"] == 1
-    assert qdt.wo_linear_plan(300, 4608, 8448)["split_k"] == 2
+    assert qdt.wo_linear_plan(300, 4608, 8704)["split_k"] == 2
     big = 0x10000000000
     assert f(A(big), 53248, A(2 * big), A(3 * big), 4, None, 512, 4608, 53248, 0, A(5 * big), 4608, None, 0,
              None) == qdt.QDT_EWORKSPACE

@@ -89,7 +89,7 @@ def exact_weights(N, K, bits, rng):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("M,N,K", [(1, 16, 256), (300, 272, 1024), (64, 256, 16384), (37, 48, 8448)])
+@pytest.mark.parametrize("M,N,K", [(1, 16, 512), (300, 272, 1024), (64, 256, 16384), (37, 48, 8704)])
 def test_wo_linear_exact_sums(bits, M, N, K):
     """X in {-1, 0, 1} / 4 and w~ = q 2^-6: every partial sum is a multiple of 2^-8 below 2^15,
     exact in fp32 in any order, so accumulators and bias outputs are bit-exact (ragged M and N
@@ -163,7 +163,7 @@ def test_wo_text_projection_shape_and_batch_invariance(bits):
 def test_wo_batch_invariance(bits):
     """A row's output is the same bits whatever the row count, the other rows and the row's
     position; also with a row stride ldx > K whose padding holds NaN."""
-    M, N, K = 700, 528, 16640
+    M, N, K = 700, 528, 16896
     announce(f"wo_linear batch invariance bits={bits} M={M} N={N} K={K}")
     rng = np.random.default_rng(740 + bits)
     d = W.make_linear(M, N, K, seed=741 + bits, x_kind="pct1", w_sigma=0.015, bias=True)

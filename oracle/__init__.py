@@ -61,6 +61,7 @@ def lib():
             "oracle_f16_to_f64": ([C.c_uint16], C.c_double),
             "oracle_wo_quantize": ([P, I64, I64, I64, I, P, P], None),
             "oracle_wo_dequantize": ([P, P, I64, I64, I, P], None),
+            "oracle_attention_rows": ([P, P, P, I64, I64, I64, P, I64, P, P], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -304,3 +305,16 @@ def wo_dequantize(Q, D, bits: int) -> np.ndarray:
 def wo_linear_rows(X, Q, D, bits: int, bias=None, rows=None, want_f32=False):
     """The weight-only linear: the bf16 GEMM of X with the dequantized weights (plus bias)."""
     return bf16_gemm_rows(X, wo_dequantize(Q, D, bits), bias, rows, want_f32)
+
+
+def attention_rows(Q, K, V, h: int, rows=None, want_f64=False):
+    """Head h of softmax(Q K^T / 16) V for the listed query rows: bf16 [n, 256] (and fp64 values).
+    Q, K, V: bf16 bits [S, ld] with head h in columns 256 h .. 256 h + 255."""
+    Q, K, V = _c(Q, np.uint16), _c(K, np.uint16), _c(V, np.uint16)
+    S, ld = Q.shape
+    r = None if rows is None else _c(rows, np.int64)
+    n = S if r is None else r.size
+    O = np.empty((n, 256), np.uint16)
+    A = np.empty((n, 256), np.float64) if want_f64 else None
+    lib().oracle_attention_rows(_p(Q), _p(K), _p(V), S, ld, h, _p(r), n, _p(O), _p(A))
+    return (O, A) if want_f64 else O

@@ -759,3 +759,89 @@ def test_wo_linear_exact_against_integer_matmul(bits):
     assert np.array_equal(Z, bf(want.astype(np.float32)))
     rows = np.array([4, 1])
     assert np.array_equal(oracle.wo_linear_rows(X, Q, D, bits, bias, rows), Z[rows])
+
+
+# ---------------------------------------------------------------- attention
+def _attn_inputs(S, H, ld, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    mk = lambda: bf(rng.standard_normal((S, ld)) * scale)
+    return mk(), mk(), mk()
+
+
+@pytest.mark.parametrize("h", [0, 2])
+def test_attention_matches_library_softmax(h):
+    """Against scipy's softmax on the same fp64 inputs; heads are column blocks of 256 inside ld."""
+    from scipy.special import softmax
+    S, H, ld = 96, 3, 3 * 256 + 8
+    Q, K, V = _attn_inputs(S, H, ld, 50 + h, 1.5)
+    rows = np.array([0, 5, 95, 40])
+    O, A = oracle.attention_rows(Q, K, V, h, rows, want_f64=True)
+    c = slice(256 * h, 256 * h + 256)
+    q, k, v = (f32(T)[:, c].astype(np.float64) for T in (Q, K, V))
+    ref = softmax(q[rows] @ k.T / 16.0, axis=1) @ v
+    assert np.allclose(A, ref, rtol=1e-12, atol=1e-14)
+    assert np.array_equal(O, bf(ref.astype(np.float32)))
+
+
+def test_attention_uniform_scores_give_the_mean_of_v():
+    """Zero queries score every key alike: the output is the plain mean of V, exact here."""
+    S, ld = 64, 256
+    rng = np.random.default_rng(52)
+    Q = np.zeros((S, ld), np.uint16)
+    K = bf(rng.standard_normal((S, ld)))
+    vi = rng.integers(-8, 9, (S, ld))
+    V = bf(vi * 0.25)
+    O = oracle.attention_rows(Q, K, V, 0, np.array([0, 63]))
+    want = bf((vi.sum(axis=0) * 0.25 / S).astype(np.float32))
+    assert np.array_equal(O[0], want) and np.array_equal(O[1], want)
+
+
+def test_attention_dominant_key_selects_its_value_row():
+    """A key far ahead of the others (score gap 60) takes all the weight: the output is its V row."""
+    S, ld = 48, 256
+    rng = np.random.default_rng(53)
+    Q = np.zeros((S, ld), np.float32)
+    K = np.zeros((S, ld), np.float32)
+    Q[:, 0] = 1.0
+    K[:, 0] = rng.uniform(-1, 1, S)
+    K[17, 0] = 960.0                      # score 60 above the rest
+    V = bf(rng.standard_normal((S, ld)))
+    O = oracle.attention_rows(bf(Q), bf(K), V, 0, np.array([3, 30]))
+    assert np.array_equal(O[0], V[17]) and np.array_equal(O[1], V[17])
+
+
+def test_attention_large_scores_stay_finite():
+    """Scores around 4096 overflow exp unless the true row max is subtracted; with it the result
+    is finite and equals the run with all scores shifted down by the same amount."""
+    S, ld = 32, 256
+    rng = np.random.default_rng(54)
+    Q = np.zeros((S, ld), np.float32)
+    K = np.zeros((S, ld), np.float32)
+    Q[:, 0] = 64.0
+    Q[:, 1] = 1.0
+    K[:, 0] = 1024.0                      # scores 4096 + K[:, 1] / 16 ...
+    K[:, 1] = rng.integers(-16, 17, S)
+    K[0, 0] = 0.0                         # ... except key 0, 4096 below them (first is not the max)
+    V = bf(rng.standard_normal((S, ld)))
+    _, A = oracle.attention_rows(bf(Q), bf(K), V, 0, np.array([0]), want_f64=True)
+    K2 = K.copy()
+    K2[:, 0] = 0.0
+    K2[0, 0] = -1024.0
+    _, A2 = oracle.attention_rows(bf(Q), bf(K2), V, 0, np.array([0]), want_f64=True)
+    assert np.all(np.isfinite(A)) and np.allclose(A, A2, rtol=1e-12, atol=1e-15)
+
+
+def test_attention_key_permutation_and_other_heads():
+    """Permuting keys with their values leaves the output (within fp64 rounding); the other
+    heads' columns are never read."""
+    S, ld = 80, 512
+    Q, K, V = _attn_inputs(S, 2, ld, 55)
+    perm = np.random.default_rng(56).permutation(S)
+    _, A = oracle.attention_rows(Q, K, V, 1, np.array([7]), want_f64=True)
+    _, Ap = oracle.attention_rows(Q, K[perm], V[perm], 1, np.array([7]), want_f64=True)
+    assert np.allclose(A, Ap, rtol=1e-13, atol=1e-15)
+    Q2, K2, V2 = Q.copy(), K.copy(), V.copy()
+    for T in (Q2, K2, V2):
+        T[:, :256] = 0x7FC0              # NaN in head 0
+    _, A2 = oracle.attention_rows(Q2, K2, V2, 1, np.array([7]), want_f64=True)
+    assert np.array_equal(A, A2)

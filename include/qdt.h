@@ -317,6 +317,30 @@ qdt_status qdt_w8a8_linear_planned(const int8_t* Xq, const float* x_scale, const
 qdt_status qdt_bf16_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, int64_t M, int64_t N,
                            int64_t K, uint16_t* Y, int64_t ldy, void* stream);
 
+/*
+ * Softmax attention per head after the QK-norm projection ([FAL]: 256-wide attention heads over the
+ * DiT's joint sequence of text and image tokens).  For every head h and query row m:
+ *   s_j = (Q[m] . K[j]) / 16 over the head's 256 columns (1/16 = 1/sqrt(256)), all S keys, no mask;
+ *   O[m] = sum_j p_j V[j] / sum_j p_j with p_j = exp(s_j - max_j s_j), rounded to bf16.
+ *   Q, K, V, O: bf16 [S, ld] / [S, ldo], head h in columns 256 h .. 256 h + 255 (the layout the
+ *   projections write).  Computed with fp32 scores, base-2 exponentials and bf16 probabilities in
+ *   the second product, like any bf16 flash-attention kernel, so the result is within a
+ *   first-order error bound of the exact one: 2^-9 (bf16 probabilities) plus the fp32 error of the
+ *   scores and of the two sums over S keys, times sum_j p_j |V[j]| / sum_j p_j, plus one bf16 ulp.
+ *   Each query row is computed independently of the other rows.
+ *   ld, ldo >= 256 H, both % 8 == 0; pointers 16-byte aligned; 1 <= H <= 1024, S <= QDT_ATTN_MAX_S.
+ *   `workspace`: caller-owned device memory of qdt_attention_workspace_size bytes (V transposed per
+ *   head, 16-byte aligned); no output may overlap an input or the workspace.  S = 0 is a no-op.
+ */
+#define QDT_ATTN_HEAD_DIM 256
+#define QDT_ATTN_MAX_S (1 << 22)
+qdt_status qdt_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int64_t S, int64_t H, int64_t ld,
+                         uint16_t* O, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace qdt_attention needs: H * 256 * roundup(S, 32) * 2 for V transposed, plus one int
+ * per 256-query block and head (padded to 16 bytes).  Pure host computation. */
+qdt_status qdt_attention_workspace_size(int64_t S, int64_t H, size_t* bytes);
+
 #ifdef __cplusplus
 }
 #endif

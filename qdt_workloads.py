@@ -32,6 +32,7 @@ import numpy as np
 # tensor ids for SeedSequence([seed, tensor_id])
 _TID_X, _TID_W, _TID_BIAS, _TID_GAMMA, _TID_WDOWN, _TID_OUTCH, _TID_OUTF = 1, 2, 3, 4, 5, 6, 7
 _TID_SHIFT, _TID_SCALE = 8, 9
+_TID_Q, _TID_K, _TID_V, _TID_GQ, _TID_GK = 10, 11, 12, 13, 14
 
 BASE_SEED = 1000  # the fixed generation seed of the INT8/GGUF quantization paper's setup
 
@@ -194,3 +195,16 @@ def make_adaln(M: int, K: int, seed: int = BASE_SEED + 1, x_kind: str = "pct1", 
     return dict(M=M, K=K, seed=seed, X=activations(M, K, seed, x_kind),
                 shift=vector(K, seed, _TID_SHIFT, shift_sigma), scale=vector(K, seed, _TID_SCALE, scale_sigma),
                 W=weights(K, K, seed, w_sigma))
+
+
+def make_attention(S: int, H: int, seed: int = BASE_SEED + 4) -> dict:
+    """Inputs of the attention after the QK-norm projection: Q and K as that projection's head
+    RMSNorm leaves them (unit mean square per head, times a per-dimension gain gamma ~ N(1, 0.1)
+    shared by all heads: a synthetic choice, the pages print no weights), V ~ N(0, 1), all bf16
+    [S, 256 H] token-major, head h in columns 256 h .. 256 h + 255."""
+    gq = np.tile(1.0 + 0.1 * rng_for(seed, _TID_GQ).standard_normal(256, dtype=np.float32), H).astype(np.float32)
+    gk = np.tile(1.0 + 0.1 * rng_for(seed, _TID_GK).standard_normal(256, dtype=np.float32), H).astype(np.float32)
+    return dict(S=S, H=H, seed=seed,
+                Q=_normal_bf16(rng_for(seed, _TID_Q), (S, 256 * H), 1.0, col_factor=gq),
+                K=_normal_bf16(rng_for(seed, _TID_K), (S, 256 * H), 1.0, col_factor=gk),
+                V=_normal_bf16(rng_for(seed, _TID_V), (S, 256 * H), 1.0))

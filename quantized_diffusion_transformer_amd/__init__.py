@@ -62,6 +62,8 @@ _SIGS = {
     "qdt_wo_quantize": ([_P, _I64, _I64, _I64, _I, _P, _P, _P], _I),
     "qdt_wo_linear": ([_P, _I64, _P, _P, _I, _P, _I64, _I64, _I64, _I, _P, _I64, _P, _SZ, _P], _I),
     "qdt_wo_linear_plan": ([_I64, _I64, _I64, C.POINTER(qdt_linear_plan)], _I),
+    "qdt_attention": ([_P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _SZ, _P], _I),
+    "qdt_attention_workspace_size": ([_I64, _I64, C.POINTER(_SZ)], _I),
     "qdt_w8a8_linear_plan": ([_I64, _I64, _I64, _I, C.POINTER(qdt_linear_plan)], _I),
     "qdt_w8a8_linear_plan_for": ([_I64, _I64, _I64, _I, C.c_int32, C.c_int32, C.POINTER(qdt_linear_plan)], _I),
     "qdt_w8a8_linear_workspace_size": ([_I64, _I64, _I64, _I, C.POINTER(_SZ)], _I),
@@ -318,6 +320,40 @@ def wo_linear(X: torch.Tensor, Wq: torch.Tensor, Wd: torch.Tensor, bias: torch.T
     _check(qdt_wo_linear(_ptr(X), ldx, _ptr(Wq), _ptr(Wd), bits, _ptr(bias), M, N, K, epi, _ptr(out), ldy,
                          _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
                          _stream(stream)), "qdt_wo_linear")
+    return out
+
+QDT_ATTN_HEAD_DIM = 256
+
+
+def attention_workspace_size(S: int, H: int) -> int:
+    n = _SZ(0)
+    _check(qdt_attention_workspace_size(S, H, C.byref(n)), "qdt_attention_workspace_size")
+    return n.value
+
+
+def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, heads: int, out=None, workspace=None,
+              stream=None) -> torch.Tensor:
+    """Softmax attention per 256-wide head: bf16 [S, 256 heads] = softmax(Q K^T / 16) V, head h in
+    columns 256 h .. 256 h + 255.  Q, K, V: bf16 [S, ld] views with one common row stride (for
+    example three column blocks of one fused projection output)."""
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _dev(t, torch.bfloat16, n)
+    Q, ld = _rows(Q, "Q")
+    K, ldk = _rows(K, "K")
+    V, ldv = _rows(V, "V")
+    if not (ld == ldk == ldv) or K.shape != Q.shape or V.shape != Q.shape:
+        raise ValueError("attention: Q, K, V must have the same shape and row stride")
+    S = Q.shape[0]
+    if Q.shape[1] < heads * QDT_ATTN_HEAD_DIM:
+        raise ValueError("attention: fewer than 256 * heads columns")
+    if out is None:
+        out = torch.empty((S, heads * QDT_ATTN_HEAD_DIM), dtype=torch.bfloat16, device=Q.device)
+    out, ldo = _rows(out, "out")
+    need = attention_workspace_size(S, heads)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Q.device)
+    _check(qdt_attention(_ptr(Q), _ptr(K), _ptr(V), S, heads, ld, _ptr(out), ldo, _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(stream)), "qdt_attention")
     return out
 
 def linear_plan(M: int, N: int, K: int, epilogue: str = "bias", tile: int | None = None,

@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqdt.so")
-SOURCES = ["qdt_abi.hip", "qdt_quant.hip", "qdt_gemm.hip", "qdt_wo.hip"]
+SOURCES = ["qdt_abi.hip", "qdt_quant.hip", "qdt_gemm.hip", "qdt_wo.hip", "qdt_attn.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

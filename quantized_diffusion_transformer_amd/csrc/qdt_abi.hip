@@ -537,4 +537,37 @@ qdt_status qdt_wo_linear(const uint16_t* X, int64_t ldx, const uint8_t* Wq, cons
     return hip_status(launch_splitk_f32_epilogue(a, p.split_k, e, st));
 }
 
+// Workspace: V^T per head (keys padded to a multiple of 32), then one int per workgroup.
+static int64_t attn_vt_bytes(int64_t S, int64_t H) { return H * QDT_ATTN_HEAD_DIM * ((S + 31) / 32 * 32) * 2; }
+static int64_t attn_ws_bytes(int64_t S, int64_t H) { return attn_vt_bytes(S, H) + ((S + 255) / 256 * H + 3) / 4 * 16; }
+
+qdt_status qdt_attention_workspace_size(int64_t S, int64_t H, size_t* bytes) {
+    if (!bytes) return QDT_EINVAL;
+    if (S < 0 || S > QDT_ATTN_MAX_S || H <= 0 || H > 1024) return QDT_ESHAPE;
+    *bytes = (size_t)attn_ws_bytes(S, H);
+    return QDT_OK;
+}
+
+qdt_status qdt_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int64_t S, int64_t H, int64_t ld,
+                         uint16_t* O, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream) {
+    if (S < 0 || S > QDT_ATTN_MAX_S || H <= 0 || H > 1024) return QDT_ESHAPE;
+    if (ld < H * QDT_ATTN_HEAD_DIM || ldo < H * QDT_ATTN_HEAD_DIM) return QDT_ESHAPE;
+    if (S == 0) return QDT_OK;
+    if (!Q || !K || !V || !O) return QDT_EINVAL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || ld % 8 != 0 || ldo % 8 != 0)
+        return QDT_EALIGN;
+    const int64_t wsb = attn_ws_bytes(S, H);
+    if (!workspace || (int64_t)workspace_bytes < wsb) return QDT_EWORKSPACE;
+    if (!aligned16(workspace)) return QDT_EALIGN;
+    const int64_t inb = ((S - 1) * ld + H * QDT_ATTN_HEAD_DIM) * 2, ob = ((S - 1) * ldo + H * QDT_ATTN_HEAD_DIM) * 2;
+    const void* ins[3] = {Q, K, V};
+    for (int i = 0; i < 3; ++i)
+        if (overlap(O, ob, ins[i], inb) || overlap(workspace, wsb, ins[i], inb)) return QDT_EALIAS;
+    if (overlap(O, ob, workspace, wsb)) return QDT_EALIAS;
+    uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+    return hip_status(launch_attention(Q, K, V, (int)S, (int)H, ld, O, ldo, reinterpret_cast<uint16_t*>(ws),
+                                       reinterpret_cast<int*>(ws + attn_vt_bytes(S, H)),
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,0 +1,337 @@
+// Softmax attention per 256-wide head, after the QK-norm projection.
+//
+// Method: "Serving sub-second Ideogram v4 without quality loss" (the DiT's attention heads are 256
+// wide; the attention runs over the joint sequence of text and image tokens).  Per head h:
+// O = softmax(Q K^T / 16) V over all S tokens (no mask; 1/16 = 1/sqrt(256)).  Q, K, V and O are
+// token-major [S, ld] with head h in columns 256 h .. 256 h + 255, as the projections write them.
+//
+// Design (gfx950):
+//   * One workgroup of 4 waves takes 256 queries of one head; each wave holds 64 queries' Q in
+//     registers (the B operand of the score MFMAs) and their 64 x 256 output accumulators in the
+//     256 AGPRs.  Keys stream through LDS in tiles of 32 (K rows and the matching V^T rows, double
+//     buffered by LDS-DMA), so each K or V element read from LDS feeds 64 queries' MFMAs.
+//   * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16): a lane then holds
+//     8 keys of one query per 16-query fragment, so the row max and the row sum are mostly
+//     lane-local (two cross-lane steps for the max, one reduction at the very end for the sum).
+//     The probabilities come out of that MFMA already in the B-operand layout of O^T += V^T P^T
+//     when V^T stores each 32-key group in the order [4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3]
+//     for lane group g = 0..3: the transpose pre-pass writes V^T that way.
+//   * Softmax in base 2 against a fixed per-query reference: the max of the first key tile.  The
+//     accumulators are never rescaled (rescaling the 256 AGPR accumulators inside the loop costs
+//     more VALU than the MFMAs it feeds, and any conditional update of them makes the compiler
+//     spill the query registers).  Later keys may exceed the reference: their probabilities are
+//     2^((s - m) C) > 1, which bf16 (fp32's exponent range) and the fp32 sums hold up to 2^64.  A
+//     workgroup in which any score passes the reference by more than 64 in log2 units raises a
+//     flag; a second launch of the kernel (EXACT) recomputes exactly those workgroups with the
+//     exact row max from a first pass over the keys, and returns at once everywhere else.
+//   * Probabilities enter the second MFMA as bf16 (as in every bf16 flash-attention kernel); the
+//     row sums use the fp32 values.
+#include "qdt_device.h"
+#include "qdt_internal.h"
+#include "qdt_lds.h"
+
+namespace qdt {
+
+constexpr int AT_D = 256;   // head width
+constexpr int AT_BQ = 256;  // queries per workgroup (64 per wave)
+constexpr int AT_BK = 32;   // keys per tile
+
+// Key (0..31) stored at position p of a 32-key group of V^T.
+__device__ __forceinline__ int vt_key_of_pos(int p) {
+    return 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3);
+}
+
+// ---------------------------------------------------------------------------- V -> V^T
+// Block (64-key block kb, head h): V rows kb*64 .. +63 of head h into LDS, then each thread writes
+// one dim row of V^T: 64 keys in the permuted order, zeros past S.
+__global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* __restrict__ V, int64_t ld, int S, int Spad,
+                                                      uint16_t* __restrict__ Vt, int* __restrict__ redo, int nredo) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64][AT_D];
+    const int kb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    if (kb == 0 && h == 0)
+        for (int i = tid; i < nredo; i += 256) redo[i] = 0;
+    const int k0 = kb * 64;
+    for (int c = tid; c < 64 * (AT_D / 8); c += 256) {
+        const int r = c / (AT_D / 8), ch = c % (AT_D / 8);
+        const int key = k0 + r;
+        v4u v = {0u, 0u, 0u, 0u};
+        if (key < S) v = *reinterpret_cast<const v4u*>(V + (int64_t)key * ld + h * AT_D + ch * 8);
+        *reinterpret_cast<v4u*>(&tile[r][ch * 8]) = v;
+    }
+    __syncthreads();
+    const int d = tid;
+    uint16_t* dst = Vt + ((int64_t)h * AT_D + d) * Spad + k0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int grp = q / 4;
+        if (k0 + 32 * grp >= Spad) break;
+        v4u o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int p0 = (q % 4) * 8 + 2 * e;
+            const uint32_t lo = tile[32 * grp + vt_key_of_pos(p0)][d];
+            const uint32_t hi = tile[32 * grp + vt_key_of_pos(p0 + 1)][d];
+            o[e] = lo | (hi << 16);
+        }
+        *reinterpret_cast<v4u*>(dst + q * 8) = o;
+    }
+}
+
+// ---------------------------------------------------------------------------- attention
+struct AttnArgs {
+    const uint16_t* Q;
+    const uint16_t* K;
+    const uint16_t* Vt;
+    uint16_t* O;
+    int* redo;  // per workgroup: scores outgrew the reference (cleared by the V^T pass)
+    int64_t ld, ldo;
+    int S, Spad, H, tiles_q;
+};
+
+// Output MFMA with the accumulator tuple tied in place in AGPRs (all 256 AGPRs hold accumulators).
+__device__ __forceinline__ void mfma_o(v4f& c, const v4u& a, const v4u& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ v4f mfma_s(const v4u& a, const v4u& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0,
+                                                   0);
+}
+// Row r mod 16 with its 2-bit halves swapped (K tile swizzle).
+__device__ __forceinline__ int at_rot4(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+template <bool EXACT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
+attn_fwd_kernel(AttnArgs p) {
+    constexpr int KROW = AT_D * 2;           // LDS bytes per key row
+    constexpr int KT = AT_BK * KROW;         // 16 KiB K tile
+    constexpr int VROW = AT_BK * 2;          // LDS bytes per V^T dim row
+    constexpr int VT = AT_D * VROW;          // 16 KiB V^T tile
+    constexpr int STG = KT + VT;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STG];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bid = blockIdx.x, nb = gridDim.x;
+    const int xcd = bid % kNumXCD, per = nb / kNumXCD, rem = nb % kNumXCD;
+    const int t = xcd * per + min(xcd, rem) + bid / kNumXCD;  // contiguous per XCD: one head's tiles
+    const int h = t / p.tiles_q, qt = t % p.tiles_q;
+    const int q0 = qt * AT_BQ + 64 * wave;  // the wave's first query
+    const int nkt = p.Spad / AT_BK;
+    if constexpr (EXACT) {
+        if (__builtin_amdgcn_readfirstlane(p.redo[t]) == 0) return;
+    }
+
+    // ---- Q fragments (B operand of S^T = K Q^T): lane holds query 16 qf + (lane & 15) of the wave,
+    // dims 32 kk + 8 (lane >> 4) .. + 7.  Queries past S are clamped (their outputs are not stored).
+    v4u qfr[4][8];
+#pragma unroll
+    for (int qf = 0; qf < 4; ++qf) {
+        const int qr = min(q0 + 16 * qf + (lane & 15), p.S - 1);
+        const uint16_t* src = p.Q + (int64_t)qr * p.ld + h * AT_D + 8 * (lane >> 4);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) qfr[qf][kk] = *reinterpret_cast<const v4u*>(src + 32 * kk);
+    }
+
+    // ---- LDS-DMA of a tile: 16 instructions for K (2 key rows each), 16 for V^T (16 dim rows of
+    // 64 bytes each); wave w issues 4 of each.  K row r sits in LDS with its 16-byte chunk c in
+    // slot c ^ rot4(r), which keeps each fragment read free of bank conflicts.  Keys past S are
+    // clamped to the last key (their scores are masked).
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.K + h * AT_D);
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.Vt + (int64_t)h * AT_D * p.Spad);
+    const uint32_t ldsk = __builtin_amdgcn_readfirstlane(lds_offset(smem) + wave * 4 * 1024);
+    const uint32_t ldsv = ldsk + KT;
+    // The per-lane offsets are recomputed at every tile from an index the optimizer cannot see
+    // through: held across the loop they would take registers the query fragments need.
+    auto dma = [&](int buf, int jt, bool with_v) __attribute__((always_inline)) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int key0 = jt * AT_BK;
+        const uint8_t* kb = kbase + (int64_t)key0 * p.ld * 2;
+        const int lim = p.S - 1 - key0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 2 * (4 * wave + i) + (ln >> 5);
+            const uint32_t off = (uint32_t)(min(row, lim) * p.ld * 2) + (uint32_t)(((ln & 31) ^ at_rot4(row & 15)) * 16);
+            lds_dma16_s(ldsk + (uint32_t)(buf * STG + i * 1024), off, kb);
+        }
+        if (!with_v) return;
+        const uint8_t* vb = vbase + (int64_t)key0 * 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t off = (uint32_t)((16 * (4 * wave + i) + (ln >> 2)) * p.Spad * 2 + (ln & 3) * 16);
+            lds_dma16_s(ldsv + (uint32_t)(buf * STG + i * 1024), off, vb);
+        }
+    };
+    // K fragment (A operand): key 16 kf + (lane & 15) of the tile, dims 32 kk + 8 (lane >> 4) .. + 7
+    auto kfrag = [&](int buf, int kf, int kk) __attribute__((always_inline)) {
+        const int row = 16 * kf + (lane & 15);
+        const int slot = (4 * kk + (lane >> 4)) ^ at_rot4(lane & 15);
+        return *reinterpret_cast<const v4u*>(smem + buf * STG + row * KROW + slot * 16);
+    };
+    // V^T fragment (A operand): dim 16 df + (lane & 15), tile positions 8 (lane >> 4) .. + 7
+    auto vfrag = [&](int buf, int df) __attribute__((always_inline)) {
+        const int row = 16 * df + (lane & 15);
+        return *reinterpret_cast<const v4u*>(smem + buf * STG + KT + row * VROW + (lane >> 4) * 16);
+    };
+
+    // ---- scores of key tile jt: S^T = K Q^T, lane holds keys 16 kf + 4 (lane >> 4) + r of query
+    // 16 qf + (lane & 15); keys past S get -inf; mt = the tile's max per query (all lane groups)
+    v4f s[2][4];
+    float mt[4];
+    auto scores = [&](int buf, int jt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kf = 0; kf < 2; ++kf)
+#pragma unroll
+            for (int qf = 0; qf < 4; ++qf) s[kf][qf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kf = 0; kf < 2; ++kf)
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const v4u a = kfrag(buf, kf, kk);
+#pragma unroll
+                for (int qf = 0; qf < 4; ++qf) s[kf][qf] = mfma_s(a, qfr[qf][kk], s[kf][qf]);
+            }
+        if ((jt + 1) * AT_BK > p.S) {
+#pragma unroll
+            for (int kf = 0; kf < 2; ++kf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool out = jt * AT_BK + 16 * kf + 4 * (lane >> 4) + r >= p.S;
+#pragma unroll
+                    for (int qf = 0; qf < 4; ++qf)
+                        if (out) s[kf][qf][r] = -__builtin_inff();
+                }
+        }
+#pragma unroll
+        for (int qf = 0; qf < 4; ++qf) {
+            float m = fmaxf(fmaxf(fmaxf(s[0][qf][0], s[0][qf][1]), fmaxf(s[0][qf][2], s[0][qf][3])),
+                            fmaxf(fmaxf(s[1][qf][0], s[1][qf][1]), fmaxf(s[1][qf][2], s[1][qf][3])));
+            m = fmaxf(m, __shfl_xor(m, 16, 64));
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            mt[qf] = m;
+        }
+    };
+    constexpr float C = 1.44269504088896341f / 16.0f;  // log2(e) / sqrt(256)
+    constexpr float LIMIT = 64.0f / C;                  // largest excess over the reference, raw units
+
+    // reference max per query fragment (raw score units) and this lane's partial row sums
+    float mu[4], lp[4];
+#pragma unroll
+    for (int qf = 0; qf < 4; ++qf) {
+        mu[qf] = -__builtin_inff();
+        lp[qf] = 0.0f;
+    }
+    if constexpr (EXACT) {
+        // first pass over the keys: the exact row max
+        dma(0, 0, false);
+        for (int jt = 0; jt < nkt; ++jt) {
+            const int buf = jt & 1;
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (jt + 1 < nkt) dma(buf ^ 1, jt + 1, false);
+            scores(buf, jt);
+#pragma unroll
+            for (int qf = 0; qf < 4; ++qf) mu[qf] = fmaxf(mu[qf], mt[qf]);
+        }
+        __syncthreads();  // every wave is done with the LDS tiles before they are refilled
+    }
+
+    v4f oacc[16][4];
+#pragma unroll
+    for (int df = 0; df < 16; ++df)
+#pragma unroll
+        for (int qf = 0; qf < 4; ++qf) oacc[df][qf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    bool bad = false;
+
+    dma(0, 0, true);
+    for (int jt = 0; jt < nkt; ++jt) {
+        const int buf = jt & 1;
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (jt + 1 < nkt) dma(buf ^ 1, jt + 1, true);
+        scores(buf, jt);
+        if constexpr (!EXACT) {
+#pragma unroll
+            for (int qf = 0; qf < 4; ++qf) {
+                mu[qf] = jt == 0 ? mt[qf] : mu[qf];
+                bad |= mt[qf] > mu[qf] + LIMIT;
+            }
+        }
+        // ---- p = 2^((s - mu) C) in fp32 for the row sums, bf16 for the MFMA; B operand of
+        // O^T += V^T P^T: positions 8 g + 4 kf + r <- key 16 kf + 4 g + r
+        v4u pb[4];
+#pragma unroll
+        for (int qf = 0; qf < 4; ++qf) {
+            const float mc = mu[qf] * C;
+            float e[2][4];
+            float sum = 0.0f;
+#pragma unroll
+            for (int kf = 0; kf < 2; ++kf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    e[kf][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kf][qf][r], C, -mc));
+                    sum += e[kf][r];
+                }
+            lp[qf] += sum;
+            pb[qf] = v4u{pack_bf16x2(e[0][0], e[0][1]), pack_bf16x2(e[0][2], e[0][3]), pack_bf16x2(e[1][0], e[1][1]),
+                         pack_bf16x2(e[1][2], e[1][3])};
+        }
+        asm volatile("s_nop 1");  // VALU-written P -> MFMA source
+        // ---- O^T += V^T P^T: lane holds dims 16 df + 4 (lane >> 4) + r of query 16 qf + (lane & 15)
+#pragma unroll
+        for (int df = 0; df < 16; ++df) {
+            const v4u a = vfrag(buf, df);
+#pragma unroll
+            for (int qf = 0; qf < 4; ++qf) mfma_o(oacc[df][qf], a, pb[qf]);
+        }
+    }
+    if constexpr (!EXACT) {
+        if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) p.redo[t] = 1;
+    }
+    mfma_drain();
+
+    // ---- normalize by the full row sums and store 4 consecutive dims per lane
+#pragma unroll
+    for (int qf = 0; qf < 4; ++qf) {
+        float l = lp[qf];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        const float inv = 1.0f / l;
+        const int q = q0 + 16 * qf + (lane & 15);
+        if (q >= p.S) continue;
+        uint16_t* dst = p.O + (int64_t)q * p.ldo + h * AT_D + 4 * (lane >> 4);
+#pragma unroll
+        for (int df = 0; df < 16; ++df) {
+            const v4f v = oacc[df][qf];
+            *reinterpret_cast<uint2*>(dst + 16 * df) =
+                make_uint2(pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv));
+        }
+    }
+}
+
+hipError_t launch_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int S, int H, int64_t ld,
+                            uint16_t* O, int64_t ldo, uint16_t* Vt, int* redo, hipStream_t st) {
+    const int Spad = (S + AT_BK - 1) / AT_BK * AT_BK;
+    const int tiles_q = (S + AT_BQ - 1) / AT_BQ;
+    hipLaunchKernelGGL(attn_vt_kernel, dim3((Spad + 63) / 64, H), dim3(256), 0, st, V, ld, S, Spad, Vt, redo,
+                       tiles_q * H);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    AttnArgs a;
+    a.Q = Q;
+    a.K = K;
+    a.Vt = Vt;
+    a.O = O;
+    a.ld = ld;
+    a.ldo = ldo;
+    a.S = S;
+    a.Spad = Spad;
+    a.H = H;
+    a.tiles_q = tiles_q;
+    a.redo = redo;
+    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(tiles_q * H), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(tiles_q * H), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace qdt

@@ -72,6 +72,11 @@ hipError_t launch_wo_quant(const uint16_t* W, int64_t ldw, int64_t N, int64_t K,
 hipError_t launch_wo_gemm(const uint16_t* X, int64_t ldx, const uint8_t* Wq, const uint16_t* Wd, int bits,
                           const uint16_t* bias, int M, int N, int K, int epi, void* Y, int64_t ldy, float* ws,
                           const Plan& pl, hipStream_t st);
+// Softmax attention per 256-wide head: V^T (keys permuted within 32-key groups, zero-padded to a
+// multiple of 32 keys) into Vt, then O = softmax(Q K^T / 16) V for every head.
+// redo: one int per workgroup (cleared here) for the exact-max rerun.
+hipError_t launch_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int S, int H, int64_t ld,
+                            uint16_t* O, int64_t ldo, uint16_t* Vt, int* redo, hipStream_t st);
 // Sum of the S int32 partial slices followed by epilogue `epi` (BIAS, SILU, RMSNORM, ACC).
 hipError_t launch_splitk_epilogue(const GemmArgs& a, int split_k, int epi, hipStream_t st);
 // Sum of the S fp32 partial slices of the FP4 GEMM, then epilogue `epi` (F32BIAS, F32SILU,

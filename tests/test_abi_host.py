@@ -151,6 +151,24 @@ def test_weight_only_validation():
     assert f(A(big), 53248, A(2 * big), A(3 * big), 4, None, 512, 4608, 53248, 0, A(5 * big), 4608, A(6 * big),
              7 * 512 * 4608 * 4 - 16, None) == qdt.QDT_EWORKSPACE
 
+def test_attention_validation():
+    f = qdt.qdt_attention
+    n = qdt.attention_workspace_size(100, 2)
+    assert n == 2 * 256 * 128 * 2 + 16 and qdt.attention_workspace_size(256, 1) == 256 * 512 + 16
+
+    def att(S=100, H=2, ld=512, ldo=512, O=0x900000, ws=0x2000000, wsb=None, q=0x100000):
+        return f(A(q), A(0x300000), A(0x500000), S, H, ld, A(O), ldo, A(ws), n if wsb is None else wsb, None)
+    assert att(H=0) == qdt.QDT_ESHAPE
+    assert att(S=-1) == qdt.QDT_ESHAPE
+    assert att(ld=500) == qdt.QDT_ESHAPE                 # fewer than 256 H columns
+    assert att(ldo=256) == qdt.QDT_ESHAPE
+    assert att(ld=516) == qdt.QDT_EALIGN
+    assert att(q=0x100008) == qdt.QDT_EALIGN
+    assert att(wsb=n - 16) == qdt.QDT_EWORKSPACE
+    assert att(O=0x300000 + 1024) == qdt.QDT_EALIAS      # O over K
+    assert att(ws=0x500000 + 64) == qdt.QDT_EALIAS       # workspace over V
+    assert att(S=0) == qdt.QDT_OK
+
 def test_smooth_prepare_validation():
     f = qdt.qdt_smooth_prepare
     outs = (A(0x100000), A(0x200000), A(0x300000), A(0x400000))

@@ -300,7 +300,8 @@ EXTRA_WORKLOADS = ("dit_ffn_gate_up_4608x24576x4608", "text_cond_proj_512x4608x5
                    "qk_proj_headnorm_6037x4608x4608", "adaln_quantize_4608x4608", "adaln_quantize_16896x4608",
                    "mxfp4_attn_proj_4608x4608x4608", "mxfp4_ffn_gate_up_4608x24576x4608",
                    "mxfp4_qk_proj_headnorm_16896x4608x4608", "mxfp4_text_cond_proj_512x4608x53248",
-                   "wo4_text_cond_proj_512x4608x53248", "wo8_text_cond_proj_512x4608x53248")
+                   "wo4_text_cond_proj_512x4608x53248", "wo8_text_cond_proj_512x4608x53248",
+                   "attention_4608x18x256", "attention_16896x18x256")
 
 
 def extra_workloads(args, only=None):
@@ -422,8 +423,39 @@ def extra_workloads(args, only=None):
         name = f"wo{bits}_text_cond_proj_512x4608x53248"
         if want(name):
             res[name] = weight_only_workload(bits, counts)
+    for S in (4608, 16896):
+        name = f"attention_{S}x18x256"
+        if want(name):
+            res[name] = attention_workload(S, 18, counts)
     torch.cuda.empty_cache()
     return res
+
+
+def attention_workload(S, H, counts):
+    """Softmax attention after the QK-norm projection over the joint sequence of S tokens, H heads
+    of 256: per step one qdt_attention (V transpose pass, attention, exact-max check)."""
+    import torch
+
+    import qdt_workloads as W
+    import quantized_diffusion_transformer_amd as qdt
+    d = W.make_attention(S, H)
+    Q, K, V = to_dev(d["Q"]), to_dev(d["K"]), to_dev(d["V"])
+    ws = torch.empty(qdt.attention_workspace_size(S, H), dtype=torch.uint8, device="cuda")
+    O = torch.empty((S, 256 * H), dtype=torch.bfloat16, device="cuda")
+
+    def step(_, ev):
+        if ev is not None:
+            ev[0].record()
+        qdt.attention(Q, K, V, H, out=O, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+            ev[2].record()
+    steps, warm = counts(step)
+    ms, tl, _ = time_loop_best(step, steps, warm)
+    flops = 4.0 * S * S * 256 * H
+    return {"S": S, "H": H, "head_dim": 256, "steps": steps, "warmup": warm, "ms_per_step": round(ms, 4),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def weight_only_workload(bits, counts):

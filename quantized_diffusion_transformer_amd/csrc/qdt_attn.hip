@@ -92,12 +92,20 @@ struct AttnArgs {
 __device__ __forceinline__ void mfma_o(v4f& c, const v4u& a, const v4u& b) {
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ v4f mfma_s(const v4u& a, const v4u& b, const v4f& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0,
-                                                   0);
+// Score MFMA with its accumulator in VGPRs (the softmax reads it; the AGPRs are all taken by the
+// output).  Asm, so the kernel drains the MFMA pipeline itself before the scores are read.
+__device__ __forceinline__ void mfma_s(v4f& c, const v4u& a, const v4u& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
-// Row r mod 16 with its 2-bit halves swapped (K tile swizzle).
-__device__ __forceinline__ int at_rot4(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// LDS swizzles.  A fragment read touches 16 rows x 4 chunks of 16 bytes (64 lanes, 1 KiB); the
+// slot permutations below put those lanes on distinct 16-byte bank groups whether the LDS serves
+// 16, 32 or 64 lanes per pass.
+// K rows (512 bytes, 32 chunks): chunk c of row r in slot c ^ ksw(r mod 16), with
+// ksw(n) = 4 (n >> 1) + 2 (n & 1) + (n >> 3): its top three bits separate rows of one parity, its
+// low four bits are a permutation of n, and no two values differ by exactly 1.
+__device__ __forceinline__ int at_ksw(int n) { return 4 * (n >> 1) + 2 * (n & 1) + ((n >> 3) & 1); }
+// V^T rows (64 bytes, 4 chunks): chunk c of row r in slot c ^ ((r >> 2) & 3).
+__device__ __forceinline__ int at_vsw(int r) { return (r >> 2) & 3; }
 
 template <bool EXACT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
@@ -130,11 +138,18 @@ attn_fwd_kernel(AttnArgs p) {
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) qfr[qf][kk] = *reinterpret_cast<const v4u*>(src + 32 * kk);
     }
+    // the compiler's wait for these loads belongs here, before the first LDS-DMA: placed at their
+    // first use inside the loop it would also hold back every tile's prefetch (the asm LDS-DMAs
+    // count in the same load counter)
+#pragma unroll
+    for (int qf = 0; qf < 4; ++qf)
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+v"(qfr[qf][kk]));
 
     // ---- LDS-DMA of a tile: 16 instructions for K (2 key rows each), 16 for V^T (16 dim rows of
-    // 64 bytes each); wave w issues 4 of each.  K row r sits in LDS with its 16-byte chunk c in
-    // slot c ^ rot4(r), which keeps each fragment read free of bank conflicts.  Keys past S are
-    // clamped to the last key (their scores are masked).
+    // 64 bytes each); wave w issues 4 of each, each lane moving the global chunk that belongs in
+    // its LDS slot under the swizzles above.  Keys past S are clamped to the last key (their
+    // scores are masked).
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.K + h * AT_D);
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.Vt + (int64_t)h * AT_D * p.Spad);
     const uint32_t ldsk = __builtin_amdgcn_readfirstlane(lds_offset(smem) + wave * 4 * 1024);
@@ -150,27 +165,29 @@ attn_fwd_kernel(AttnArgs p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 2 * (4 * wave + i) + (ln >> 5);
-            const uint32_t off = (uint32_t)(min(row, lim) * p.ld * 2) + (uint32_t)(((ln & 31) ^ at_rot4(row & 15)) * 16);
+            const uint32_t off = (uint32_t)(min(row, lim) * p.ld * 2) + (uint32_t)(((ln & 31) ^ at_ksw(row & 15)) * 16);
             lds_dma16_s(ldsk + (uint32_t)(buf * STG + i * 1024), off, kb);
         }
         if (!with_v) return;
         const uint8_t* vb = vbase + (int64_t)key0 * 2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t off = (uint32_t)((16 * (4 * wave + i) + (ln >> 2)) * p.Spad * 2 + (ln & 3) * 16);
+            const int row = 16 * (4 * wave + i) + (ln >> 2);
+            const uint32_t off = (uint32_t)(row * p.Spad * 2 + (((ln & 3) ^ at_vsw(row)) * 16));
             lds_dma16_s(ldsv + (uint32_t)(buf * STG + i * 1024), off, vb);
         }
     };
     // K fragment (A operand): key 16 kf + (lane & 15) of the tile, dims 32 kk + 8 (lane >> 4) .. + 7
     auto kfrag = [&](int buf, int kf, int kk) __attribute__((always_inline)) {
         const int row = 16 * kf + (lane & 15);
-        const int slot = (4 * kk + (lane >> 4)) ^ at_rot4(lane & 15);
+        const int slot = (4 * kk + (lane >> 4)) ^ at_ksw(lane & 15);
         return *reinterpret_cast<const v4u*>(smem + buf * STG + row * KROW + slot * 16);
     };
     // V^T fragment (A operand): dim 16 df + (lane & 15), tile positions 8 (lane >> 4) .. + 7
     auto vfrag = [&](int buf, int df) __attribute__((always_inline)) {
         const int row = 16 * df + (lane & 15);
-        return *reinterpret_cast<const v4u*>(smem + buf * STG + KT + row * VROW + (lane >> 4) * 16);
+        return *reinterpret_cast<const v4u*>(smem + buf * STG + KT + row * VROW +
+                                             (((lane >> 4) ^ at_vsw(lane & 15)) * 16));
     };
 
     // ---- scores of key tile jt: S^T = K Q^T, lane holds keys 16 kf + 4 (lane >> 4) + r of query
@@ -182,14 +199,17 @@ attn_fwd_kernel(AttnArgs p) {
         for (int kf = 0; kf < 2; ++kf)
 #pragma unroll
             for (int qf = 0; qf < 4; ++qf) s[kf][qf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        // 16 K fragments, each read one group of 4 MFMAs ahead of its use
+        v4u a = kfrag(buf, 0, 0);
 #pragma unroll
-        for (int kf = 0; kf < 2; ++kf)
+        for (int g = 0; g < 16; ++g) {
+            const int kf = g / 8, kk = g % 8;
+            const v4u an = g + 1 < 16 ? kfrag(buf, (g + 1) / 8, (g + 1) % 8) : a;
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const v4u a = kfrag(buf, kf, kk);
-#pragma unroll
-                for (int qf = 0; qf < 4; ++qf) s[kf][qf] = mfma_s(a, qfr[qf][kk], s[kf][qf]);
-            }
+            for (int qf = 0; qf < 4; ++qf) mfma_s(s[kf][qf], a, qfr[qf][kk]);
+            a = an;
+        }
+        mfma_drain();
         if ((jt + 1) * AT_BK > p.S) {
 #pragma unroll
             for (int kf = 0; kf < 2; ++kf)
@@ -250,10 +270,10 @@ attn_fwd_kernel(AttnArgs p) {
         if (jt + 1 < nkt) dma(buf ^ 1, jt + 1, true);
         scores(buf, jt);
         if constexpr (!EXACT) {
+            if (jt == 0) {
+                // the reference: the first tile's max (a uniform branch that touches no accumulator)
 #pragma unroll
-            for (int qf = 0; qf < 4; ++qf) {
-                mu[qf] = jt == 0 ? mt[qf] : mu[qf];
-                bad |= mt[qf] > mu[qf] + LIMIT;
+                for (int qf = 0; qf < 4; ++qf) mu[qf] = mt[qf];
             }
         }
         // ---- p = 2^((s - mu) C) in fp32 for the row sums, bf16 for the MFMA; B operand of
@@ -275,13 +295,20 @@ attn_fwd_kernel(AttnArgs p) {
             pb[qf] = v4u{pack_bf16x2(e[0][0], e[0][1]), pack_bf16x2(e[0][2], e[0][3]), pack_bf16x2(e[1][0], e[1][1]),
                          pack_bf16x2(e[1][2], e[1][3])};
         }
+        if constexpr (!EXACT) {
+            // after the exponentials: p above does not wait for this tile's max
+#pragma unroll
+            for (int qf = 0; qf < 4; ++qf) bad |= mt[qf] > mu[qf] + LIMIT;
+        }
         asm volatile("s_nop 1");  // VALU-written P -> MFMA source
         // ---- O^T += V^T P^T: lane holds dims 16 df + 4 (lane >> 4) + r of query 16 qf + (lane & 15)
+        v4u va = vfrag(buf, 0);
 #pragma unroll
         for (int df = 0; df < 16; ++df) {
-            const v4u a = vfrag(buf, df);
+            const v4u vn = df + 1 < 16 ? vfrag(buf, df + 1) : va;
 #pragma unroll
-            for (int qf = 0; qf < 4; ++qf) mfma_o(oacc[df][qf], a, pb[qf]);
+            for (int qf = 0; qf < 4; ++qf) mfma_o(oacc[df][qf], va, pb[qf]);
+            va = vn;
         }
     }
     if constexpr (!EXACT) {

@@ -97,15 +97,14 @@ __device__ __forceinline__ void mfma_o(v4f& c, const v4u& a, const v4u& b) {
 __device__ __forceinline__ void mfma_s(v4f& c, const v4u& a, const v4u& b) {
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
-// LDS swizzles.  A fragment read touches 16 rows x 4 chunks of 16 bytes (64 lanes, 1 KiB); the
-// slot permutations below put those lanes on distinct 16-byte bank groups whether the LDS serves
-// 16, 32 or 64 lanes per pass.
-// K rows (512 bytes, 32 chunks): chunk c of row r in slot c ^ ksw(r mod 16), with
-// ksw(n) = 4 (n >> 1) + 2 (n & 1) + (n >> 3): its top three bits separate rows of one parity, its
-// low four bits are a permutation of n, and no two values differ by exactly 1.
-__device__ __forceinline__ int at_ksw(int n) { return 4 * (n >> 1) + 2 * (n & 1) + ((n >> 3) & 1); }
-// V^T rows (64 bytes, 4 chunks): chunk c of row r in slot c ^ ((r >> 2) & 3).
-__device__ __forceinline__ int at_vsw(int r) { return (r >> 2) & 3; }
+// LDS swizzles.  A fragment read touches 16 rows x 4 chunks of 16 bytes (64 lanes, 1 KiB).  The LDS
+// (64 banks of 4 bytes) serves a 16-byte read in four passes of 16 lanes: lanes 0-3, 12-15, 20-23
+// and 24-27 form one pass, the other passes are the same set XORed with 4, 32 and 36.  The slot
+// permutations below put each pass on 16 distinct 16-byte bank groups.
+// K rows (512 bytes, 32 chunks): chunk c of row r in slot c ^ (r mod 16).
+__device__ __forceinline__ int at_ksw(int n) { return n & 15; }
+// V^T rows (64 bytes, 4 chunks): chunk c of row r in slot c ^ (bit 3 of r, moved to bit 1).
+__device__ __forceinline__ int at_vsw(int r) { return (r >> 2) & 2; }
 
 template <bool EXACT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
@@ -156,7 +155,7 @@ attn_fwd_kernel(AttnArgs p) {
     const uint32_t ldsv = ldsk + KT;
     // The per-lane offsets are recomputed at every tile from an index the optimizer cannot see
     // through: held across the loop they would take registers the query fragments need.
-    auto dma = [&](int buf, int jt, bool with_v) __attribute__((always_inline)) {
+    auto dma_k = [&](int buf, int jt) __attribute__((always_inline)) {
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int key0 = jt * AT_BK;
@@ -168,7 +167,11 @@ attn_fwd_kernel(AttnArgs p) {
             const uint32_t off = (uint32_t)(min(row, lim) * p.ld * 2) + (uint32_t)(((ln & 31) ^ at_ksw(row & 15)) * 16);
             lds_dma16_s(ldsk + (uint32_t)(buf * STG + i * 1024), off, kb);
         }
-        if (!with_v) return;
+    };
+    auto dma_v = [&](int buf, int jt) __attribute__((always_inline)) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int key0 = jt * AT_BK;
         const uint8_t* vb = vbase + (int64_t)key0 * 2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -194,7 +197,7 @@ attn_fwd_kernel(AttnArgs p) {
     // 16 qf + (lane & 15); keys past S get -inf; mt = the tile's max per query (all lane groups)
     v4f s[2][4];
     float mt[4];
-    auto scores = [&](int buf, int jt) __attribute__((always_inline)) {
+    auto scores = [&](int buf, int jt, bool cross) __attribute__((always_inline)) {
 #pragma unroll
         for (int kf = 0; kf < 2; ++kf)
 #pragma unroll
@@ -225,8 +228,10 @@ attn_fwd_kernel(AttnArgs p) {
         for (int qf = 0; qf < 4; ++qf) {
             float m = fmaxf(fmaxf(fmaxf(s[0][qf][0], s[0][qf][1]), fmaxf(s[0][qf][2], s[0][qf][3])),
                             fmaxf(fmaxf(s[1][qf][0], s[1][qf][1]), fmaxf(s[1][qf][2], s[1][qf][3])));
-            m = fmaxf(m, __shfl_xor(m, 16, 64));
-            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            if (cross) {
+                m = fmaxf(m, __shfl_xor(m, 16, 64));
+                m = fmaxf(m, __shfl_xor(m, 32, 64));
+            }
             mt[qf] = m;
         }
     };
@@ -242,13 +247,13 @@ attn_fwd_kernel(AttnArgs p) {
     }
     if constexpr (EXACT) {
         // first pass over the keys: the exact row max
-        dma(0, 0, false);
+        dma_k(0, 0);
         for (int jt = 0; jt < nkt; ++jt) {
             const int buf = jt & 1;
             wait_vmcnt<0>();
             __syncthreads();
-            if (jt + 1 < nkt) dma(buf ^ 1, jt + 1, false);
-            scores(buf, jt);
+            if (jt + 1 < nkt) dma_k(buf ^ 1, jt + 1);
+            scores(buf, jt, true);
 #pragma unroll
             for (int qf = 0; qf < 4; ++qf) mu[qf] = fmaxf(mu[qf], mt[qf]);
         }
@@ -262,55 +267,79 @@ attn_fwd_kernel(AttnArgs p) {
         for (int qf = 0; qf < 4; ++qf) oacc[df][qf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     bool bad = false;
 
-    dma(0, 0, true);
-    for (int jt = 0; jt < nkt; ++jt) {
+    // ---- softmax of the scores in s against mu, in 4 parts per query fragment qf so that each part
+    // can follow one group of the previous tile's PV MFMAs: p = 2^((s - mu) C) in fp32 for the row
+    // sums, bf16 for the MFMA (B operand of O^T += V^T P^T: positions 8 g + 4 kf + r <- key
+    // 16 kf + 4 g + r).  Part 3 also raises the rerun flag from the lane's own scores.
+    float tt[8];
+    auto softmax_part = [&](int qf, int part, v4u (&pn)[4]) __attribute__((always_inline)) {
+        if (part == 0) {
+            const float mc = mu[qf] * C;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tt[e] = __builtin_fmaf(s[e / 4][qf][e % 4], C, -mc);
+        } else if (part == 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tt[e] = __builtin_amdgcn_exp2f(tt[e]);
+        } else if (part == 2) {
+#pragma unroll
+            for (int e = 4; e < 8; ++e) tt[e] = __builtin_amdgcn_exp2f(tt[e]);
+        } else {
+            lp[qf] += ((tt[0] + tt[1]) + (tt[2] + tt[3])) + ((tt[4] + tt[5]) + (tt[6] + tt[7]));
+            pn[qf] = v4u{pack_bf16x2(tt[0], tt[1]), pack_bf16x2(tt[2], tt[3]), pack_bf16x2(tt[4], tt[5]),
+                         pack_bf16x2(tt[6], tt[7])};
+            if constexpr (!EXACT) bad |= mt[qf] > mu[qf] + LIMIT;
+        }
+    };
+    // ---- O^T += V^T P^T for the tile in V^T buffer vbuf, with the softmax parts of the current
+    // scores after the groups (lane holds dims 16 df + 4 (lane >> 4) + r of query 16 qf + (lane & 15))
+    auto pv = [&](int vbuf, const v4u (&pp)[4], bool with_softmax, v4u (&pn)[4]) __attribute__((always_inline)) {
+        asm volatile("s_nop 1");  // VALU-written P -> MFMA source
+        v4u va = vfrag(vbuf, 0);
+#pragma unroll
+        for (int df = 0; df < 16; ++df) {
+            const v4u vn = df + 1 < 16 ? vfrag(vbuf, df + 1) : va;
+#pragma unroll
+            for (int qf = 0; qf < 4; ++qf) mfma_o(oacc[df][qf], va, pp[qf]);
+            if (with_softmax) softmax_part(df / 4, df % 4, pn);
+            __builtin_amdgcn_sched_barrier(0);
+            va = vn;
+        }
+    };
+
+    // V lags K by one tile: iteration jt computes the scores of tile jt and the PV product of tile
+    // jt - 1, whose V^T arrived in the other V^T buffer one iteration earlier.
+    v4u pprev[4], pnew[4];
+    dma_k(0, 0);
+    {
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (1 < nkt) dma_k(1, 1);
+        dma_v(0, 0);
+        scores(0, 0, !EXACT);
+        if constexpr (!EXACT) {
+            // the reference: the first tile's max
+#pragma unroll
+            for (int qf = 0; qf < 4; ++qf) mu[qf] = mt[qf];
+        }
+#pragma unroll
+        for (int qf = 0; qf < 4; ++qf)
+#pragma unroll
+            for (int part = 0; part < 4; ++part) softmax_part(qf, part, pprev);
+    }
+    for (int jt = 1; jt < nkt; ++jt) {
         const int buf = jt & 1;
         wait_vmcnt<0>();
         __syncthreads();
-        if (jt + 1 < nkt) dma(buf ^ 1, jt + 1, true);
-        scores(buf, jt);
-        if constexpr (!EXACT) {
-            if (jt == 0) {
-                // the reference: the first tile's max (a uniform branch that touches no accumulator)
+        if (jt + 1 < nkt) dma_k(buf ^ 1, jt + 1);
+        dma_v(buf, jt);
+        scores(buf, jt, false);
+        pv(buf ^ 1, pprev, true, pnew);
 #pragma unroll
-                for (int qf = 0; qf < 4; ++qf) mu[qf] = mt[qf];
-            }
-        }
-        // ---- p = 2^((s - mu) C) in fp32 for the row sums, bf16 for the MFMA; B operand of
-        // O^T += V^T P^T: positions 8 g + 4 kf + r <- key 16 kf + 4 g + r
-        v4u pb[4];
-#pragma unroll
-        for (int qf = 0; qf < 4; ++qf) {
-            const float mc = mu[qf] * C;
-            float e[2][4];
-            float sum = 0.0f;
-#pragma unroll
-            for (int kf = 0; kf < 2; ++kf)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    e[kf][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kf][qf][r], C, -mc));
-                    sum += e[kf][r];
-                }
-            lp[qf] += sum;
-            pb[qf] = v4u{pack_bf16x2(e[0][0], e[0][1]), pack_bf16x2(e[0][2], e[0][3]), pack_bf16x2(e[1][0], e[1][1]),
-                         pack_bf16x2(e[1][2], e[1][3])};
-        }
-        if constexpr (!EXACT) {
-            // after the exponentials: p above does not wait for this tile's max
-#pragma unroll
-            for (int qf = 0; qf < 4; ++qf) bad |= mt[qf] > mu[qf] + LIMIT;
-        }
-        asm volatile("s_nop 1");  // VALU-written P -> MFMA source
-        // ---- O^T += V^T P^T: lane holds dims 16 df + 4 (lane >> 4) + r of query 16 qf + (lane & 15)
-        v4u va = vfrag(buf, 0);
-#pragma unroll
-        for (int df = 0; df < 16; ++df) {
-            const v4u vn = df + 1 < 16 ? vfrag(buf, df + 1) : va;
-#pragma unroll
-            for (int qf = 0; qf < 4; ++qf) mfma_o(oacc[df][qf], va, pb[qf]);
-            va = vn;
-        }
+        for (int qf = 0; qf < 4; ++qf) pprev[qf] = pnew[qf];
     }
+    wait_vmcnt<0>();
+    __syncthreads();
+    pv((nkt - 1) & 1, pprev, false, pnew);
     if constexpr (!EXACT) {
         if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) p.redo[t] = 1;
     }

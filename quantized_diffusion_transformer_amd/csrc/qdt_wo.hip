@@ -169,9 +169,9 @@ wo_gemm_kernel(WoKArgs p) {
     // ---- token LDS-DMA: instruction i of wave w fills LDS rows 4 (NDMA w + i) .. + 3 of the
     // stage (1 KiB); lane l moves row r = 4 (NDMA w + i) + l / 16 into LDS chunk slot l % 16, which
     // holds the row's global 16-byte chunk (l % 16) ^ rot4(r).  rot4 swaps the two 2-bit halves of
-    // r mod 16, so the 16 rows x 4 chunks of a fragment read land on distinct 16-byte bank groups
-    // whether the LDS serves 16, 32 or 64 lanes per pass.  Rows past M are clamped to the last
-    // row: their outputs are not stored.
+    // r mod 16, so each of the four 16-lane passes of a fragment read (lanes 0-3, 12-15, 20-23,
+    // 24-27 and that set XORed with 4, 32, 36) lands on distinct 16-byte bank groups, which the
+    // plain c ^ r does not.  Rows past M are clamped to the last row: their outputs are not stored.
     const int xlast = p.M - m0 - 1;
     const uint8_t* xbase =
         uniform_ptr(reinterpret_cast<const uint8_t*>(p.X + (int64_t)m0 * p.ldx + (int64_t)kt0 * BK));

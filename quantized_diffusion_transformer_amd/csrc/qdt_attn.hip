@@ -21,9 +21,10 @@
 //     more VALU than the MFMAs it feeds, and any conditional update of them makes the compiler
 //     spill the query registers).  Later keys may exceed the reference: their probabilities are
 //     2^((s - m) C) > 1, which bf16 (fp32's exponent range) and the fp32 sums hold up to 2^64.  A
-//     workgroup in which any score passes the reference by more than 64 in log2 units raises a
-//     flag; a second launch of the kernel (EXACT) recomputes exactly those workgroups with the
-//     exact row max from a first pass over the keys, and returns at once everywhere else.
+//     workgroup in which some lane's partial row sum passes 2^64 (as it does whenever a score
+//     passes the reference by more than 64 in log2 units) raises a flag; a second launch of the
+//     kernel (EXACT) recomputes exactly those workgroups with the exact row max from a first pass
+//     over the keys, and returns at once everywhere else.
 //   * Probabilities enter the second MFMA as bf16 (as in every bf16 flash-attention kernel); the
 //     row sums use the fp32 values.
 #include "qdt_device.h"
@@ -35,6 +36,7 @@ namespace qdt {
 constexpr int AT_D = 256;   // head width
 constexpr int AT_BQ = 256;  // queries per workgroup (64 per wave)
 constexpr int AT_BK = 32;   // keys per tile
+constexpr int AT_LA = 3;    // LDS fragment reads in flight ahead of the MFMA group that uses them
 
 // Key (0..31) stored at position p of a 32-key group of V^T.
 __device__ __forceinline__ int vt_key_of_pos(int p) {
@@ -97,6 +99,10 @@ __device__ __forceinline__ void mfma_o(v4f& c, const v4u& a, const v4u& b) {
 __device__ __forceinline__ void mfma_s(v4f& c, const v4u& a, const v4u& b) {
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
+// The same with a zero accumulator (inline constant 0), for the first K step of a fragment.
+__device__ __forceinline__ void mfma_s0(v4f& c, const v4u& a, const v4u& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
 // LDS swizzles.  A fragment read touches 16 rows x 4 chunks of 16 bytes (64 lanes, 1 KiB).  The LDS
 // (64 banks of 4 bytes) serves a 16-byte read in four passes of 16 lanes: lanes 0-3, 12-15, 20-23
 // and 24-27 form one pass, the other passes are the same set XORed with 4, 32 and 36.  The slot
@@ -153,32 +159,25 @@ attn_fwd_kernel(AttnArgs p) {
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.Vt + (int64_t)h * AT_D * p.Spad);
     const uint32_t ldsk = __builtin_amdgcn_readfirstlane(lds_offset(smem) + wave * 4 * 1024);
     const uint32_t ldsv = ldsk + KT;
-    // The per-lane offsets are recomputed at every tile from an index the optimizer cannot see
-    // through: held across the loop they would take registers the query fragments need.
-    auto dma_k = [&](int buf, int jt) __attribute__((always_inline)) {
+    // The per-lane offsets are recomputed at every instruction from an index the optimizer cannot
+    // see through: held across the loop they would take registers the query fragments need.
+    // Instruction i (0..3) of this wave for the K rows of tile jt:
+    auto dma_k = [&](int buf, int jt, int i) __attribute__((always_inline)) {
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int key0 = jt * AT_BK;
-        const uint8_t* kb = kbase + (int64_t)key0 * p.ld * 2;
-        const int lim = p.S - 1 - key0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 2 * (4 * wave + i) + (ln >> 5);
-            const uint32_t off = (uint32_t)(min(row, lim) * p.ld * 2) + (uint32_t)(((ln & 31) ^ at_ksw(row & 15)) * 16);
-            lds_dma16_s(ldsk + (uint32_t)(buf * STG + i * 1024), off, kb);
-        }
+        const int row = 2 * (4 * wave + i) + (ln >> 5);
+        const uint32_t off = (uint32_t)(min(row, p.S - 1 - key0) * p.ld * 2) +
+                             (uint32_t)(((ln & 31) ^ at_ksw(row & 15)) * 16);
+        lds_dma16_s(ldsk + (uint32_t)(buf * STG + i * 1024), off, kbase + (int64_t)key0 * p.ld * 2);
     };
-    auto dma_v = [&](int buf, int jt) __attribute__((always_inline)) {
+    // ... and for the V^T rows of tile jt:
+    auto dma_v = [&](int buf, int jt, int i) __attribute__((always_inline)) {
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        const int key0 = jt * AT_BK;
-        const uint8_t* vb = vbase + (int64_t)key0 * 2;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * (4 * wave + i) + (ln >> 2);
-            const uint32_t off = (uint32_t)(row * p.Spad * 2 + (((ln & 3) ^ at_vsw(row)) * 16));
-            lds_dma16_s(ldsv + (uint32_t)(buf * STG + i * 1024), off, vb);
-        }
+        const int row = 16 * (4 * wave + i) + (ln >> 2);
+        const uint32_t off = (uint32_t)(row * p.Spad * 2 + (((ln & 3) ^ at_vsw(row)) * 16));
+        lds_dma16_s(ldsv + (uint32_t)(buf * STG + i * 1024), off, vbase + (int64_t)jt * AT_BK * 2);
     };
     // K fragment (A operand): key 16 kf + (lane & 15) of the tile, dims 32 kk + 8 (lane >> 4) .. + 7
     auto kfrag = [&](int buf, int kf, int kk) __attribute__((always_inline)) {
@@ -193,26 +192,33 @@ attn_fwd_kernel(AttnArgs p) {
                                              (((lane >> 4) ^ at_vsw(lane & 15)) * 16));
     };
 
-    // ---- scores of key tile jt: S^T = K Q^T, lane holds keys 16 kf + 4 (lane >> 4) + r of query
-    // 16 qf + (lane & 15); keys past S get -inf; mt = the tile's max per query (all lane groups)
+    // ---- scores of the key tile in K buffer buf: S^T = K Q^T, lane holds keys
+    // 16 kf + 4 (lane >> 4) + r of query 16 qf + (lane & 15).  hook(g) runs after MFMA group g
+    // (0..15): the next tiles' LDS-DMAs go there, between the MFMAs.
     v4f s[2][4];
-    float mt[4];
-    auto scores = [&](int buf, int jt, bool cross) __attribute__((always_inline)) {
+    auto scores = [&](int buf, auto&& hook) __attribute__((always_inline)) {
+        // 16 K fragments, each read AT_LA groups of 4 MFMAs ahead of its use (one group, 64 MFMA
+        // cycles, is shorter than the LDS read latency)
+        v4u a[16];
 #pragma unroll
-        for (int kf = 0; kf < 2; ++kf)
-#pragma unroll
-            for (int qf = 0; qf < 4; ++qf) s[kf][qf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        // 16 K fragments, each read one group of 4 MFMAs ahead of its use
-        v4u a = kfrag(buf, 0, 0);
+        for (int g = 0; g < AT_LA; ++g) a[g] = kfrag(buf, g / 8, g % 8);
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
-            const int kf = g / 8, kk = g % 8;
-            const v4u an = g + 1 < 16 ? kfrag(buf, (g + 1) / 8, (g + 1) % 8) : a;
+            if (g + AT_LA < 16) a[g + AT_LA] = kfrag(buf, (g + AT_LA) / 8, (g + AT_LA) % 8);
 #pragma unroll
-            for (int qf = 0; qf < 4; ++qf) mfma_s(s[kf][qf], a, qfr[qf][kk]);
-            a = an;
+            for (int qf = 0; qf < 4; ++qf) {
+                if (g % 8 == 0)
+                    mfma_s0(s[g / 8][qf], a[g], qfr[qf][0]);
+                else
+                    mfma_s(s[g / 8][qf], a[g], qfr[qf][g % 8]);
+            }
+            hook(g);
+            __builtin_amdgcn_sched_barrier(0);
         }
         mfma_drain();
+    };
+    // keys past S get -inf
+    auto mask_tail = [&](int jt) __attribute__((always_inline)) {
         if ((jt + 1) * AT_BK > p.S) {
 #pragma unroll
             for (int kf = 0; kf < 2; ++kf)
@@ -224,19 +230,15 @@ attn_fwd_kernel(AttnArgs p) {
                         if (out) s[kf][qf][r] = -__builtin_inff();
                 }
         }
-#pragma unroll
-        for (int qf = 0; qf < 4; ++qf) {
-            float m = fmaxf(fmaxf(fmaxf(s[0][qf][0], s[0][qf][1]), fmaxf(s[0][qf][2], s[0][qf][3])),
-                            fmaxf(fmaxf(s[1][qf][0], s[1][qf][1]), fmaxf(s[1][qf][2], s[1][qf][3])));
-            if (cross) {
-                m = fmaxf(m, __shfl_xor(m, 16, 64));
-                m = fmaxf(m, __shfl_xor(m, 32, 64));
-            }
-            mt[qf] = m;
-        }
+    };
+    // the tile's max per query (all lane groups), raw score units
+    auto tile_max = [&](int qf) __attribute__((always_inline)) {
+        float m = fmaxf(fmaxf(fmaxf(s[0][qf][0], s[0][qf][1]), fmaxf(s[0][qf][2], s[0][qf][3])),
+                        fmaxf(fmaxf(s[1][qf][0], s[1][qf][1]), fmaxf(s[1][qf][2], s[1][qf][3])));
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        return fmaxf(m, __shfl_xor(m, 32, 64));
     };
     constexpr float C = 1.44269504088896341f / 16.0f;  // log2(e) / sqrt(256)
-    constexpr float LIMIT = 64.0f / C;                  // largest excess over the reference, raw units
 
     // reference max per query fragment (raw score units) and this lane's partial row sums
     float mu[4], lp[4];
@@ -247,16 +249,20 @@ attn_fwd_kernel(AttnArgs p) {
     }
     if constexpr (EXACT) {
         // first pass over the keys: the exact row max
-        dma_k(0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma_k(0, 0, i);
         for (int jt = 0; jt < nkt; ++jt) {
-            const int buf = jt & 1;
+            const int buf = jt & 1, jn = min(jt + 1, nkt - 1);
             wait_vmcnt<0>();
             __syncthreads();
-            if (jt + 1 < nkt) dma_k(buf ^ 1, jt + 1);
-            scores(buf, jt, true);
+            scores(buf, [&](int g) __attribute__((always_inline)) {
+                if (g < 4) dma_k(buf ^ 1, jn, g);
+            });
+            mask_tail(jt);
 #pragma unroll
-            for (int qf = 0; qf < 4; ++qf) mu[qf] = fmaxf(mu[qf], mt[qf]);
+            for (int qf = 0; qf < 4; ++qf) mu[qf] = fmaxf(mu[qf], tile_max(qf));
         }
+        wait_vmcnt<0>();
         __syncthreads();  // every wave is done with the LDS tiles before they are refilled
     }
 
@@ -265,82 +271,107 @@ attn_fwd_kernel(AttnArgs p) {
     for (int df = 0; df < 16; ++df)
 #pragma unroll
         for (int qf = 0; qf < 4; ++qf) oacc[df][qf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    bool bad = false;
 
-    // ---- softmax of the scores in s against mu, in 4 parts per query fragment qf so that each part
-    // can follow one group of the previous tile's PV MFMAs: p = 2^((s - mu) C) in fp32 for the row
-    // sums, bf16 for the MFMA (B operand of O^T += V^T P^T: positions 8 g + 4 kf + r <- key
-    // 16 kf + 4 g + r).  Part 3 also raises the rerun flag from the lane's own scores.
-    float tt[8];
-    auto softmax_part = [&](int qf, int part, v4u (&pn)[4]) __attribute__((always_inline)) {
-        if (part == 0) {
-            const float mc = mu[qf] * C;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tt[e] = __builtin_fmaf(s[e / 4][qf][e % 4], C, -mc);
-        } else if (part == 1) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) tt[e] = __builtin_amdgcn_exp2f(tt[e]);
-        } else if (part == 2) {
-#pragma unroll
-            for (int e = 4; e < 8; ++e) tt[e] = __builtin_amdgcn_exp2f(tt[e]);
+    // ---- softmax of the scores in s against mu, 16 pieces per query fragment qf, each small enough
+    // to issue in the shadow of one MFMA of the previous tile's PV product: p = 2^((s - mu) C) in
+    // fp32 for the row sums, bf16 for the MFMA (B operand of O^T += V^T P^T: positions 8 g + 4 kf + r
+    // <- key 16 kf + 4 g + r)
+    float tt[8], sa[4], mc;
+    auto softmax_piece = [&](int qf, int i, v4u (&pn)[4]) __attribute__((always_inline)) {
+        if (i < 4) {
+            if (i == 0) mc = mu[qf] * C;
+            tt[2 * i] = __builtin_fmaf(s[i / 2][qf][(2 * i) % 4], C, -mc);
+            tt[2 * i + 1] = __builtin_fmaf(s[i / 2][qf][(2 * i) % 4 + 1], C, -mc);
+        } else if (i < 12) {
+            tt[i - 4] = __builtin_amdgcn_exp2f(tt[i - 4]);
+        } else if (i == 12) {
+            sa[0] = tt[0] + tt[1];
+            sa[1] = tt[2] + tt[3];
+            pn[qf][0] = pack_bf16x2(tt[0], tt[1]);
+            pn[qf][1] = pack_bf16x2(tt[2], tt[3]);
+        } else if (i == 13) {
+            sa[2] = tt[4] + tt[5];
+            sa[3] = tt[6] + tt[7];
+            pn[qf][2] = pack_bf16x2(tt[4], tt[5]);
+            pn[qf][3] = pack_bf16x2(tt[6], tt[7]);
+        } else if (i == 14) {
+            sa[0] = (sa[0] + sa[1]) + (sa[2] + sa[3]);
         } else {
-            lp[qf] += ((tt[0] + tt[1]) + (tt[2] + tt[3])) + ((tt[4] + tt[5]) + (tt[6] + tt[7]));
-            pn[qf] = v4u{pack_bf16x2(tt[0], tt[1]), pack_bf16x2(tt[2], tt[3]), pack_bf16x2(tt[4], tt[5]),
-                         pack_bf16x2(tt[6], tt[7])};
-            if constexpr (!EXACT) bad |= mt[qf] > mu[qf] + LIMIT;
+            lp[qf] += sa[0];
         }
     };
-    // ---- O^T += V^T P^T for the tile in V^T buffer vbuf, with the softmax parts of the current
-    // scores after the groups (lane holds dims 16 df + 4 (lane >> 4) + r of query 16 qf + (lane & 15))
+    // ---- O^T += V^T P^T for the tile in V^T buffer vbuf (lane holds dims 16 df + 4 (lane >> 4) + r
+    // of query 16 qf + (lane & 15)), each MFMA followed by one softmax piece of the current scores
     auto pv = [&](int vbuf, const v4u (&pp)[4], bool with_softmax, v4u (&pn)[4]) __attribute__((always_inline)) {
         asm volatile("s_nop 1");  // VALU-written P -> MFMA source
-        v4u va = vfrag(vbuf, 0);
+        v4u va[16];
+#pragma unroll
+        for (int df = 0; df < AT_LA; ++df) va[df] = vfrag(vbuf, df);
 #pragma unroll
         for (int df = 0; df < 16; ++df) {
-            const v4u vn = df + 1 < 16 ? vfrag(vbuf, df + 1) : va;
+            if (df + AT_LA < 16) va[df + AT_LA] = vfrag(vbuf, df + AT_LA);
 #pragma unroll
-            for (int qf = 0; qf < 4; ++qf) mfma_o(oacc[df][qf], va, pp[qf]);
-            if (with_softmax) softmax_part(df / 4, df % 4, pn);
-            __builtin_amdgcn_sched_barrier(0);
-            va = vn;
+            for (int qf = 0; qf < 4; ++qf) {
+                mfma_o(oacc[df][qf], va[df], pp[qf]);
+                if (with_softmax) softmax_piece(df / 4, 4 * (df % 4) + qf, pn);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
     // V lags K by one tile: iteration jt computes the scores of tile jt and the PV product of tile
-    // jt - 1, whose V^T arrived in the other V^T buffer one iteration earlier.
+    // jt - 1, whose V^T arrived in the other V^T buffer one iteration earlier.  The LDS-DMAs of an
+    // iteration (K of tile jt + 1, V^T of tile jt) run between its score MFMAs; tile indices past
+    // the last are clamped rather than branched on.  The last PV product runs in one more
+    // iteration (jt = nkt) whose scores are all masked to -inf, so that it adds nothing to the row
+    // sums: a PV product outside the loop would have the compiler move the 256 accumulators to
+    // other registers, right before MFMAs that read them.
     v4u pprev[4], pnew[4];
-    dma_k(0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_k(0, 0, i);
     {
         wait_vmcnt<0>();
         __syncthreads();
-        if (1 < nkt) dma_k(1, 1);
-        dma_v(0, 0);
-        scores(0, 0, !EXACT);
+        const int jn = min(1, nkt - 1);
+        scores(0, [&](int g) __attribute__((always_inline)) {
+            if (g < 4)
+                dma_k(1, jn, g);
+            else if (g < 8)
+                dma_v(0, 0, g - 4);
+        });
+        mask_tail(0);
         if constexpr (!EXACT) {
             // the reference: the first tile's max
 #pragma unroll
-            for (int qf = 0; qf < 4; ++qf) mu[qf] = mt[qf];
+            for (int qf = 0; qf < 4; ++qf) mu[qf] = tile_max(qf);
         }
 #pragma unroll
         for (int qf = 0; qf < 4; ++qf)
 #pragma unroll
-            for (int part = 0; part < 4; ++part) softmax_part(qf, part, pprev);
+            for (int i = 0; i < 16; ++i) softmax_piece(qf, i, pprev);
     }
-    for (int jt = 1; jt < nkt; ++jt) {
-        const int buf = jt & 1;
+    for (int jt = 1; jt <= nkt; ++jt) {
+        const int buf = jt & 1, jn = min(jt + 1, nkt - 1), jv = min(jt, nkt - 1);
         wait_vmcnt<0>();
         __syncthreads();
-        if (jt + 1 < nkt) dma_k(buf ^ 1, jt + 1);
-        dma_v(buf, jt);
-        scores(buf, jt, false);
+        scores(buf, [&](int g) __attribute__((always_inline)) {
+            if (g < 4)
+                dma_k(buf ^ 1, jn, g);
+            else if (g < 8)
+                dma_v(buf, jv, g - 4);
+        });
+        mask_tail(jt);
         pv(buf ^ 1, pprev, true, pnew);
 #pragma unroll
         for (int qf = 0; qf < 4; ++qf) pprev[qf] = pnew[qf];
     }
-    wait_vmcnt<0>();
-    __syncthreads();
-    pv((nkt - 1) & 1, pprev, false, pnew);
+    wait_vmcnt<0>();  // the last iteration's LDS-DMAs land before the workgroup ends
     if constexpr (!EXACT) {
+        // a probability past 2^64 (a score more than 64 log2 units above the reference) leaves a
+        // lane's partial row sum past 2^64: flag the workgroup for the exact-max rerun
+        bool bad = false;
+#pragma unroll
+        for (int qf = 0; qf < 4; ++qf) bad |= !(lp[qf] <= 0x1p64f);
         if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) p.redo[t] = 1;
     }
     mfma_drain();

@@ -159,25 +159,31 @@ attn_fwd_kernel(AttnArgs p) {
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.Vt + (int64_t)h * AT_D * p.Spad);
     const uint32_t ldsk = __builtin_amdgcn_readfirstlane(lds_offset(smem) + wave * 4 * 1024);
     const uint32_t ldsv = ldsk + KT;
-    // The per-lane offsets are recomputed at every instruction from an index the optimizer cannot
-    // see through: held across the loop they would take registers the query fragments need.
-    // Instruction i (0..3) of this wave for the K rows of tile jt:
+    // Per-lane offsets, computed once: K instruction i of this wave moves key rows
+    // 2 (4 w + i) + (lane >> 5) of the tile, V^T instruction i dim rows 16 (4 w + i) + lane / 4
+    // (the i-dependence of the V^T offset is uniform and goes into the scalar base).  Only a
+    // partial last key tile recomputes its K offsets, with rows past S clamped to the last key
+    // (their scores are masked).
+    uint32_t koff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 2 * (4 * wave + i) + (lane >> 5);
+        koff[i] = (uint32_t)(row * p.ld * 2) + (uint32_t)(((lane & 31) ^ at_ksw(row & 15)) * 16);
+    }
+    const uint32_t voff = (uint32_t)((64 * wave + (lane >> 2)) * p.Spad * 2) +
+                          (uint32_t)(((lane & 3) ^ at_vsw(lane >> 2)) * 16);
     auto dma_k = [&](int buf, int jt, int i) __attribute__((always_inline)) {
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
         const int key0 = jt * AT_BK;
-        const int row = 2 * (4 * wave + i) + (ln >> 5);
-        const uint32_t off = (uint32_t)(min(row, p.S - 1 - key0) * p.ld * 2) +
-                             (uint32_t)(((ln & 31) ^ at_ksw(row & 15)) * 16);
+        uint32_t off = koff[i];
+        if (key0 + AT_BK > p.S) {
+            const int row = 2 * (4 * wave + i) + (lane >> 5);
+            off = (uint32_t)(min(row, p.S - 1 - key0) * p.ld * 2) + (uint32_t)(((lane & 31) ^ at_ksw(row & 15)) * 16);
+        }
         lds_dma16_s(ldsk + (uint32_t)(buf * STG + i * 1024), off, kbase + (int64_t)key0 * p.ld * 2);
     };
-    // ... and for the V^T rows of tile jt:
     auto dma_v = [&](int buf, int jt, int i) __attribute__((always_inline)) {
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        const int row = 16 * (4 * wave + i) + (ln >> 2);
-        const uint32_t off = (uint32_t)(row * p.Spad * 2 + (((ln & 3) ^ at_vsw(row)) * 16));
-        lds_dma16_s(ldsv + (uint32_t)(buf * STG + i * 1024), off, vbase + (int64_t)jt * AT_BK * 2);
+        lds_dma16_s(ldsv + (uint32_t)(buf * STG + i * 1024), voff,
+                    vbase + (int64_t)jt * AT_BK * 2 + (int64_t)16 * i * p.Spad * 2);
     };
     // K fragment (A operand): key 16 kf + (lane & 15) of the tile, dims 32 kk + 8 (lane >> 4) .. + 7
     auto kfrag = [&](int buf, int kf, int kk) __attribute__((always_inline)) {

@@ -202,7 +202,9 @@ attn_fwd_kernel(AttnArgs p) {
     // 16 kf + 4 (lane >> 4) + r of query 16 qf + (lane & 15).  hook(g) runs after MFMA group g
     // (0..15): the next tiles' LDS-DMAs go there, between the MFMAs.
     v4f s[2][4];
-    auto scores = [&](int buf, auto&& hook) __attribute__((always_inline)) {
+    // drain: wait for the last MFMAs' results here (needed when VALU reads or writes the scores
+    // at once); in the main loop the first such read comes at least five MFMAs later.
+    auto scores = [&](int buf, auto&& hook, bool drain) __attribute__((always_inline)) {
         // 16 K fragments, each read AT_LA groups of 4 MFMAs ahead of its use (one group, 64 MFMA
         // cycles, is shorter than the LDS read latency)
         v4u a[16];
@@ -221,11 +223,12 @@ attn_fwd_kernel(AttnArgs p) {
             hook(g);
             __builtin_amdgcn_sched_barrier(0);
         }
-        mfma_drain();
+        if (drain) mfma_drain();
     };
     // keys past S get -inf
     auto mask_tail = [&](int jt) __attribute__((always_inline)) {
         if ((jt + 1) * AT_BK > p.S) {
+            mfma_drain();
 #pragma unroll
             for (int kf = 0; kf < 2; ++kf)
 #pragma unroll
@@ -261,9 +264,11 @@ attn_fwd_kernel(AttnArgs p) {
             const int buf = jt & 1, jn = min(jt + 1, nkt - 1);
             wait_vmcnt<0>();
             __syncthreads();
-            scores(buf, [&](int g) __attribute__((always_inline)) {
-                if (g < 4) dma_k(buf ^ 1, jn, g);
-            });
+            scores(
+                buf, [&](int g) __attribute__((always_inline)) {
+                    if (g < 4) dma_k(buf ^ 1, jn, g);
+                },
+                true);
             mask_tail(jt);
 #pragma unroll
             for (int qf = 0; qf < 4; ++qf) mu[qf] = fmaxf(mu[qf], tile_max(qf));
@@ -339,12 +344,15 @@ attn_fwd_kernel(AttnArgs p) {
         wait_vmcnt<0>();
         __syncthreads();
         const int jn = min(1, nkt - 1);
-        scores(0, [&](int g) __attribute__((always_inline)) {
-            if (g < 4)
-                dma_k(1, jn, g);
-            else if (g < 8)
-                dma_v(0, 0, g - 4);
-        });
+        scores(
+            0,
+            [&](int g) __attribute__((always_inline)) {
+                if (g < 4)
+                    dma_k(1, jn, g);
+                else if (g < 8)
+                    dma_v(0, 0, g - 4);
+            },
+            true);
         mask_tail(0);
         if constexpr (!EXACT) {
             // the reference: the first tile's max
@@ -360,12 +368,15 @@ attn_fwd_kernel(AttnArgs p) {
         const int buf = jt & 1, jn = min(jt + 1, nkt - 1), jv = min(jt, nkt - 1);
         wait_vmcnt<0>();
         __syncthreads();
-        scores(buf, [&](int g) __attribute__((always_inline)) {
-            if (g < 4)
-                dma_k(buf ^ 1, jn, g);
-            else if (g < 8)
-                dma_v(buf, jv, g - 4);
-        });
+        scores(
+            buf,
+            [&](int g) __attribute__((always_inline)) {
+                if (g < 4)
+                    dma_k(buf ^ 1, jn, g);
+                else if (g < 8)
+                    dma_v(buf, jv, g - 4);
+            },
+            false);
         mask_tail(jt);
         pv(buf ^ 1, pprev, true, pnew);
 #pragma unroll

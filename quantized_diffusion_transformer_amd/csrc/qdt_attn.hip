@@ -36,7 +36,7 @@ namespace qdt {
 constexpr int AT_D = 256;   // head width
 constexpr int AT_BQ = 256;  // queries per workgroup (64 per wave)
 constexpr int AT_BK = 32;   // keys per tile
-constexpr int AT_LA = 3;    // LDS fragment reads in flight ahead of the MFMA group that uses them
+constexpr int AT_LA = 4;    // LDS fragment reads in flight ahead of the MFMA group that uses them
 
 // Key (0..31) stored at position p of a 32-key group of V^T.
 __device__ __forceinline__ int vt_key_of_pos(int p) {

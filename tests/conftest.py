@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session", autouse=True)
 def _oracle_threads():
-    # the oracle uses the CPU share given to this process (16 on the GPU machine)
+    # the oracle uses the CPU share given to this process (OMP_NUM_THREADS when set)
     import oracle
     n = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
     if n > 0:

@@ -53,7 +53,7 @@ typedef enum qdt_status {
     QDT_EWORKSPACE = 4,   /* workspace missing or smaller than required */
     QDT_EALIAS = 5,       /* output overlaps an input */
     QDT_EHIP = 6,         /* the HIP runtime reported an error at launch */
-    QDT_EUNSUPPORTED = 7  /* valid request this build cannot serve (e.g. plan/epilogue pair) */
+    QDT_EUNSUPPORTED = 7  /* valid request the library does not implement (e.g. plan/epilogue pair) */
 } qdt_status;
 
 typedef enum qdt_epilogue {

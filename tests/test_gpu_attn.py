@@ -159,3 +159,14 @@ def test_attention_full_size_sampled_rows():
     for h in (0, 17):
         exact = within_bound(O, d["Q"], d["K"], d["V"], h, rows)
         print(f"head {h}: {exact:.3f} of the sampled outputs equal the correctly rounded result", flush=True)
+
+
+def test_attention_ragged_full_heads_sampled_rows():
+    """6037 tokens (21 keys past the last full 32-key tile, 149 queries past the last full 256-query
+    block), all 18 heads, sampled rows of three heads including the last query row."""
+    d = W.make_attention(6037, 18, seed=W.BASE_SEED + 5)
+    announce("attention 6037 x 18 heads")
+    O = to_host(qdt.attention(to_dev(d["Q"]), to_dev(d["K"]), to_dev(d["V"]), 18))
+    rows = np.array([0, 255, 256, 5887, 5888, 6000, 6036])
+    for h in (0, 9, 17):
+        within_bound(O, d["Q"], d["K"], d["V"], h, rows)

@@ -38,8 +38,14 @@ def parse():
     # the clock settles after about 20 ms of sustained load: the default warm-up covers ~45 ms
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="minimum warm-up load in milliseconds before the timed steps (the shader clock "
+                         "settles under sustained MFMA load); the warm-up runs max(--warmup steps, this long)")
     ap.add_argument("--rotate", type=int, default=6, help="rotating buffer sets (cold Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="headline timing loop only (no step distribution, flushed steps, clock record or "
+                         "accuracy pass): for runs under rocprofv3")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--only", default=None,
                     help="run only this workload's timing loop (per-workload profiles); the headline "
@@ -65,19 +71,36 @@ def to_dev(a):
     return torch.from_numpy(a).cuda()
 
 
-EVENT_EVERY = 10  # steps between event-bracketed steps (a timing event record costs ~5 us of stream time)
+EVENT_EVERY = 10   # steps between event-bracketed steps (a timing event record costs ~5 us of stream time)
+MIN_EVENT_SAMPLES = 20
 
 
-def time_loop(fn_step, sets, steps, warmup):
+def warm_up(fn_step, sets, warmup, settle_ms=0.0):
+    """`warmup` untimed steps, continued until at least `settle_ms` of wall time has passed.
+    Returns the number of warm-up steps run."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(50 if n >= warmup else min(50, warmup - n)):
+            fn_step(sets[n % len(sets)], None)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def time_loop(fn_step, sets, steps, warmup, settle_ms=0.0, stats_out=None):
     """Wall time of `steps` steps (sync on both sides) + per-phase HIP event times.
 
-    Every EVENT_EVERY-th step of the timed region records HIP events (on the stream the library
-    launches on) around its two launches; the others run without events."""
+    Every k-th step of the timed region records HIP events (on the stream the library launches
+    on) around its two launches, k = EVENT_EVERY, or less so that there are at least
+    MIN_EVENT_SAMPLES samples; the others run without events."""
     import torch
-    for i in range(warmup):
-        fn_step(sets[i % len(sets)], None)
-    torch.cuda.synchronize()
-    sampled = list(range(0, steps, EVENT_EVERY))
+    nw = warm_up(fn_step, sets, warmup, settle_ms)
+    if stats_out is not None:
+        stats_out["warmup_steps_run"] = nw
+    every = max(1, min(EVENT_EVERY, steps // MIN_EVENT_SAMPLES))
+    sampled = list(range(0, steps, every))
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -85,9 +108,76 @@ def time_loop(fn_step, sets, steps, warmup):
         fn_step(sets[i % len(sets)], evs.get(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if stats_out is not None:
+        stats_out["event_every"] = every
+        stats_out["event_samples"] = len(sampled)
     ph1 = [evs[i][0].elapsed_time(evs[i][1]) for i in sampled]
     ph2 = [evs[i][1].elapsed_time(evs[i][2]) for i in sampled]
     return (t1 - t0) * 1e3 / steps, ph1, ph2
+
+
+def step_distribution(fn_step, sets, blocks=30, per_block=10):
+    """Mean step time of each of `blocks` runs of `per_block` back-to-back steps, bracketed by HIP
+    events at the block ends only (the event cost is spread over the block)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
+    n = 0
+    evs[0].record()
+    for b in range(blocks):
+        for _ in range(per_block):
+            fn_step(sets[n % len(sets)], None)
+            n += 1
+        evs[b + 1].record()
+    torch.cuda.synchronize()
+    return [evs[b].elapsed_time(evs[b + 1]) / per_block for b in range(blocks)]
+
+
+FLUSH_BYTES = 512 << 20  # more than the 256 MB Infinity Cache
+
+
+def flushed_steps(fn_step, sets, reps=25):
+    """Single steps bracketed by HIP events, each after a 512 MiB write that evicts the caches
+    (outside the events)."""
+    import torch
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    times = []
+    for r in range(reps):
+        scratch.fill_(r & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn_step(sets[r % len(sets)], None)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del scratch
+    return times
+
+
+def clock_during(fn_step, sets, qdt, launches=100, grid=256):
+    """Shader clock of the GEMM kernel from the library's clock record: per launch, the sum over
+    workgroups of shader-clock cycles over the sum of 100 MHz real-time ticks, from each
+    workgroup's start to its last store."""
+    import numpy as np
+    import torch
+    buf = torch.zeros((launches * grid, 4), dtype=torch.int64, device="cuda")
+    qdt.clock_record(buf)
+    try:
+        for i in range(launches):
+            fn_step(sets[i % len(sets)], None)
+        torch.cuda.synchronize()
+        used = qdt.clock_record_used()
+    finally:
+        qdt.clock_record(None)
+    rec = buf[:used].cpu().numpy().astype(np.int64).reshape(-1, grid, 4)
+    cyc = (rec[:, :, 2] - rec[:, :, 0]).sum(axis=1).astype(np.float64)
+    real = (rec[:, :, 3] - rec[:, :, 1]).sum(axis=1).astype(np.float64)
+    mhz = cyc / real * 100.0
+    span_us = (rec[:, :, 3].max(axis=1) - rec[:, :, 1].min(axis=1)) / 100.0
+    return {"clock_mhz": float(np.median(mhz)), "clock_mhz_p10": float(np.percentile(mhz, 10)),
+            "clock_mhz_p90": float(np.percentile(mhz, 90)), "launches": int(rec.shape[0]),
+            "kernel_span_us_median": float(np.median(span_us)),
+            "how": "s_memtime / s_memrealtime read by each workgroup's first wave at its start and after its "
+                   "last store; clock = sum of cycles / sum of 100 MHz ticks per launch (median over launches)"}
 
 
 def time_loop_best(fn_step, steps, warmup, reps=2):
@@ -96,7 +186,8 @@ def time_loop_best(fn_step, steps, warmup, reps=2):
     the number)."""
     best = None
     for r in range(reps):
-        res = time_loop(fn_step, [None], steps, warmup if r == 0 else max(1, warmup // 4))
+        res = time_loop(fn_step, [None], steps, warmup if r == 0 else max(1, warmup // 4),
+                        settle_ms=100.0 if r == 0 else 0.0)
         if best is None or res[0] < best[0]:
             best = res
     return best
@@ -208,7 +299,6 @@ def headline(args):
         sets.append(dict(X=X, Wq=Wq, Xq=torch.empty((M, K), dtype=torch.int8, device="cuda"),
                          sx=torch.empty(M, dtype=torch.float32, device="cuda"),
                          Y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
-    del W0
     torch.cuda.synchronize()
 
     def step(S, ev):
@@ -221,9 +311,22 @@ def headline(args):
         if ev is not None:
             ev[2].record()
 
-    log(f"timing {args.steps} steps (warmup {args.warmup}, {R} rotating sets), plan {plan}")
-    ms, tq, tg = time_loop(step, sets, args.steps, args.warmup)
+    log(f"timing {args.steps} steps (warmup {args.warmup} steps and >= {args.settle_ms} ms, {R} rotating sets), "
+        f"plan {plan}")
+    info = {}
+    ms, tq, tg = time_loop(step, sets, args.steps, args.warmup, args.settle_ms, info)
     log(f"wall {ms:.4f} ms/step; quantize {stats(tq)['mean']:.4f} ms + linear {stats(tg)['mean']:.4f} ms (HIP events)")
+    if args.profile_run:
+        dist, flushed, acc = [ms], [ms], None
+        clk = {"clock_mhz": float("nan")}
+    else:
+        dist = step_distribution(step, sets)
+        flushed = flushed_steps(step, sets)
+        clk = clock_during(step, sets, qdt, grid=plan["grid"])
+        log(f"step blocks median {np.median(dist):.4f} ms; flushed median {np.median(flushed):.4f} ms; "
+            f"GEMM clock {clk['clock_mhz']:.0f} MHz")
+        acc = accuracy_info(d, sets[0]["Y"], W0, b, qdt)
+    del W0
     ops = 2.0 * M * N * K
     tops = ops / (ms * 1e-3) / 1e12
     q = stats(tq)
@@ -232,6 +335,7 @@ def headline(args):
     gbytes = M * K + N * K + 4 * M + 4 * N + 2 * N + 2 * M * N
     gemm_tops = ops / (g["mean"] * 1e-3) / 1e12
     traffic = traffic_record("w8a8_gemm_bias_4608")
+    peak_clk = PEAK_INT8_TOPS * clk["clock_mhz"] / 2400.0
     out = {
         "metric": METRIC,
         "value": round(tops, 2),
@@ -239,6 +343,8 @@ def headline(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
+        "warmup_steps_run": info["warmup_steps_run"],
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -248,23 +354,63 @@ def headline(args):
         "config": {"workload": name, "M": M, "N": N, "K": K, "epilogue": "bias", "smoothquant_alpha": 0.5,
                    "plan": plan, "rotating_sets": R},
         "pct_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
+        "step_ms": {"back_to_back_blocks": {k: round(v, 5) for k, v in stats(dist).items()},
+                    "blocks": len(dist), "steps_per_block": 10,
+                    "flushed_single": {k: round(v, 5) for k, v in stats(flushed).items()}, "flushed_reps": len(flushed),
+                    "note": "back_to_back_blocks: mean step of each block of 10 rotating-set steps (HIP events at "
+                            "block ends); flushed_single: one step between HIP events after a 512 MiB write that "
+                            "evicts L2 and the Infinity Cache (includes the event-to-launch gap)"},
+        "clock_mhz": round(clk["clock_mhz"], 1),
+        "clock": {k: (round(v, 2) if isinstance(v, float) else v) for k, v in clk.items()},
         "roofline": {"bound": "mfma", "kernel": "gemm_kernel (qdt_w8a8_linear, BIAS)",
                      "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                      "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
                      "algorithmic_ops_per_launch": ops, "avg_launch_ms": round(g["mean"], 5),
-                     "launch_ms": {k: round(v, 5) for k, v in g.items()}},
+                     "launch_ms": {k: round(v, 5) for k, v in g.items()},
+                     "event_samples": info["event_samples"],
+                     "peak_at_measured_clock": round(peak_clk, 1),
+                     "frac_at_measured_clock": round(gemm_tops / peak_clk, 4)},
         "roofline_quantize": {"bound": "hbm", "kernel": "quant_rows_kernel (qdt_quantize_per_token)",
                               "achieved": round(qbytes / (q["mean"] * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "frac": round(qbytes / (q["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                               "algorithmic_bytes_per_launch": qbytes, "avg_launch_ms": round(q["mean"], 5),
                               "launch_ms": {k: round(v, 5) for k, v in q.items()},
+                              "timing": "HIP event interval, which also holds the dispatch gap between the event "
+                                        "record and the kernel start; the kernel's own duration is in the "
+                                        "rocprofv3 kernel trace",
                               "traffic": None if traffic_record("quantize_4608") is None
                               else traffic_record("quantize_4608")["bytes_per_launch"]},
+        "accuracy_vs_fp64_unquantized": acc,
         "gemm_algorithmic_bytes": gbytes,
         "device": torch.cuda.get_device_name(0),
     }
     return out, d
+
+
+def accuracy_info(d, Y, Wt, b, qdt, nrows=64):
+    """Information, not a gate: the W8A8 output's error against the unquantized linear in fp64
+    (X W^T + b on the bf16 inputs) on sampled rows, with SmoothQuant (the timed path's output) and
+    without smoothing (lambda = 1, run here once)."""
+    import numpy as np
+    import torch
+
+    import qdt_workloads as W
+    X = to_dev(d["X"])
+    Wq, sw, _, _ = qdt.smooth_prepare(Wt, None)
+    Xq, sx = qdt.quantize_per_token(X, None)
+    Yp = qdt.w8a8_linear(Xq, sx, Wq, sw, b, "bias")
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(1).choice(d["M"], nrows, replace=False))
+    ref = W.bf16_bits_to_f32(d["X"][rows]).astype(np.float64) @ W.bf16_bits_to_f32(d["W"]).astype(np.float64).T
+    ref += W.bf16_bits_to_f32(d["bias"]).astype(np.float64)[None, :]
+    out = {"rows": int(nrows)}
+    for label, t in (("smoothquant_alpha_0.5", Y), ("no_smoothing", Yp)):
+        y = t[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+        e = y - ref
+        out[label] = {"rel_frobenius": round(float(np.linalg.norm(e) / np.linalg.norm(ref)), 6),
+                      "max_abs": round(float(np.abs(e).max()), 6)}
+    return out
 
 
 def cpu_baseline(d):

@@ -289,7 +289,10 @@ qdt_status qdt_w8a8_linear_workspace_size(int64_t M, int64_t N, int64_t K, qdt_e
  *   workspace: device buffer of at least qdt_w8a8_linear_workspace_size() bytes (may be NULL
  *   when that size is 0).
  * Shapes: M >= 0 (rows are masked, any M), K % 128 == 0, N % 16 == 0 (N % 32 == 0 for
- * SILU_GATE, N % 256 == 0 for HEAD_RMSNORM).  Results do not depend on M, the tile or the
+ * SILU_GATE, N % 256 == 0 for HEAD_RMSNORM).  K % 128 rather than the MFMA's K step of 64: each
+ * main-loop stage copies one whole 128-byte cache line of every operand row into LDS (half-line
+ * stages move operands at two thirds of the rate), and the kernel has no masked partial stage;
+ * every K of the DiT's linears (4608, 12288, 53248) is a multiple of 128.  Results do not depend on M, the tile or the
  * K split: the integer sum is exact and every output element is computed by the same
  * fp32 operation sequence.
  */
@@ -311,7 +314,9 @@ qdt_status qdt_w8a8_linear_planned(const int8_t* Xq, const float* x_scale, const
  * down-projections stay in bf16): Y[m][n] = bf16_rne(sum_k X[m][k] * W[n][k] + bias[n]),
  * products exact, accumulated in fp32 on bf16 MFMA (summation order differs from a serial
  * sum; error within the fp32 forward-error bound of a K-term sum).
- *   X bf16 [M, K], W bf16 [N, K], bias bf16 [N] or NULL, Y bf16 [M, ldy].
+ *   X bf16 [M, K], W bf16 [N, K], bias bf16 [N] or NULL, Y bf16 [M, ldy].  ldy (>= N, % 8 == 0)
+ *   lets the output land in a column window of a wider row-major buffer, as the other linears
+ *   allow, e.g. one projection of several written side by side into a shared activation tensor.
  * Shapes: K % 64 == 0, N % 16 == 0, any M >= 0.
  */
 qdt_status qdt_bf16_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, int64_t M, int64_t N,
@@ -340,6 +345,24 @@ qdt_status qdt_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V
 /* Bytes of workspace qdt_attention needs: H * 256 * roundup(S, 32) * 2 for V transposed, plus one int
  * per 256-query block and head (padded to 16 bytes).  Pure host computation. */
 qdt_status qdt_attention_workspace_size(int64_t S, int64_t H, size_t* bytes);
+
+/*
+ * Clock record (diagnostic; not part of the layer).  While a buffer is armed, every W8A8 GEMM
+ * kernel that qdt_w8a8_linear / qdt_w8a8_linear_planned launch takes the next `grid` entries of it
+ * (one per workgroup, in workgroup-id order) as long as they fit; launches that do not fit record
+ * nothing.  Entry = 4 uint64: the shader-clock counter (s_memtime) and the 100 MHz real-time
+ * counter (s_memrealtime) read by the workgroup's first wave when it starts, then the same two
+ * after its last output store is issued.  The shader clock of a launch is therefore
+ * sum(cycles) / sum(real ticks) * 100 MHz over its entries.
+ *   buf: device memory of `entries` * 32 bytes, 8-byte aligned, owned by the caller, or NULL to
+ *   disarm.  Arming resets the fill level.  The setting is process-wide (all devices, all threads);
+ *   it adds one uniform branch per kernel when disarmed.  QDT_EINVAL for entries <= 0 with a
+ *   buffer, or a misaligned buffer.
+ */
+qdt_status qdt_clock_record(uint64_t* buf, int64_t entries);
+
+/* Entries of the armed clock record filled so far (pure host computation). */
+qdt_status qdt_clock_record_used(int64_t* entries);
 
 #ifdef __cplusplus
 }

@@ -71,6 +71,8 @@ _SIGS = {
     "qdt_w8a8_linear_planned": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P, _SZ,
                                  C.POINTER(qdt_linear_plan), _P], _I),
     "qdt_bf16_linear": ([_P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
+    "qdt_clock_record": ([_P, _I64], _I),
+    "qdt_clock_record_used": ([C.POINTER(_I64)], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -94,6 +96,25 @@ def _check(status: int, where: str) -> None:
 
 def version() -> str:
     return qdt_version().decode()
+
+
+def clock_record(buf: torch.Tensor | None) -> None:
+    """Arm (int64 device tensor [entries, 4]) or disarm (None) the W8A8 GEMM clock record: each
+    GEMM launch then fills one row per workgroup with its start / end shader-clock counter and
+    100 MHz real-time counter, while rows remain."""
+    if buf is None:
+        _check(qdt_clock_record(None, 0), "qdt_clock_record")
+        return
+    _dev(buf, torch.int64, "buf")
+    if buf.dim() != 2 or buf.shape[1] != 4 or not buf.is_contiguous():
+        raise ValueError("clock record buffer must be a contiguous int64 [entries, 4] tensor")
+    _check(qdt_clock_record(_ptr(buf), buf.shape[0]), "qdt_clock_record")
+
+
+def clock_record_used() -> int:
+    n = _I64(0)
+    _check(qdt_clock_record_used(C.byref(n)), "qdt_clock_record_used")
+    return n.value
 
 
 # ------------------------------------------------------------------------------- helpers

@@ -28,12 +28,30 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compiles every source to an object (in parallel), then links libqdt.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    cflags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    jobs = []
+    for s in SOURCES:
+        obj = os.path.join(objdir, s.replace(".hip", ".o"))
+        jobs.append((obj, [hipcc(), *cflags, "-c", "-I", os.path.join(ROOT, "include"), os.path.join(CSRC, s),
+                           "-o", obj]))
+
+    def run(job):
+        if verbose:
+            print(" ".join(job[1]), flush=True)
+        subprocess.run(job[1], check=True)
+        return job[0]
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "0") or 0) or (os.cpu_count() or 1)))
+    with ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(run, jobs))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
+    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+        print(" ".join(link), flush=True)
+    subprocess.run(link, check=True)
     os.replace(tmp, LIB)
     return LIB
 

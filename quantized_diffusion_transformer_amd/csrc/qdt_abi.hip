@@ -2,9 +2,24 @@
 // Validation and planning are pure host code; nothing is enqueued unless every check passes.
 #include <string.h>
 
+#include <mutex>
+
 #include "qdt_internal.h"
 
 namespace qdt {
+
+// Clock record of the W8A8 GEMM (qdt_clock_record): buffer, capacity and fill level in entries.
+static std::mutex g_clk_mu;
+static uint64_t* g_clk_buf = nullptr;
+static int64_t g_clk_cap = 0, g_clk_used = 0;
+
+uint64_t* clock_record_take(int grid) {
+    std::lock_guard<std::mutex> lk(g_clk_mu);
+    if (!g_clk_buf || g_clk_used + grid > g_clk_cap) return nullptr;
+    uint64_t* p = g_clk_buf + 4 * g_clk_used;
+    g_clk_used += grid;
+    return p;
+}
 
 static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -96,7 +111,23 @@ const char* qdt_status_string(qdt_status s) {
     return "unknown qdt_status";
 }
 
-const char* qdt_version(void) { return "qdt 0.1 gfx950"; }
+const char* qdt_version(void) { return "qdt 0.2 gfx950"; }
+
+qdt_status qdt_clock_record(uint64_t* buf, int64_t entries) {
+    if (buf && (entries <= 0 || (reinterpret_cast<uintptr_t>(buf) & 7u) != 0)) return QDT_EINVAL;
+    std::lock_guard<std::mutex> lk(g_clk_mu);
+    g_clk_buf = buf;
+    g_clk_cap = buf ? entries : 0;
+    g_clk_used = 0;
+    return QDT_OK;
+}
+
+qdt_status qdt_clock_record_used(int64_t* entries) {
+    if (!entries) return QDT_EINVAL;
+    std::lock_guard<std::mutex> lk(g_clk_mu);
+    *entries = g_clk_used;
+    return QDT_OK;
+}
 
 qdt_status qdt_channel_absmax(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, float* s, int accumulate,
                               void* stream) {
@@ -316,6 +347,7 @@ static qdt_status linear_impl(const int8_t* Xq, const float* x_scale, const int8
     a.Y = Y;
     a.ldy = ldy;
     a.ws = reinterpret_cast<int32_t*>(workspace);
+    a.clk = clock_record_take(p.grid);
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;

@@ -223,12 +223,22 @@ attn_fwd_kernel(AttnArgs p) {
             hook(g);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (drain) mfma_drain();
+        if (drain) {
+            mfma_drain();
+#pragma unroll
+            for (int kf = 0; kf < 2; ++kf)
+#pragma unroll
+                for (int qf = 0; qf < 4; ++qf) keep_after_v(s[kf][qf]);
+        }
     };
     // keys past S get -inf
     auto mask_tail = [&](int jt) __attribute__((always_inline)) {
         if ((jt + 1) * AT_BK > p.S) {
             mfma_drain();
+#pragma unroll
+            for (int kf = 0; kf < 2; ++kf)
+#pragma unroll
+                for (int qf = 0; qf < 4; ++qf) keep_after_v(s[kf][qf]);
 #pragma unroll
             for (int kf = 0; kf < 2; ++kf)
 #pragma unroll
@@ -364,7 +374,9 @@ attn_fwd_kernel(AttnArgs p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) softmax_piece(qf, i, pprev);
     }
-    for (int jt = 1; jt <= nkt; ++jt) {
+    // nkt >= 1.  The loop leaves only through the drain, so the register copies the compiler places
+    // on its exit edge read finished accumulators.
+    for (int jt = 1;; ++jt) {
         const int buf = jt & 1, jn = min(jt + 1, nkt - 1), jv = min(jt, nkt - 1);
         wait_vmcnt<0>();
         __syncthreads();
@@ -381,6 +393,10 @@ attn_fwd_kernel(AttnArgs p) {
         pv(buf ^ 1, pprev, true, pnew);
 #pragma unroll
         for (int qf = 0; qf < 4; ++qf) pprev[qf] = pnew[qf];
+        if (jt == nkt) {
+            mfma_drain();
+            break;
+        }
     }
     wait_vmcnt<0>();  // the last iteration's LDS-DMAs land before the workgroup ends
     if constexpr (!EXACT) {
@@ -392,6 +408,10 @@ attn_fwd_kernel(AttnArgs p) {
         if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) p.redo[t] = 1;
     }
     mfma_drain();
+#pragma unroll
+    for (int df = 0; df < 16; ++df)
+#pragma unroll
+        for (int qf = 0; qf < 4; ++qf) keep_after_a(oacc[df][qf]);
 
     // ---- normalize by the full row sums and store 4 consecutive dims per lane
 #pragma unroll

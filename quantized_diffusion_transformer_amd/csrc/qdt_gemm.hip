@@ -49,6 +49,7 @@ struct KArgs {
     const uint8_t* wsc;
     void* Y;
     int32_t* ws;
+    uint64_t* clk;       // clock record: 4 words per workgroup (start / end shader cycles and real time), or null
     int64_t ldy;
     float eps;
     int M, N, Kb, F;
@@ -152,6 +153,13 @@ gemm_kernel(KArgs p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave % WN, wm = wave / WN;
+    // clock record (diagnostic, off unless armed): wave 0 reads the shader-clock counter and the
+    // fixed 100 MHz real-time counter here and after its last store
+    uint64_t clk_c0 = 0, clk_r0 = 0;
+    if (p.clk != nullptr && wave == 0) {
+        clk_c0 = __builtin_amdgcn_s_memtime();
+        clk_r0 = __builtin_amdgcn_s_memrealtime();
+    }
 
     // ---- workgroup id -> (tile, K slice), contiguous per XCD
     const int bid = blockIdx.x, nb = gridDim.x;
@@ -447,6 +455,15 @@ gemm_kernel(KArgs p) {
     }
     wait_vmcnt<0>();
     mfma_drain();
+#pragma unroll
+    for (int g = 0; g < FN; ++g)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            if (g * FM + fm < NACC_A)
+                keep_after_a(acc[g][fm]);
+            else
+                keep_after_v(acc[g][fm]);
+        }
 
     // ---------------------------------------------------------------- epilogues
     // Staged parameters of tile weight rows rl .. rl+3 and tile token row.
@@ -702,11 +719,45 @@ gemm_kernel(KArgs p) {
                 return make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
             });
     }
+    if (p.clk != nullptr && wave == 0) {
+        const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+        if (lane == 0) {
+            uint64_t* o = p.clk + 4 * (int64_t)blockIdx.x;
+            o[0] = clk_c0;
+            o[1] = clk_r0;
+            o[2] = c1;
+            o[3] = r1;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------- split-K epilogue
+// Sum of y^2 over one 256-wide head, in exactly the order of the fused RMSNorm epilogue, so that
+// a split plan gives the same bits as the fused one.  Lane L of the wave holds columns 4L .. 4L+3
+// of the head (y[0..3]).  In the fused kernel the head is split between two waves of 128 columns;
+// there lane group q (lanes 16q .. 16q+15 of a fragment row) sums the squares of columns
+// 128 wn + 16 fn + 4 q + r in the order fn = 0..7, r = 0..3; the four lane-group sums are combined
+// as (P0 + P1) + (P2 + P3) and the two waves' totals as T0 + T1.  Here that column is held by
+// lane 32 wn + 4 fn + q.
+__device__ __forceinline__ float head_sumsq_fused_order(const float (&y)[4], int lane) {
+    float sq[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sq[r] = y[r] * y[r];
+    const int base = (lane & 32) | (lane & 3);
+    float p = 0.0f;
+#pragma unroll
+    for (int fn = 0; fn < 8; ++fn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p += __shfl(sq[r], base | (fn << 2), 64);
+    p += __shfl_xor(p, 1, 64);
+    p += __shfl_xor(p, 2, 64);
+    return __shfl(p, 0, 64) + __shfl(p, 32, 64);
+}
+
 // Sums the S int32 partial slices (exact, any order) and applies the same epilogue
-// arithmetic as the fused kernel.  BIAS / SILU / ACC: one thread per 4 output columns.
+// arithmetic as the fused kernel, including its order of the head RMSNorm's sum of squares, so
+// every plan gives the same bits.  BIAS / SILU / ACC: one thread per 4 output columns; RMSNORM:
+// one wave per (row, head).
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_epi_kernel(KArgs p) {
     const int64_t MN = (int64_t)p.M * p.N;
@@ -729,13 +780,10 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(KArgs p) {
             b[0] = bf16_to_f32(bb.x & 0xFFFFu); b[1] = bf16_to_f32(bb.x >> 16);
             b[2] = bf16_to_f32(bb.y & 0xFFFFu); b[3] = bf16_to_f32(bb.y >> 16);
         }
-        float y[4], ss = 0.0f;
+        float y[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            y[r] = dequant(a[r], sx, swv[r], b[r]);
-            ss += y[r] * y[r];
-        }
-        ss = wave_sum(ss);
+        for (int r = 0; r < 4; ++r) y[r] = dequant(a[r], sx, swv[r], b[r]);
+        const float ss = head_sumsq_fused_order(y, lane);
         const float ms = ss / (float)p.head_dim;
         const float rinv = 1.0f / sqrtf(ms + p.eps);
         uint2 gg = *reinterpret_cast<const uint2*>(p.gamma + d);
@@ -823,6 +871,7 @@ static KArgs make_kargs(const GemmArgs& a, const Plan& pl, int esize) {
     k.head_dim = 256;
     k.xsc = nullptr;
     k.wsc = nullptr;
+    k.clk = a.clk;
     return k;
 }
 
@@ -913,14 +962,11 @@ __global__ __launch_bounds__(256) void splitk_f32_epi_kernel(KArgs p) {
         const int m = (int)(item / heads), h = (int)(item % heads);
         const int d = lane * 4, n = h * p.head_dim + d;
         const v4f a = sum4((int64_t)m * p.N + n);
-        float b[4], y[4], ss = 0.0f;
+        float b[4], y[4];
         bias4(n, b);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            y[r] = a[r] + b[r];
-            ss += y[r] * y[r];
-        }
-        ss = wave_sum(ss);
+        for (int r = 0; r < 4; ++r) y[r] = a[r] + b[r];
+        const float ss = head_sumsq_fused_order(y, lane);
         const float rinv = 1.0f / sqrtf(ss / (float)p.head_dim + p.eps);
         const uint2 gg = *reinterpret_cast<const uint2*>(p.gamma + d);
         const float g[4] = {bf16_to_f32(gg.x & 0xFFFFu), bf16_to_f32(gg.x >> 16), bf16_to_f32(gg.y & 0xFFFFu),

@@ -54,11 +54,15 @@ struct GemmArgs {
     void* Y;
     int64_t ldy;
     int32_t* ws;         // split-K partials [S][M][N]
+    uint64_t* clk;       // clock record of the GEMM kernel (4 words per workgroup) or null
     int M, N, K;         // K in elements
     int epi;             // EpiKind for the fused epilogue (EPI_PARTIAL when split)
 };
 
 hipError_t launch_gemm_i8(const GemmArgs& a, const Plan& p, hipStream_t st);
+// Clock record of the W8A8 GEMM (diagnostic): the next `grid` 4-word entries of the armed record
+// buffer, or null when the record is off or full.
+uint64_t* clock_record_take(int grid);
 hipError_t launch_gemm_bf16(const GemmArgs& a, const Plan& p, hipStream_t st);
 // Block-scaled FP4 GEMM (256 x 256 tiles; a K split writes fp32 partials to a.ws): a.K is the element count; xsc / wsc the
 // biased block exponents [M][K/32] / [N][K/32]; a.epi EPI_F32BIAS, EPI_F32SILU, EPI_F32RMSNORM or

@@ -19,6 +19,18 @@ __device__ __forceinline__ void mfma_drain() {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
+// Pins a register value after the preceding volatile asm statements (an mfma_drain): the empty asm
+// "writes" it, so no read of it can be scheduled above the drain.  Volatile asm statements keep
+// their order, so the drain's wait states always separate the last MFMA from the first read.
+template <typename T>
+__device__ __forceinline__ void keep_after_a(T& v) {
+    asm volatile("" : "+a"(v));
+}
+template <typename T>
+__device__ __forceinline__ void keep_after_v(T& v) {
+    asm volatile("" : "+v"(v));
+}
+
 // LDS-DMA of one dword per lane (global_load_lds_dword): lane l writes LDS m0 + 4 l.
 __device__ __forceinline__ void lds_dma4(uint32_t lds_addr, const void* gptr) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr), "v"(gptr)

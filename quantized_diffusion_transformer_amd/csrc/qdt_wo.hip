@@ -364,14 +364,24 @@ wo_gemm_kernel(WoKArgs p) {
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) a[f][pr] = deq_pair(S0, f, 0, pr, d0, n0d);
     }
-    for (int j = 0; j < nk; j += 4) {
+    // nk is a positive multiple of 4 (K % 512 == 0).  The loop leaves only through the drain, so
+    // the register copies the compiler places on its exit edge read finished accumulators.
+    for (int j = 0;; j += 4) {
         stage(j, S0, S1, S2, 0);
         stage(j + 1, S1, S2, S3, 1);
         stage(j + 2, S2, S3, S0, 0);
         stage(j + 3, S3, S0, S1, 1);
+        if (j + 4 >= nk) {
+            mfma_drain();
+            break;
+        }
     }
     wait_vmcnt<0>();  // the clamped LDS-DMAs of the last stage land before the workgroup ends
     mfma_drain();
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) keep_after_a(acc[f][fm]);
 
     // ---------------------------------------------------------------- epilogue
     // Lane l of fragment (f, fm) holds outputs of token row m0 + 16 fm + (l & 15) and weight rows

@@ -109,6 +109,34 @@ def test_smooth_prepare_without_smoothing_and_accumulated_calibration():
     assert bits_equal(to_host(s), oracle.channel_absmax(d["X"]))
 
 
+def test_smooth_prepare_zero_channels_and_zero_weight_rows():
+    # lambda = 1 where s_j = 0 or w_j = 0 (both, for one column); an all-zero weight row gets
+    # scale 0 and codes 0, and its outputs are the bias exactly
+    announce("prepare zero channels / zero weight rows")
+    M, N, K = 300, 256, 1024
+    d = W.make_linear(M, N, K, seed=23, x_kind="pct1")
+    X, Wt = d["X"].copy(), d["W"].copy()
+    zx, zw, zr = [3, 100, 517, 1023], [5, 100, 900], [7, 200, 255]
+    X[:, zx] = 0
+    Wt[:, zw] = 0
+    Wt[zr, :] = 0
+    d = dict(d, X=X, W=Wt)
+    ref, dev = prepared(d)
+    assert_stages_exact(ref, dev)
+    lam, inv, sw, Wq = (to_host(dev[k]) for k in ("lam", "inv", "sw", "Wq"))
+    for j in sorted(set(zx) | set(zw)):
+        assert lam[j] == 1.0 and inv[j] == 1.0, j
+    assert np.all(sw[zr] == 0) and np.all(Wq[zr] == 0)
+    assert np.all(sw[np.setdiff1d(np.arange(N), zr)] > 0)
+    b = to_dev(d["bias"])
+    Y = qdt.w8a8_linear(dev["Xq"], dev["sx"], dev["Wq"], dev["sw"], b, "bias")
+    torch.cuda.synchronize()
+    Y = to_host(Y)
+    Y_ref = oracle.epilogue(oracle.gemm_i32(ref["Xq"], ref["Wq"]), ref["sx"], ref["sw"], d["bias"], "bias")
+    assert bits_equal(Y, Y_ref)
+    assert np.all(Y[:, zr] == d["bias"][zr][None, :])
+
+
 def test_smooth_prepare_other_alpha_close():
     # alpha != 0.5 uses powf on both sides; parity unpinned bit-wise (tolerance only)
     announce("prepare alpha 0.25")
@@ -261,6 +289,19 @@ def test_results_do_not_depend_on_plan():
     sub = qdt.w8a8_linear(dev["Xq"][:37], dev["sx"][:37], dev["Wq"], dev["sw"], b, "bias")
     torch.cuda.synchronize()
     assert bits_equal(to_host(sub), outs[0][:37])
+
+
+@pytest.mark.parametrize("epi", ["head_rmsnorm", "silu_gate"])
+def test_fused_epilogues_do_not_depend_on_plan(epi):
+    # the gated SiLU and the head RMSNorm give the same bits under every tile and K split: the
+    # split-K epilogue sums a head's squares in the fused kernel's order
+    announce(f"plan independence {epi}")
+    d = W.make_linear(600, 1024, 2048, seed=43, x_kind="pct1", epi=epi)
+    outs = [run_linear(d, epi, t, s)[0] for t, s in ((None, None), (qdt.QDT_TILE_256, 1), (qdt.QDT_TILE_256, 3),
+                                                     (qdt.QDT_TILE_256, 7), (qdt.QDT_TILE_288x256, 1),
+                                                     (qdt.QDT_TILE_288x256, 2))]
+    for o in outs[1:]:
+        assert bits_equal(o, outs[0]), f"{np.sum(o != outs[0])} elements differ between plans"
 
 
 def test_zero_rows_give_bias_and_padding_keeps_rows():

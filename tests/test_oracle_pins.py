@@ -544,6 +544,84 @@ def test_mx_gemm_exact_against_rationals():
             assert Fraction(float(acc[m, n])) == exact
 
 
+def _fp4_grid_operands(rng, rows, K):
+    """bf16 rows whose values lie on the FP4 grid with block exponent 0: every 32-element block
+    holds a 4 or a 6, so its max is in [4, 8) and its scale is 2^0; the decoded values are then
+    the values themselves (the lossless round trip is pinned above)."""
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    v = grid[rng.integers(0, 8, (rows, K))] * rng.choice([-1.0, 1.0], (rows, K))
+    v[:, ::32] = rng.choice([-6.0, -4.0, 4.0, 6.0], (rows, K // 32))
+    return v
+
+
+def _bf16_rne_torch(x):
+    """fp32 -> bf16 bit patterns through torch's own cast (round half to even), independent of
+    the oracle's conversion."""
+    torch = pytest.importorskip("torch")
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_mx_bias_epilogue_closed_form():
+    # y = fp32(acc) + bias (one fp32 addition), then bf16: on grid operands acc is an exact
+    # multiple of 1/4 computed here in integers, so the output is fixed by the closed form.
+    # Dropping the bias, adding it after the bf16 rounding, or taking the wrong row's bias fails.
+    rng = np.random.default_rng(36)
+    M, N, K = 5, 48, 128
+    xv, wv = _fp4_grid_operands(rng, M, K), _fp4_grid_operands(rng, N, K)
+    Xq, Xs = oracle.mxfp4_quantize(bf(xv))
+    Wq, Ws = oracle.mxfp4_quantize(bf(wv))
+    assert np.all(Xs == 127) and np.all(Ws == 127)
+    acc4 = (xv * 2).astype(np.int64) @ (wv * 2).astype(np.int64).T   # 4 acc, exact integers
+    acc = acc4.astype(np.float64) / 4.0
+    bias = bf(rng.standard_normal(N) * 40.0 + 0.3)
+    Y, got_acc = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, want_acc=True, epi="bias")
+    assert np.array_equal(got_acc, acc)
+    want = _bf16_rne_torch(acc.astype(np.float32) + f32(bias)[None, :])
+    assert np.array_equal(Y, want)
+    assert not np.array_equal(Y, _bf16_rne_torch(acc.astype(np.float32)))          # bias dropped
+    assert not np.array_equal(Y, _bf16_rne_torch(acc.astype(np.float32) + f32(bias)[::-1][None, :]))
+    # no bias: y = fp32(acc)
+    Y0 = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, None, epi="bias")
+    assert np.array_equal(Y0, _bf16_rne_torch(acc.astype(np.float32)))
+    # selected rows are the same rows of the full result
+    rows = np.array([4, 0, 2])
+    assert np.array_equal(oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, rows, epi="bias"), Y[rows])
+
+
+def test_mx_silu_gate_epilogue_closed_form():
+    # W rows [gate (0..F-1); up (F..2F-1)], g = fp32(acc_g) + b_g, u = fp32(acc_u) + b_u,
+    # Y = bf16(silu(g) * u): within 1 bf16 ulp of the fp64 closed form on exact accumulators.
+    # Gate and up are drawn with different scales, so swapping them, pairing gate f with up
+    # row f + 1, or giving both halves the gate's bias moves some output by more than 1 ulp.
+    from scipy.special import expit
+    rng = np.random.default_rng(37)
+    M, F, K = 6, 40, 96
+    xv = _fp4_grid_operands(rng, M, K)
+    wg, wu = _fp4_grid_operands(rng, F, K) * 0.125, _fp4_grid_operands(rng, F, K)
+    Xq, Xs = oracle.mxfp4_quantize(bf(xv))
+    Wq, Ws = oracle.mxfp4_quantize(bf(np.concatenate([wg, wu])))
+    ag = (xv * 2).astype(np.int64) @ (wg * 16).astype(np.int64).T / 32.0   # exact
+    au = (xv * 2).astype(np.int64) @ (wu * 2).astype(np.int64).T / 4.0
+    bias = bf(np.concatenate([rng.standard_normal(F) * 0.5, rng.standard_normal(F) * 3.0 + 1.0]))
+    bg, bu = f32(bias)[:F].astype(np.float64), f32(bias)[F:].astype(np.float64)
+    Y, acc = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, want_acc=True, epi="silu_gate")
+    assert Y.shape == (M, F)
+    assert np.array_equal(acc[:, :F], ag) and np.array_equal(acc[:, F:], au)
+    g = ag.astype(np.float32).astype(np.float64) + bg[None, :]
+    u = au.astype(np.float32).astype(np.float64) + bu[None, :]
+    want = g * expit(g) * u
+    assert ulp_dist_bf16(Y, _bf16_rne_torch(want)).max() <= 1
+    assert np.abs(g).max() > 4 and np.abs(u - g).max() > 4       # the two roles are far apart
+    for wrong in (u * expit(u) * g,                               # gate and up swapped
+                  g * expit(g) * np.roll(u, 1, axis=1),           # up row of the next gate
+                  g * expit(g) * (u - bu + bg)):                  # the gate's bias on both halves
+        assert ulp_dist_bf16(Y, _bf16_rne_torch(wrong)).max() > 1
+    # zero gate gives zero; zero up gives zero
+    Yz = oracle.mxfp4_gemm_rows(np.zeros_like(Xq), np.full_like(Xs, 0), Wq, Ws, None, epi="silu_gate")
+    assert np.all(f32(Yz) == 0)
+
+
 def test_bf16_gemm_within_fp64_bound():
     rng = np.random.default_rng(14)
     M, N, K = 9, 13, 512

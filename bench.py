@@ -502,6 +502,7 @@ def extra_workloads(args, only=None):
                 ev[2].record()
         steps, warm = counts(step)
         ms, tq, tg = time_loop_best(step, steps, warm)
+        clk = clock_during(step, [None], qdt, launches=30, grid=plan["grid"])["clock_mhz"]
         ops = 2.0 * M * N * K
         g = stats(tg)["mean"]
         r = {"M": M, "N": N, "K": K, "epilogue": epi, "plan": plan, "steps": steps, "warmup": warm,
@@ -509,6 +510,8 @@ def extra_workloads(args, only=None):
              "eff_tops": round(ops / (ms * 1e-3) / 1e12, 1), "gemm_ms": round(g, 4),
              "gemm_tops": round(ops / (g * 1e-3) / 1e12, 1),
              "gemm_frac_int8_peak": round(ops / (g * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+             "gemm_clock_mhz": round(clk, 1),
+             "gemm_frac_at_measured_clock": round(ops / (g * 1e-3) / 1e12 / (PEAK_INT8_TOPS * clk / 2400.0), 4),
              "quantize_ms": round(stats(tq)["mean"], 4)}
         if extra:
             r.update(extra(Y))
@@ -663,7 +666,7 @@ def mxfp4_workload(src, epi, counts):
     Wq, Ws = qdt.mxfp4_quantize(to_dev(d["W"]))
     b = None if d.get("bias") is None else to_dev(d["bias"])
     Xq = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
-    Xs = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+    Xs = torch.empty((K // 256, M, 8), dtype=torch.uint8, device="cuda")
     Y = torch.empty((M, N // 2 if epi == "silu_gate" else N), dtype=torch.bfloat16, device="cuda")
     g = to_dev(d["gamma"]) if epi == "head_rmsnorm" else None
     plan = qdt.mxfp4_linear_plan(M, N, K, epi)
@@ -680,6 +683,7 @@ def mxfp4_workload(src, epi, counts):
             ev[2].record()
     steps, warm = counts(step)
     ms, tq, tg = time_loop_best(step, steps, warm)
+    clk = clock_during(step, [None], qdt, launches=30, grid=plan["grid"])["clock_mhz"]
     ops = 2.0 * M * N * K
     g = stats(tg)["mean"]
     qb = 2 * M * K + M * K // 2 + M * K // 32
@@ -688,6 +692,8 @@ def mxfp4_workload(src, epi, counts):
             "eff_tops": round(ops / (ms * 1e-3) / 1e12, 1), "gemm_ms": round(g, 4),
             "gemm_tops": round(ops / (g * 1e-3) / 1e12, 1),
             "gemm_frac_fp4_peak": round(ops / (g * 1e-3) / 1e12 / PEAK_FP4_TOPS, 4),
+            "gemm_clock_mhz": round(clk, 1),
+            "gemm_frac_at_measured_clock": round(ops / (g * 1e-3) / 1e12 / (PEAK_FP4_TOPS * clk / 2400.0), 4),
             "quantize_ms": round(stats(tq)["mean"], 4),
             "quantize_gbs": round(qb / (stats(tq)["mean"] * 1e-3) / 1e9, 1)}
 

@@ -180,14 +180,19 @@ qdt_status qdt_adaln_quantize(const uint16_t* X, int64_t ldx, const uint16_t* sh
  * cores ([FAL]: the DiT runs in a block-scaled 4-bit floating-point format).  Per block of 32
  * consecutive elements of a row, v = (float)X[m][j] * colmul[j] (v = (float)X[m][j] when colmul is
  * NULL):
- *   e = clamp(floor(log2(max |v|)) - 2, -127, 127)  (-127 for an all-zero block); S[m][b] = e + 127
+ *   e = clamp(floor(log2(max |v|)) - 2, -127, 127)  (-127 for an all-zero block), stored as e + 127
  *   code_j = nearest of {0, 0.5, 1, 1.5, 2, 3, 4, 6} to |v_j| / 2^e (ties to the even mantissa,
  *            saturating at 6), sign in bit 3, zero stored as +0
  *   Q[m][j / 2] holds code_j in its low nibble for even j, high nibble for odd j.
+ *   S holds the biased exponents stage-major, uint8 [K/256][M][8]: the 8 blocks of row m in
+ *   elements 256 s .. 256 s + 255 sit in the 8 bytes S[s][m][*], block 8 s + w at byte
+ *   2 (w % 4) + w / 4 (order w = 0, 4, 1, 5, 2, 6, 3, 7).  A tile of the GEMM then finds a stage's
+ *   exponents of its rows in one contiguous span, and a matrix-core lane finds the two blocks it
+ *   needs in a stage side by side.
  *   Used for the activations (colmul = inv_lambda or NULL, per step) and for the weights (colmul =
  *   lambda or NULL, offline).  X: bf16 [M, ldx] (first K columns).  Q: uint8 [M, K/2].  S: uint8
- *   [M, K/32].  K % 64 == 0, ldx >= K, ldx % 8 == 0; X, colmul and Q 16-byte aligned.  Bit-exact.
- *   M = 0 is a no-op.
+ *   M K / 32 bytes as above.  K % 256 == 0, ldx >= K, ldx % 8 == 0; X, colmul and Q 16-byte aligned.
+ *   Bit-exact.  M = 0 is a no-op.
  */
 qdt_status qdt_mxfp4_quantize(const uint16_t* X, const float* colmul, int64_t M, int64_t K, int64_t ldx,
                               uint8_t* Q, uint8_t* S, void* stream);
@@ -203,10 +208,10 @@ qdt_status qdt_mxfp4_quantize(const uint16_t* X, const float* colmul, int64_t M,
  *   QDT_EPI_HEAD_RMSNORM: y = acc + bias; per row and head of 256 columns r = 1/sqrtf(mean(y^2) + eps),
  *     Y = bf16_rne((y * r) * gamma[n mod 256]) (epi_params: qdt_rmsnorm_params, as for qdt_w8a8_linear);
  *   QDT_EPI_ACC_F32: Y fp32 [M, ldy], the accumulators.
- *   Xq / Xs: qdt_mxfp4_quantize of the activations ([M, K/2] codes, [M, K/32] exponents); Wq / Ws
- *   the same of the weights ([N, K/2], [N, K/32]).  K % 256 == 0 (whole 128-byte stages of codes),
- *   N % 16 == 0, ldy >= N (F for the gated SiLU), ldy % 8 == 0; code and Y pointers 16-byte aligned,
- *   exponent rows 4-byte aligned (K % 128 == 0 gives that).  Y must not overlap an input.
+ *   Xq / Xs: qdt_mxfp4_quantize of the activations ([M, K/2] codes, [K/256][M][8] exponents); Wq /
+ *   Ws the same of the weights ([N, K/2], [K/256][N][8]).  K % 256 == 0 (whole 128-byte stages of
+ *   codes), N % 16 == 0, ldy >= N (F for the gated SiLU), ldy % 8 == 0; code and Y pointers 16-byte
+ *   aligned, exponent pointers 4-byte aligned.  Y must not overlap an input.
  *   When the plan splits K (deep K, few output tiles: qdt_mxfp4_linear_plan), the slices write fp32
  *   partial sums to `workspace` (plan.workspace_bytes = split_k * M * N * 4, 16-byte aligned, caller
  *   owned) and a second kernel adds them in slice order before the epilogue; otherwise workspace may
@@ -347,8 +352,9 @@ qdt_status qdt_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V
 qdt_status qdt_attention_workspace_size(int64_t S, int64_t H, size_t* bytes);
 
 /*
- * Clock record (diagnostic; not part of the layer).  While a buffer is armed, every W8A8 GEMM
- * kernel that qdt_w8a8_linear / qdt_w8a8_linear_planned launch takes the next `grid` entries of it
+ * Clock record (diagnostic; not part of the layer).  While a buffer is armed, every GEMM kernel
+ * that qdt_w8a8_linear, qdt_w8a8_linear_planned, qdt_mxfp4_linear and
+ * qdt_bf16_linear launch (not their split-K sums) takes the next `grid` entries of it
  * (one per workgroup, in workgroup-id order) as long as they fit; launches that do not fit record
  * nothing.  Entry = 4 uint64: the shader-clock counter (s_memtime) and the 100 MHz real-time
  * counter (s_memrealtime) read by the workgroup's first wave when it starts, then the same two

@@ -223,14 +223,15 @@ def adaln_modulate(X: torch.Tensor, shift: torch.Tensor | None, scale: torch.Ten
 
 
 def mxfp4_quantize(X: torch.Tensor, colmul: torch.Tensor | None = None, Q=None, S=None, stream=None):
-    """Block-scaled FP4 of bf16 X [M, K] (times colmul): (codes uint8 [M, K/2], exponents uint8 [M, K/32])."""
+    """Block-scaled FP4 of bf16 X [M, K] (times colmul): (codes uint8 [M, K/2], biased block exponents
+    uint8 [K/256, M, 8], stage-major: byte 2 (w % 4) + w / 4 of S[s, m] is block 8 s + w of row m)."""
     _dev(X, torch.bfloat16, "X")
     X, ldx = _rows(X, "X")
     M, K = X.shape
     if Q is None:
         Q = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
     if S is None:
-        S = torch.empty((M, K // 32), dtype=torch.uint8, device=X.device)
+        S = torch.empty((K // 256, M, 8), dtype=torch.uint8, device=X.device)
     _check(qdt_mxfp4_quantize(_ptr(X), _ptr(colmul), M, K, ldx, _ptr(Q), _ptr(S), _stream(stream)),
            "qdt_mxfp4_quantize")
     return Q, S
@@ -252,14 +253,14 @@ def mxfp4_linear(Xq: torch.Tensor, Xs: torch.Tensor, Wq: torch.Tensor, Ws: torch
     """Block-scaled FP4 linear: bf16 [M, N] = acc + bias ("bias"), bf16 [M, N/2] = silu(gate) * up
     ("silu_gate", W rows [gate; up]), RMSNorm of acc + bias over 256-wide heads with gamma
     ("head_rmsnorm"), or the fp32 accumulators ("acc_f32").
-    Xq uint8 [M, K/2] and Xs uint8 [M, K/32] from mxfp4_quantize of the activations; Wq, Ws the
+    Xq uint8 [M, K/2] and Xs uint8 [K/256, M, 8] from mxfp4_quantize of the activations; Wq, Ws the
     same of the weights."""
     for t, n in ((Xq, "Xq"), (Xs, "Xs"), (Wq, "Wq"), (Ws, "Ws")):
         _dev(t, torch.uint8, n)
     if bias is not None:
         _dev(bias, torch.bfloat16, "bias")
     M, N, K = Xq.shape[0], Wq.shape[0], Xq.shape[1] * 2
-    if Wq.shape[1] * 2 != K or Xs.shape != (M, K // 32) or Ws.shape != (N, K // 32):
+    if Wq.shape[1] * 2 != K or Xs.shape != (K // 256, M, 8) or Ws.shape != (K // 256, N, 8):
         raise ValueError("mxfp4_linear: inconsistent operand shapes")
     epi = _MX_EPI[epilogue]
     params = None

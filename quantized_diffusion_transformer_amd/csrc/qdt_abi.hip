@@ -222,7 +222,7 @@ qdt_status qdt_mxfp4_quantize(const uint16_t* X, const float* colmul, int64_t M,
                               uint8_t* S, void* stream) {
     if (M < 0) return QDT_ESHAPE;
     if (M > 0 && (!X || !Q || !S)) return QDT_EINVAL;
-    if (K <= 0 || K % 64 != 0 || K > QDT_MAX_K || ldx < K || M > INT32_MAX) return QDT_ESHAPE;
+    if (K <= 0 || K % 256 != 0 || K > QDT_MAX_K || ldx < K || M > INT32_MAX) return QDT_ESHAPE;
     if (!aligned16(X) || !aligned16(colmul) || !aligned16(Q) || ldx % 8 != 0) return QDT_EALIGN;
     if (M == 0) return QDT_OK;
     const int64_t xb = ((M - 1) * ldx + K) * 2, qb = M * K / 2, sb = M * K / 32;
@@ -399,6 +399,7 @@ qdt_status qdt_bf16_linear(const uint16_t* X, const uint16_t* W, const uint16_t*
     a.N = (int)N;
     a.K = (int)K;
     a.epi = EPI_F32BIAS;
+    a.clk = clock_record_take(p.grid);
     return hip_status(launch_gemm_bf16(a, p, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -474,6 +475,7 @@ qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t*
             : epi == QDT_EPI_SILU_GATE     ? EPI_F32SILU
             : epi == QDT_EPI_HEAD_RMSNORM  ? EPI_F32RMSNORM
                                            : EPI_F32BIAS;
+    a.clk = clock_record_take(p.grid);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if ((r = hip_status(launch_gemm_mx(a, Xs, Ws, p, st))) != QDT_OK) return r;
     if (p.split_k > 1) return hip_status(launch_splitk_f32_epilogue(a, p.split_k, a.epi, st));

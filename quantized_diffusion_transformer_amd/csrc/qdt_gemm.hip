@@ -29,7 +29,9 @@
 //     exactly the bytes of two int8 K steps, and v_mfma_scale_f32_16x16x128_f8f6f4 reads its
 //     fragments in the int8 layout.  Its per-lane block exponents (lane l covers the 32 elements
 //     of one block) ride along in LDS: 8 bytes per row and stage, copied by dword LDS-DMAs with
-//     the operand rows and read as single bytes beside the fragments.
+//     the operand rows and read as single bytes beside the fragments.  The exponents are stored
+//     stage-major (all rows' bytes of one 256-element stage together), so those LDS-DMAs read
+//     whole cache lines.
 #include <type_traits>
 
 #include "qdt_device.h"
@@ -225,23 +227,27 @@ gemm_kernel(KArgs p) {
     auto dma = [&](int buf, int stage, int i) __attribute__((always_inline)) {
         lds_dma16_s(ldsw + (uint32_t)(buf * STAGE + i * 1024), voff(i), wbase + (int64_t)stage * BK);
     };
-    // FP4 block exponents: dword LDS-DMA i of a wave copies rows rlocal0 + 32 i .. + 31 of its
-    // region (lane l: row + l / 2, dword l % 2), to LDS [row][8 bytes] of the stage
+    // FP4 block exponents, stored stage-major: for each 256-element stage, every row's 8 exponent
+    // bytes are consecutive and rows follow each other (a stage's exponents of R rows are 8 R
+    // contiguous bytes).  Dword LDS-DMA i of a wave copies rows rlocal0 + 32 i .. + 31 of its region
+    // (lane l: row + l / 2, dword l % 2, i.e. 256 contiguous bytes) to LDS [row][8 bytes] of the
+    // stage.
     uint32_t scvoffs[NSC > 0 ? NSC : 1];
     const uint8_t* scbase = nullptr;
     uint32_t ldss = 0;
+    int64_t sstride = 0;  // exponent bytes per stage of the wave's operand (8 x its row count)
     if constexpr (MX) {
-        const int64_t scb = Kb / 16;  // exponent bytes per row: K / 32 = 2 Kb / 32
         const int wrow0 = (SILU && wave == 1 ? p.F : 0) + n0;  // the up half's rows for SILU
-        scbase = uniform_ptr((wwave ? p.wsc + (int64_t)wrow0 * scb : p.xsc + (int64_t)m0 * scb) + (int64_t)kta * 8);
+        sstride = __builtin_amdgcn_readfirstlane(wwave ? p.N : p.M) * (int64_t)8;
+        scbase = uniform_ptr((wwave ? p.wsc + (int64_t)wrow0 * 8 : p.xsc + (int64_t)m0 * 8) + (int64_t)kta * sstride);
 #pragma unroll
         for (int i = 0; i < NSC; ++i)
-            scvoffs[i] = (uint32_t)(min(rlocal0 + i * 32 + (lane >> 1), rlast) * scb) + (lane & 1) * 4;
+            scvoffs[i] = (uint32_t)(min(rlocal0 + i * 32 + (lane >> 1), rlast) * 8) + (lane & 1) * 4;
         const int row0 = wwave ? wave * NIW * 8 : BN + (wave - 2) * NIX * 8;
         ldss = __builtin_amdgcn_readfirstlane(lds_offset(smem_sc) + row0 * 8);
     }
     auto sdma = [&](int buf, int stage, int i) __attribute__((always_inline)) {
-        lds_dma4_s(ldss + (uint32_t)(buf * SCST + i * 256), scvoffs[i], scbase + (int64_t)stage * 8);
+        lds_dma4_s(ldss + (uint32_t)(buf * SCST + i * 256), scvoffs[i], scbase + (int64_t)stage * sstride);
     };
 
     // Global weight row of tile weight row r (clamped like the operand rows).
@@ -304,10 +310,11 @@ gemm_kernel(KArgs p) {
         }
     };
     // FP4: the block exponent of this lane's row (lane & 15) of a fragment starting at tile row
-    // `row`, K step ks of the stage (lane group lane >> 4 covers block 4 ks + (lane >> 4))
-    const int sclane = (lane & 15) * 8 + (lane >> 4);
+    // `row`, K step ks of the stage: lane group q = lane >> 4 covers block 4 ks + q, stored at byte
+    // 2 q + ks of the row's 8 bytes
+    const int sclane = (lane & 15) * 8 + 2 * (lane >> 4);
     auto sc = [&](int buf, int row, int ks) __attribute__((always_inline)) {
-        return (uint32_t)smem_sc[buf * SCST + row * 8 + ks * 4 + sclane];
+        return (uint32_t)smem_sc[buf * SCST + row * 8 + ks + sclane];
     };
     auto frag = [&](const uint8_t* s, int row, int lck) __attribute__((always_inline)) {
         return *reinterpret_cast<const v4u*>(s + row * BK + lck);
@@ -413,7 +420,7 @@ gemm_kernel(KArgs p) {
         const uint32_t ldsd = ldsw + (uint32_t)((j % NB) * STAGE);
         const uint8_t* sbase = wbase + (int64_t)jd * BK;
         const uint32_t ldssd = ldss + (uint32_t)((j % NB) * SCST);
-        const uint8_t* scbased = MX ? scbase + (int64_t)jd * 8 : nullptr;
+        const uint8_t* scbased = MX ? scbase + (int64_t)jd * sstride : nullptr;
         (void)ldssd;
         (void)scbased;
         set_m0(ldsd);

@@ -560,7 +560,12 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
         packed &= 0x77777777u | ((mag + 0x77777777u) & 0x88888888u);
         if (ok) {
             *reinterpret_cast<uint32_t*>(Q + row * (K >> 1) + cc * 4) = packed;
-            if ((lane & 3) == 0) S[row * (K >> 5) + (cc >> 2)] = (uint8_t)(ex + 127);
+            // stage-major exponents: block b of the row goes to group b / 8 (256 elements), byte
+            // 2 (b % 4) + (b % 8) / 4 of the row's 8-byte slot in that group
+            if ((lane & 3) == 0) {
+                const int64_t b = cc >> 2, w = b & 7;
+                S[(b >> 3) * M * 8 + row * 8 + 2 * (w & 3) + (w >> 2)] = (uint8_t)(ex + 127);
+            }
         }
     }
 }

@@ -50,3 +50,25 @@ def sample_rows(M: int, n: int, seed: int = 0) -> np.ndarray:
     tail = list(range(max(0, M - (M % 256 or 256)), M))[:8]
     rows = np.unique(np.clip(np.concatenate([fixed, tail, rng.integers(0, M, n)]), 0, M - 1))
     return rows.astype(np.int64)
+
+
+# Block-scaled FP4 exponents as the library stores them: stage-major [K/256, rows, 8], block 8 s + w
+# of a row at byte MX_POS[w] of its 8-byte slot in stage s.  The oracle keeps them row-major
+# [rows, K/32]; these two permutations convert between the layouts (no arithmetic).
+MX_POS = np.array([0, 2, 4, 6, 1, 3, 5, 7])
+
+
+def mx_exponents_to_rows(S) -> np.ndarray:
+    """[K/256, rows, 8] (library) -> [rows, K/32] (oracle)."""
+    s = np.asarray(S)
+    st, rows, _ = s.shape
+    return np.ascontiguousarray(s[:, :, MX_POS].transpose(1, 0, 2).reshape(rows, st * 8))
+
+
+def mx_exponents_from_rows(S) -> np.ndarray:
+    """[rows, K/32] (oracle) -> [K/256, rows, 8] (library)."""
+    s = np.asarray(S)
+    rows, nb = s.shape
+    out = np.empty((nb // 8, rows, 8), s.dtype)
+    out[:, :, MX_POS] = s.reshape(rows, nb // 8, 8).transpose(1, 0, 2)
+    return out

@@ -81,12 +81,12 @@ def test_adaln_quantize_validation():
 
 def test_mxfp4_validation():
     q = qdt.qdt_mxfp4_quantize
-    assert q(A(), None, 4, 96, 96, A(0x200000), A(0x300000), None) == qdt.QDT_ESHAPE      # K % 64
-    assert q(A(), None, 4, 128, 64, A(0x200000), A(0x300000), None) == qdt.QDT_ESHAPE     # ldx < K
-    assert q(A(), None, 4, 128, 128, A(0x200008), A(0x300000), None) == qdt.QDT_EALIGN
-    assert q(A(), None, 4, 128, 128, A(0x10010), A(0x300000), None) == qdt.QDT_EALIAS     # Q inside X
-    assert q(A(), None, 4, 128, 128, None, A(0x300000), None) == qdt.QDT_EINVAL
-    assert q(A(), None, 0, 128, 128, A(0x200000), A(0x300000), None) == qdt.QDT_OK
+    assert q(A(), None, 4, 128, 128, A(0x200000), A(0x300000), None) == qdt.QDT_ESHAPE    # K % 256 (stages)
+    assert q(A(), None, 4, 256, 128, A(0x200000), A(0x300000), None) == qdt.QDT_ESHAPE     # ldx < K
+    assert q(A(), None, 4, 256, 256, A(0x200008), A(0x300000), None) == qdt.QDT_EALIGN
+    assert q(A(), None, 4, 256, 256, A(0x10010), A(0x300000), None) == qdt.QDT_EALIAS     # Q inside X
+    assert q(A(), None, 4, 256, 256, None, A(0x300000), None) == qdt.QDT_EINVAL
+    assert q(A(), None, 0, 256, 256, A(0x200000), A(0x300000), None) == qdt.QDT_OK
     f = qdt.qdt_mxfp4_linear
 
     def lin(M=64, N=128, K=256, epi=0, Y=0x900000, ldy=None, xs=0x200000, ws=0x400000):

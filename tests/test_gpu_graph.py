@@ -75,7 +75,7 @@ def test_adaln_producer_and_fp4_in_a_graph():
     sx = torch.empty(512, dtype=torch.float32, device="cuda")
     Wq4, Ws4 = qdt.mxfp4_quantize(to_dev(d["W"][:1024]))
     Q4 = torch.empty((512, 2304), dtype=torch.uint8, device="cuda")
-    S4 = torch.empty((512, 144), dtype=torch.uint8, device="cuda")
+    S4 = torch.empty((18, 512, 8), dtype=torch.uint8, device="cuda")
     Y4 = torch.empty((512, 1024), dtype=torch.bfloat16, device="cuda")
 
     def step():

@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 import qdt_workloads as W
-from qdt_testutil import bits_equal, sample_rows, to_dev, to_host, ulp_bf16
+from qdt_testutil import (bits_equal, mx_exponents_from_rows, mx_exponents_to_rows, sample_rows, to_dev, to_host,
+                          ulp_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +26,16 @@ def announce(msg):
     print(f"[case] {msg}", flush=True)
 
 
+def ex_host(S):
+    """Library-layout exponents on the device -> the oracle's row-major [rows, K/32]."""
+    return mx_exponents_to_rows(to_host(S))
+
+
+def ex_dev(S):
+    """Row-major [rows, K/32] exponents (oracle layout) -> library layout on the device."""
+    return to_dev(mx_exponents_from_rows(S))
+
+
 def check_quant(X, colmul=None, ldx=None):
     M, K = X.shape
     Xh = X
@@ -35,13 +46,13 @@ def check_quant(X, colmul=None, ldx=None):
     Q, S = qdt.mxfp4_quantize(Xd, None if colmul is None else to_dev(colmul))
     torch.cuda.synchronize()
     Qr, Sr = oracle.mxfp4_quantize(X, colmul)
-    Qg, Sg = to_host(Q), to_host(S)
+    Qg, Sg = to_host(Q), ex_host(S)
     assert bits_equal(Sg, Sr), f"exponents: {np.sum(Sg != Sr)} differ"
     assert bits_equal(Qg, Qr), f"codes: {np.sum(Qg != Qr)} bytes differ"
     return Q, S
 
 
-@pytest.mark.parametrize("M,K", [(1, 64), (37, 256), (300, 4608), (5, 53248)])
+@pytest.mark.parametrize("M,K", [(1, 256), (37, 512), (300, 4608), (5, 53248)])
 def test_mxfp4_quantize_parity(M, K):
     announce(f"mxfp4_quantize M={M} K={K}")
     X = W.activations(M, K, 4000 + K, "pct1")
@@ -80,7 +91,7 @@ def test_mxfp4_gemm_exact_accumulators(M, N, K):
     Xq, Xs = exact_operands(M, K, 50 + M)
     Wq, Ws = exact_operands(N, K, 60 + N)
     _, acc = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, want_acc=True)
-    Y = to_host(qdt.mxfp4_linear(to_dev(Xq), to_dev(Xs), to_dev(Wq), to_dev(Ws), None, "acc_f32"))
+    Y = to_host(qdt.mxfp4_linear(to_dev(Xq), ex_dev(Xs), to_dev(Wq), ex_dev(Ws), None, "acc_f32"))
     assert np.array_equal(Y.astype(np.float64), acc), f"{np.sum(Y != acc)} accumulators differ"
 
 
@@ -107,7 +118,7 @@ def test_mxfp4_linear_bias_within_bound(M, N, K):
     Wq, Ws = check_quant(d["W"])
     Y = to_host(qdt.mxfp4_linear(Xq, Xs, Wq, Ws, to_dev(d["bias"]), "bias"))
     rows = np.arange(M) if M <= 64 else sample_rows(M, 24, 5)
-    exact = within_bound(Y, to_host(Xq), to_host(Xs), to_host(Wq), to_host(Ws), d["bias"], rows)
+    exact = within_bound(Y, to_host(Xq), ex_host(Xs), to_host(Wq), ex_host(Ws), d["bias"], rows)
     assert exact > 0.9, f"only {exact:.3f} of the outputs equal the correctly rounded result"
 
 
@@ -120,10 +131,10 @@ def test_mxfp4_attention_projection_4608():
     Y = to_host(qdt.mxfp4_linear(Xq, Xs, Wq, Ws, to_dev(d["bias"]), "bias"))
     rows = sample_rows(4608, 16, 6)
     Qr, Sr = oracle.mxfp4_quantize(d["X"][rows])
-    assert bits_equal(to_host(Xq)[rows], Qr) and bits_equal(to_host(Xs)[rows], Sr)
+    assert bits_equal(to_host(Xq)[rows], Qr) and bits_equal(ex_host(Xs)[rows], Sr)
     Wqr, Wsr = oracle.mxfp4_quantize(d["W"])
-    assert bits_equal(to_host(Wq), Wqr) and bits_equal(to_host(Ws), Wsr)
-    Xqh, Xsh = to_host(Xq), to_host(Xs)
+    assert bits_equal(to_host(Wq), Wqr) and bits_equal(ex_host(Ws), Wsr)
+    Xqh, Xsh = to_host(Xq), ex_host(Xs)
     within_bound(Y, Xqh, Xsh, Wqr, Wsr, d["bias"], rows)
 
 
@@ -136,7 +147,7 @@ def test_mxfp4_silu_gate_exact_sums_within_one_ulp(M, F, K):
     Wq, Ws = exact_operands(2 * F, K, 80 + F)
     bias = W.f32_to_bf16_bits(np.random.default_rng(F).standard_normal(2 * F).astype(np.float32) * 4)
     Y_ref = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, epi="silu_gate")
-    Y = to_host(qdt.mxfp4_linear(to_dev(Xq), to_dev(Xs), to_dev(Wq), to_dev(Ws), to_dev(bias), "silu_gate"))
+    Y = to_host(qdt.mxfp4_linear(to_dev(Xq), ex_dev(Xs), to_dev(Wq), ex_dev(Ws), to_dev(bias), "silu_gate"))
     assert Y.shape == (M, F)
     u = ulp_bf16(Y, Y_ref)
     assert u.max() <= 1, f"max ulp {u.max()}"
@@ -152,7 +163,7 @@ def test_mxfp4_silu_gate_within_bound(M, F, K):
     Wq, Ws = check_quant(d["W"])
     Y = to_host(qdt.mxfp4_linear(Xq, Xs, Wq, Ws, to_dev(d["bias"]), "silu_gate"))
     rows = sample_rows(M, 24, 8)
-    Xqh, Xsh, Wqh, Wsh = to_host(Xq), to_host(Xs), to_host(Wq), to_host(Ws)
+    Xqh, Xsh, Wqh, Wsh = to_host(Xq), ex_host(Xs), to_host(Wq), ex_host(Ws)
     Y_ref, acc = oracle.mxfp4_gemm_rows(Xqh, Xsh, Wqh, Wsh, d["bias"], rows, want_acc=True, epi="silu_gate")
     xd = np.abs(oracle.mxfp4_dequantize(Xqh[rows], Xsh[rows]))
     wd = np.abs(oracle.mxfp4_dequantize(Wqh, Wsh))
@@ -181,7 +192,7 @@ def test_mxfp4_head_rmsnorm_exact_sums_within_one_ulp(M, N, K):
     bias = W.f32_to_bf16_bits(rng.standard_normal(N).astype(np.float32))
     gamma = W.f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(256)).astype(np.float32))
     Y_ref = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, epi="head_rmsnorm", gamma=gamma, eps=1e-6)
-    Y = to_host(qdt.mxfp4_linear(to_dev(Xq), to_dev(Xs), to_dev(Wq), to_dev(Ws), to_dev(bias), "head_rmsnorm",
+    Y = to_host(qdt.mxfp4_linear(to_dev(Xq), ex_dev(Xs), to_dev(Wq), ex_dev(Ws), to_dev(bias), "head_rmsnorm",
                                  gamma=to_dev(gamma), eps=1e-6))
     u = ulp_bf16(Y, Y_ref)
     assert u.max() <= 1, f"max ulp {u.max()}"
@@ -197,7 +208,7 @@ def test_mxfp4_head_rmsnorm_within_bound():
     Y = to_host(qdt.mxfp4_linear(Xq, Xs, Wq, Ws, to_dev(d["bias"]), "head_rmsnorm", gamma=to_dev(d["gamma"]),
                                  eps=d["eps"]))
     rows = sample_rows(M, 16, 10)
-    Xqh, Xsh, Wqh, Wsh = to_host(Xq), to_host(Xs), to_host(Wq), to_host(Ws)
+    Xqh, Xsh, Wqh, Wsh = to_host(Xq), ex_host(Xs), to_host(Wq), ex_host(Ws)
     Y_ref, acc = oracle.mxfp4_gemm_rows(Xqh, Xsh, Wqh, Wsh, d["bias"], rows, want_acc=True, epi="head_rmsnorm",
                                         gamma=d["gamma"], eps=d["eps"])
     xd = np.abs(oracle.mxfp4_dequantize(Xqh[rows], Xsh[rows]))
@@ -243,7 +254,7 @@ def test_mxfp4_split_k_exact(M, N, K):
     rng = np.random.default_rng(K)
     bias = W.f32_to_bf16_bits(rng.standard_normal(N).astype(np.float32))
     gamma = W.f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(256)).astype(np.float32))
-    dX, dXs, dW, dWs, db = (to_dev(a) for a in (Xq, Xs, Wq, Ws, bias))
+    dX, dXs, dW, dWs, db = to_dev(Xq), ex_dev(Xs), to_dev(Wq), ex_dev(Ws), to_dev(bias)
     Y_ref, acc = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, want_acc=True)
     Yacc = to_host(qdt.mxfp4_linear(dX, dXs, dW, dWs, None, "acc_f32"))
     assert np.array_equal(Yacc.astype(np.float64), acc), f"{np.sum(Yacc != acc)} accumulators differ"
@@ -263,4 +274,4 @@ def test_mxfp4_text_projection_shape():
     Xq, Xs = check_quant(d["X"])
     Wq, Ws = qdt.mxfp4_quantize(to_dev(d["W"]))
     Y = to_host(qdt.mxfp4_linear(Xq, Xs, Wq, Ws, to_dev(d["bias"]), "bias"))
-    within_bound(Y, to_host(Xq), to_host(Xs), to_host(Wq), to_host(Ws), d["bias"], sample_rows(512, 4, 11))
+    within_bound(Y, to_host(Xq), ex_host(Xs), to_host(Wq), ex_host(Ws), d["bias"], sample_rows(512, 4, 11))

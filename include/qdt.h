@@ -306,6 +306,24 @@ qdt_status qdt_w8a8_linear(const int8_t* Xq, const float* x_scale, const int8_t*
                            const void* epi_params, void* Y, int64_t ldy, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): qdt_w8a8_linear with the same arguments, results and
+ * errors, minus the workspace.  When the plan splits K, the int32 partial sums go to a scratch
+ * array the library holds in static device memory, QDT_NOALLOC_SCRATCH_BYTES per device (64 MiB:
+ * the 512 x 4608 x 53248 text projection at its 7-way split needs 63 MiB), allocated when the
+ * library's code is loaded on a device and held until the process ends.  A plan whose workspace
+ * would exceed it returns QDT_EWORKSPACE (qdt_w8a8_linear_workspace_size gives that size); the call
+ * itself allocates nothing.  Every slice writes each partial sum it owns before the reduction reads
+ * it, so nothing in the scratch needs clearing between calls.  All calls on one device share its
+ * scratch: calls that may overlap in time on one device (different streams, threads) race and
+ * must be serialized by the caller.
+ */
+#define QDT_NOALLOC_SCRATCH_BYTES (64ll << 20)
+qdt_status qdt_w8a8_linear_noalloc(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
+                                   const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi,
+                                   const void* epi_params, void* Y, int64_t ldy, void* stream);
+
 /* As qdt_w8a8_linear with an explicit tile and K split (plan->tile, plan->split_k; the other
  * fields are recomputed and written back).  Used to show that results are plan-independent. */
 qdt_status qdt_w8a8_linear_planned(const int8_t* Xq, const float* x_scale, const int8_t* Wq,
@@ -353,7 +371,7 @@ qdt_status qdt_attention_workspace_size(int64_t S, int64_t H, size_t* bytes);
 
 /*
  * Clock record (diagnostic; not part of the layer).  While a buffer is armed, every GEMM kernel
- * that qdt_w8a8_linear, qdt_w8a8_linear_planned, qdt_mxfp4_linear and
+ * that qdt_w8a8_linear, qdt_w8a8_linear_planned, qdt_w8a8_linear_noalloc, qdt_mxfp4_linear and
  * qdt_bf16_linear launch (not their split-K sums) takes the next `grid` entries of it
  * (one per workgroup, in workgroup-id order) as long as they fit; launches that do not fit record
  * nothing.  Entry = 4 uint64: the shader-clock counter (s_memtime) and the 100 MHz real-time

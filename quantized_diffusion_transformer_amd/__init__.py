@@ -71,6 +71,7 @@ _SIGS = {
     "qdt_w8a8_linear_planned": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P, _SZ,
                                  C.POINTER(qdt_linear_plan), _P], _I),
     "qdt_bf16_linear": ([_P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
+    "qdt_w8a8_linear_noalloc": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P], _I),
     "qdt_clock_record": ([_P, _I64], _I),
     "qdt_clock_record_used": ([C.POINTER(_I64)], _I),
 }
@@ -431,6 +432,29 @@ def w8a8_linear(Xq, x_scale, Wq, w_scale, bias=None, epilogue: str = "bias", gam
         _check(qdt_w8a8_linear_planned(*args, C.byref(plan), _stream(stream)), "qdt_w8a8_linear_planned")
     else:
         _check(qdt_w8a8_linear(*args, _stream(stream)), "qdt_w8a8_linear")
+    return out
+
+
+QDT_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def w8a8_linear_noalloc(Xq, x_scale, Wq, w_scale, bias=None, epilogue: str = "bias", gamma=None,
+                        head_dim: int = 256, eps: float = 1e-6, out=None, stream=None):
+    """W8A8 linear that allocates nothing in the library: split-K partial sums go to the library's
+    static per-device scratch (QDT_NOALLOC_SCRATCH_BYTES).  ``out`` is required, so this call
+    allocates nothing either.  Calls on one device must not overlap in time."""
+    if out is None:
+        raise ValueError("w8a8_linear_noalloc needs a preallocated out")
+    epi = EPILOGUES[epilogue]
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    params = None
+    if epi == QDT_EPI_HEAD_RMSNORM:
+        params = qdt_rmsnorm_params(gamma.data_ptr(), head_dim, eps)
+    out, ldy = _rows(out, "out")
+    _check(qdt_w8a8_linear_noalloc(_ptr(Xq), _ptr(x_scale), _ptr(Wq), _ptr(w_scale), _ptr(bias), M, N, K, epi,
+                                   None if params is None else C.cast(C.byref(params), C.c_void_p), _ptr(out), ldy,
+                                   _stream(stream)), "qdt_w8a8_linear_noalloc")
     return out
 
 

@@ -8,6 +8,33 @@
 
 namespace qdt {
 
+// Scratch of qdt_w8a8_linear_noalloc: the split-K partial sums live in this file-scope device
+// array instead of a caller workspace.  Each device holds its own copy (allocated when the code
+// object is loaded on it, kept until the process ends).  Host code never uses the array's name as
+// a device address: the per-device address comes from hipGetSymbolAddress, taken once per device
+// with that device current.
+static __device__ __align__(256) uint8_t scratch[QDT_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call per device).
+static hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 // Clock record of the W8A8 GEMM (qdt_clock_record): buffer, capacity and fill level in entries.
 static std::mutex g_clk_mu;
 static uint64_t* g_clk_buf = nullptr;
@@ -300,7 +327,8 @@ qdt_status qdt_w8a8_linear_workspace_size(int64_t M, int64_t N, int64_t K, qdt_e
 static qdt_status linear_impl(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
                               const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi,
                               const void* epi_params, void* Y, int64_t ldy, void* workspace, size_t workspace_bytes,
-                              int tile_req, int split_req, qdt_linear_plan* plan_out, void* stream) {
+                              int tile_req, int split_req, qdt_linear_plan* plan_out, void* stream,
+                              bool static_scratch = false) {
     qdt_status r = check_shape(M, N, K, epi);
     if (r != QDT_OK) return r;
     if (tile_req != QDT_TILE_AUTO && (tile_req < QDT_TILE_256 || tile_req > QDT_TILE_288x256)) return QDT_EINVAL;
@@ -316,6 +344,7 @@ static qdt_status linear_impl(const int8_t* Xq, const float* x_scale, const int8
     Plan p;
     if ((r = make_plan(M, N, K, kind, 1, tile_req, split_req, &p)) != QDT_OK) return r;
     if (plan_out) export_plan(p, plan_out);
+    if (static_scratch && p.ws_bytes > QDT_NOALLOC_SCRATCH_BYTES) return QDT_EWORKSPACE;
     const int64_t nout = epi == QDT_EPI_SILU_GATE ? N / 2 : N;
     const int64_t ysz = epi == QDT_EPI_ACC_I32 ? 4 : 2;
     if (ldy < nout) return QDT_ESHAPE;
@@ -329,6 +358,10 @@ static qdt_status linear_impl(const int8_t* Xq, const float* x_scale, const int8
     const int64_t inb[6] = {M * K, M * 4, N * K, N * 4, bias ? N * 2 : 0, 512};
     for (int i = 0; i < 6; ++i)
         if (overlap(Y, ybytes, ins[i], inb[i])) return QDT_EALIAS;
+    if (static_scratch && p.ws_bytes > 0) {
+        if ((r = hip_status(scratch_address(&workspace))) != QDT_OK) return r;
+        workspace_bytes = QDT_NOALLOC_SCRATCH_BYTES;
+    }
     if (p.ws_bytes > 0) {
         if (!workspace || (int64_t)workspace_bytes < p.ws_bytes) return QDT_EWORKSPACE;
         if (!aligned16(workspace)) return QDT_EALIGN;
@@ -364,6 +397,13 @@ qdt_status qdt_w8a8_linear(const int8_t* Xq, const float* x_scale, const int8_t*
                            void* stream) {
     return linear_impl(Xq, x_scale, Wq, w_scale, bias, M, N, K, epi, epi_params, Y, ldy, workspace, workspace_bytes,
                        QDT_TILE_AUTO, 0, nullptr, stream);
+}
+
+qdt_status qdt_w8a8_linear_noalloc(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,
+                                   const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi,
+                                   const void* epi_params, void* Y, int64_t ldy, void* stream) {
+    return linear_impl(Xq, x_scale, Wq, w_scale, bias, M, N, K, epi, epi_params, Y, ldy, nullptr, 0, QDT_TILE_AUTO,
+                       0, nullptr, stream, true);
 }
 
 qdt_status qdt_w8a8_linear_planned(const int8_t* Xq, const float* x_scale, const int8_t* Wq, const float* w_scale,

@@ -256,3 +256,20 @@ def test_plan_for_honours_requests():
     assert p["tile_m"] == 288 and p["tile_n"] == 256
     with pytest.raises(qdt.QdtError):
         qdt.linear_plan(600, 1024, 4096, "bias", tile=3)
+
+
+def test_noalloc_linear_validation():
+    f = qdt.qdt_w8a8_linear_noalloc
+    # 512 x 11008 x 53248 splits K 3 ways: 67.6 MB of partial sums, more than the static scratch;
+    # refused right after planning, before any pointer is looked at
+    M, N, K = 512, 11008, 53248
+    assert qdt.linear_plan(M, N, K, "bias")["workspace_bytes"] > qdt.QDT_NOALLOC_SCRATCH_BYTES
+    assert f(None, None, None, None, None, M, N, K, qdt.QDT_EPI_BIAS, None, None, N, None) == qdt.QDT_EWORKSPACE
+    # the usual argument checks, as qdt_w8a8_linear
+    assert f(A(), A(0x20000), A(0x30000), A(0x40000), None, 4, 16, 64, qdt.QDT_EPI_BIAS, None, A(0x50000), 16,
+             None) == qdt.QDT_ESHAPE                                                    # K % 128
+    assert f(A(), A(0x20000), A(0x30000), A(0x40000), None, 4, 16, 128, 9, None, A(0x50000), 16,
+             None) == qdt.QDT_EINVAL                                                    # epilogue
+    assert f(A(), A(0x20000), A(0x30000), A(0x40000), None, 4, 16, 128, qdt.QDT_EPI_BIAS, None, A(0x10040), 16,
+             None) == qdt.QDT_EALIAS                                                    # Y inside Xq
+    assert f(None, None, None, None, None, 0, 16, 128, qdt.QDT_EPI_BIAS, None, None, 16, None) == qdt.QDT_OK

@@ -52,6 +52,9 @@ def parse():
                          "workload skips the others and the CPU baseline, another prints its own line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--counters-from", default=None, metavar="DIR",
+                    help="print a markdown summary (per kernel: dispatches, duration, counter means, MFMA busy "
+                         "cycles per SIMD) of the rocprofv3 --pmc --kernel-trace CSVs under DIR and exit")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="write profiles/*_traffic.json from rocprofv3 --pmc CSVs under DIR/{fetch,write,"
                          "copy_fetch,copy_write} and exit")
@@ -273,6 +276,48 @@ def write_traffic(d):
         with open(os.path.join(ROOT, "profiles", f"{rec}_traffic.json"), "w") as f:
             json.dump(out, f, indent=1)
         print(json.dumps({rec: out}), flush=True)
+
+
+N_SIMD = 1024  # MI355X: 256 CUs x 4 SIMDs
+
+
+def summarize_counters(d, last_fraction=0.5):
+    """Markdown table per kernel of a rocprofv3 counter run (its later dispatches: the timed steps):
+    dispatches, mean duration, mean of each counter (rocprofv3 sums over XCDs, shader engines and
+    SIMDs), and SQ_VALU_MFMA_BUSY_CYCLES per SIMD."""
+    import csv
+    import glob
+    cc = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not cc:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    per, name, dur = {}, {}, {}
+    for f in cc:
+        for r in csv.DictReader(open(f)):
+            k = (f, int(r["Dispatch_Id"]))
+            per.setdefault(k, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+            name[k] = r["Kernel_Name"]
+            dur[k] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    byk = {}
+    for k in sorted(per):
+        byk.setdefault(name[k], []).append(k)
+    lines = []
+    for kn, ks in byk.items():
+        ks = ks[int(len(ks) * (1 - last_fraction)):] if len(ks) >= 4 else ks
+        cnames = sorted(per[ks[0]])
+        mean = {c: sum(per[k][c] for k in ks) / len(ks) for c in cnames}
+        us = sum(dur[k] for k in ks) / len(ks) / 1e3
+        lines.append(f"### `{kn[:110]}`")
+        lines.append("")
+        lines.append(f"{len(ks)} dispatches, mean duration {us:.2f} us")
+        lines.append("")
+        lines.append("| counter | mean per dispatch |")
+        lines.append("|---|---:|")
+        for c in cnames:
+            lines.append(f"| {c} | {mean[c]:.5g} |")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            lines.append(f"| SQ_VALU_MFMA_BUSY_CYCLES per SIMD | {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / N_SIMD:.5g} |")
+        lines.append("")
+    print("\n".join(lines), flush=True)
 
 
 def headline(args):
@@ -746,6 +791,9 @@ def adaln_producer(M, K, counts):
 
 def main():
     args = parse()
+    if args.counters_from:
+        summarize_counters(args.counters_from)
+        return
     if args.traffic_from:
         write_traffic(args.traffic_from)
         return

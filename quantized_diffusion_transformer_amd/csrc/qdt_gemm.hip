@@ -327,11 +327,13 @@ gemm_kernel(KArgs p) {
     // is free, so sub-step 1 issues the LDS-DMAs of stage j+2 into buffer j % 2 and reads the
     // sub-step 0 fragments of stage j+1, while sub-step 0 reads the sub-step 1 fragments of its
     // own stage.  Every LDS read and LDS-DMA is issued between two MFMAs, so a wave never waits
-    // on LDS latency after a barrier.  Past the last stage, loads are clamped to stage nk-1 (their
-    // data is never used), which keeps the loop free of branches.
-    // Prologue: the LDS-DMAs of stages 0 and 1 go out first, then the parameter chunks (needed
-    // only by the epilogue); the accumulators are cleared while they are in flight.  Loads
-    // complete in issue order, so vmcnt <= NI means stage 0 has landed.
+    // on LDS latency after a barrier.  The last two stages are separate copies of the loop body:
+    // they issue no LDS-DMAs (there is no stage j+2), and the last one reads no stage j+1, so after
+    // its barrier no wave touches the stage buffers and the epilogue needs no barrier of its own.
+    // Prologue: the LDS-DMAs of stage 0 go out first, then the parameter chunks (needed only by
+    // the epilogue), then stage 1's; the accumulators are cleared while they are in flight.  Loads
+    // complete in issue order, so vmcnt <= NI means stage 0 and the parameters have landed, and
+    // the bias is converted to fp32 right after the first barrier.
     const int nkc = max(nk, 1);
     v4u a0[FN], b0[FM], a1[FN], b1[FM];
     // FP4 block exponents of the fragments (one byte per lane in byte 0), per K step
@@ -351,16 +353,17 @@ gemm_kernel(KArgs p) {
         if (dma_used(i)) dma(0, 0, i);
 #pragma unroll
     for (int i = 0; i < NSC; ++i) sdma(0, 0, i);
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-        if (dma_used(i)) dma(1, min(1, nkc - 1), i);
-#pragma unroll
-    for (int i = 0; i < NSC; ++i) sdma(1, min(1, nkc - 1), i);
+    // the epilogue parameters land with stage 0 (loads complete in issue order)
 #pragma unroll
     for (int c = 0; c < P_BF / 64; ++c) {
         const bool is_bias = c * 64 >= P_B && c * 64 < P_G;
         if (c % NW == wave && (!is_bias || p.bias != nullptr)) prm_dma(c);
     }
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        if (dma_used(i)) dma(1, min(1, nkc - 1), i);
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) sdma(1, min(1, nkc - 1), i);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
@@ -374,6 +377,18 @@ gemm_kernel(KArgs p) {
     else
         wait_vmcnt<NIX + NSC>();
     __syncthreads();
+    if constexpr (HAS_BIAS) {
+        // bias of the tile's weight rows to fp32 (0 without bias), once; the main loop's barriers
+        // order these writes before the epilogue reads them
+        for (int r = tid; r < BN; r += NW * 64) {
+            float v = 0.0f;
+            if (p.bias) {
+                const uint32_t pr = prm[P_B + r / 2];
+                v = bf16_to_f32((r & 1) ? pr >> 16 : pr & 0xFFFFu);
+            }
+            prm[P_BF + r] = __float_as_uint(v);
+        }
+    }
     {
         const uint8_t* s = smem + lrow;
 #pragma unroll
@@ -387,10 +402,13 @@ gemm_kernel(KArgs p) {
             for (int fm = 0; fm < FM; ++fm) sb0[fm] = sc(0, xrow0 + fm * 16, 0);
         }
     }
-    for (int j = 0; j < nk; ++j) {
+    // one main-loop stage; DMA: issue the LDS-DMAs of stage j + 2, NEXT: read the first fragments
+    // of stage j + 1 (the last two stages have no stage j + 2, the last one no stage j + 1)
+    auto iter = [&](int j, auto dma_on, auto next_on) __attribute__((always_inline)) {
+        constexpr bool DMA = decltype(dma_on)::value, NEXT = decltype(next_on)::value;
         const uint8_t* s = smem + (j % NB) * STAGE + lrow;
         const uint8_t* sn = smem + ((j + 1) % NB) * STAGE + lrow;
-        const int jd = min(j + 2, nk - 1);
+        const int jd = j + 2;
         // sub-step 0: every SP-th slot reads b1[0..FM-1], then a1[0..FN-1]
 #pragma unroll
         for (int g = 0; g < FN; ++g) {
@@ -423,7 +441,7 @@ gemm_kernel(KArgs p) {
         const uint8_t* scbased = MX ? scbase + (int64_t)jd * sstride : nullptr;
         (void)ldssd;
         (void)scbased;
-        set_m0(ldsd);
+        if constexpr (DMA) set_m0(ldsd);
 #pragma unroll
         for (int g = 0; g < FN; ++g) {
 #pragma unroll
@@ -442,15 +460,15 @@ gemm_kernel(KArgs p) {
                 for (int t = 0; t < FM + FN; ++t) if ((t * S) / NDMA + 1 == k) qs = t;
                 if (qd >= 0 && qd < NI) {
                     const uint32_t next = qd + 1 < NI || !MX ? ldsd + (uint32_t)((qd + 1) * 1024) : ldssd;
-                    if (dma_used(qd)) lds_dma16_next(voff(qd), sbase, next);
+                    if (DMA && dma_used(qd)) lds_dma16_next(voff(qd), sbase, next);
                 } else if (qd >= NI) {
-                    if constexpr (MX)
+                    if constexpr (MX && DMA)
                         lds_dma4_next(scvoffs[qd - NI], scbased, ldssd + (uint32_t)((qd - NI + 1) * 256));
-                } else if (qr >= 0 && qr < FM)
+                } else if (NEXT && qr >= 0 && qr < FM)
                     b0[qr] = frag(sn, xrow0 + qr * 16, lck0);
-                else if (qr >= FM)
+                else if (NEXT && qr >= FM)
                     a0[qr - FM] = frag(sn, wrow[qr - FM], lck0);
-                if constexpr (MX) {
+                if constexpr (MX && NEXT) {
                     if (qs >= 0 && qs < FM)
                         sb0[qs] = sc((j + 1) % NB, xrow0 + qs * 16, 0);
                     else if (qs >= FM)
@@ -459,7 +477,12 @@ gemm_kernel(KArgs p) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-    }
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    for (int j = 0; j < nk - 2; ++j) iter(j, T{}, T{});
+    if (nk >= 2) iter(nk - 2, F{}, T{});
+    if (nk >= 1) iter(nk - 1, F{}, F{});
     wait_vmcnt<0>();
     mfma_drain();
 #pragma unroll
@@ -490,18 +513,8 @@ gemm_kernel(KArgs p) {
     constexpr int ES = (EPI == EPI_ACC || EPI == EPI_PARTIAL) ? 4 : 2;   // output element bytes
     constexpr int CW = NF * 16 * ES, RS = CW + 16, CPR = CW / 16, NCH = 16 * CPR;
     static_assert(NW * 2 * 16 * RS <= NB * STAGE, "output strips fit in the stage buffers");
-    if constexpr (HAS_BIAS) {
-        // bias of the tile's weight rows to fp32 (0 without bias), once
-        for (int r = tid; r < BN; r += NW * 64) {
-            float v = 0.0f;
-            if (p.bias) {
-                const uint32_t pr = prm[P_B + r / 2];
-                v = bf16_to_f32((r & 1) ? pr >> 16 : pr & 0xFFFFu);
-            }
-            prm[P_BF + r] = __float_as_uint(v);
-        }
-    }
-    __syncthreads();
+    // no barrier: after the last stage's barrier no wave reads the stage buffers, no LDS-DMA is in
+    // flight, and each wave's output strips are its own
     uint8_t* Yb;
     int64_t ldb;
     int ncols;

@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--counters-from", default=None, metavar="DIR",
                     help="print a markdown summary (per kernel: dispatches, duration, counter means, MFMA busy "
                          "cycles per SIMD) of the rocprofv3 --pmc --kernel-trace CSVs under DIR and exit")
+    ap.add_argument("--trace-from", default=None, metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 --kernel-trace run under DIR (per kernel, over "
+                         "the later half of its dispatches: count, mean, median, min, max in microseconds) and exit")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="write profiles/*_traffic.json from rocprofv3 --pmc CSVs under DIR/{fetch,write,"
                          "copy_fetch,copy_write} and exit")
@@ -92,12 +95,14 @@ def warm_up(fn_step, sets, warmup, settle_ms=0.0):
     return n
 
 
-def time_loop(fn_step, sets, steps, warmup, settle_ms=0.0, stats_out=None):
+def time_loop(fn_step, sets, steps, warmup, settle_ms=0.0, stats_out=None, clock_grid=None):
     """Wall time of `steps` steps (sync on both sides) + per-phase HIP event times.
 
     Every k-th step of the timed region records HIP events (on the stream the library launches
     on) around its two launches, k = EVENT_EVERY, or less so that there are at least
-    MIN_EVENT_SAMPLES samples; the others run without events."""
+    MIN_EVENT_SAMPLES samples; the others run without events.  With `clock_grid` (the GEMM's
+    workgroup count) the library's clock record is armed over the timed steps, and the GEMM's
+    shader clock during them goes to stats_out["clock"]."""
     import torch
     nw = warm_up(fn_step, sets, warmup, settle_ms)
     if stats_out is not None:
@@ -105,12 +110,22 @@ def time_loop(fn_step, sets, steps, warmup, settle_ms=0.0, stats_out=None):
     every = max(1, min(EVENT_EVERY, steps // MIN_EVENT_SAMPLES))
     sampled = list(range(0, steps, every))
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+    rec = None
+    if clock_grid is not None:
+        import quantized_diffusion_transformer_amd as qdt
+        rec = torch.zeros((steps * clock_grid, 4), dtype=torch.int64, device="cuda")
+        qdt.clock_record(rec)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         fn_step(sets[i % len(sets)], evs.get(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if rec is not None:
+        used = qdt.clock_record_used()
+        qdt.clock_record(None)
+        if stats_out is not None:
+            stats_out["clock"] = clock_stats(rec[:used], clock_grid)
     if stats_out is not None:
         stats_out["event_every"] = every
         stats_out["event_samples"] = len(sampled)
@@ -156,22 +171,12 @@ def flushed_steps(fn_step, sets, reps=25):
     return times
 
 
-def clock_during(fn_step, sets, qdt, launches=100, grid=256):
+def clock_stats(buf, grid):
     """Shader clock of the GEMM kernel from the library's clock record: per launch, the sum over
     workgroups of shader-clock cycles over the sum of 100 MHz real-time ticks, from each
-    workgroup's start to its last store."""
+    workgroup's start to its last store; median and p10 / p90 over the launches."""
     import numpy as np
-    import torch
-    buf = torch.zeros((launches * grid, 4), dtype=torch.int64, device="cuda")
-    qdt.clock_record(buf)
-    try:
-        for i in range(launches):
-            fn_step(sets[i % len(sets)], None)
-        torch.cuda.synchronize()
-        used = qdt.clock_record_used()
-    finally:
-        qdt.clock_record(None)
-    rec = buf[:used].cpu().numpy().astype(np.int64).reshape(-1, grid, 4)
+    rec = buf.cpu().numpy().astype(np.int64).reshape(-1, grid, 4)
     cyc = (rec[:, :, 2] - rec[:, :, 0]).sum(axis=1).astype(np.float64)
     real = (rec[:, :, 3] - rec[:, :, 1]).sum(axis=1).astype(np.float64)
     mhz = cyc / real * 100.0
@@ -179,20 +184,24 @@ def clock_during(fn_step, sets, qdt, launches=100, grid=256):
     return {"clock_mhz": float(np.median(mhz)), "clock_mhz_p10": float(np.percentile(mhz, 10)),
             "clock_mhz_p90": float(np.percentile(mhz, 90)), "launches": int(rec.shape[0]),
             "kernel_span_us_median": float(np.median(span_us)),
-            "how": "s_memtime / s_memrealtime read by each workgroup's first wave at its start and after its "
-                   "last store; clock = sum of cycles / sum of 100 MHz ticks per launch (median over launches)"}
+            "how": "over the timed steps: s_memtime / s_memrealtime read by each workgroup's first wave at its "
+                   "start and after its last store; clock = sum of cycles / sum of 100 MHz ticks per launch "
+                   "(median over launches)"}
 
 
-def time_loop_best(fn_step, steps, warmup, reps=2):
+def time_loop_best(fn_step, steps, warmup, reps=2, clock_grid=None, info=None):
     """time_loop on one buffer set, repeated: the repetition with the lowest wall time (context
     numbers of the other workloads; a one-off stall of the device then costs a repetition, not
-    the number)."""
+    the number).  With clock_grid, info["clock"] is the GEMM clock over that repetition."""
     best = None
     for r in range(reps):
+        st = {}
         res = time_loop(fn_step, [None], steps, warmup if r == 0 else max(1, warmup // 4),
-                        settle_ms=100.0 if r == 0 else 0.0)
+                        settle_ms=100.0 if r == 0 else 0.0, stats_out=st, clock_grid=clock_grid)
         if best is None or res[0] < best[0]:
             best = res
+            if info is not None and "clock" in st:
+                info["clock"] = st["clock"]
     return best
 
 
@@ -281,6 +290,29 @@ def write_traffic(d):
 N_SIMD = 1024  # MI355X: 256 CUs x 4 SIMDs
 
 
+def summarize_trace(d, last_fraction=0.5):
+    """Per-kernel duration statistics of a rocprofv3 kernel trace, over the later `last_fraction` of
+    each kernel's dispatches (the timed steps follow the warm-up)."""
+    import csv
+    import glob
+    import numpy as np
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no kernel_trace.csv under {d}")
+    durs = {}
+    for f in files:
+        rows = sorted(csv.DictReader(open(f)), key=lambda r: int(r["Start_Timestamp"]))
+        for r in rows:
+            durs.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["| kernel | dispatches (all) | summarized | mean | median | min | max |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        w = np.asarray(v[int(len(v) * (1 - last_fraction)):] if len(v) >= 4 else v)
+        lines.append(f"| `{k[:100]}` | {len(v)} | {len(w)} | {w.mean():.2f} | {np.median(w):.2f} | {w.min():.2f} | "
+                     f"{w.max():.2f} |")
+    print("\n".join(lines), flush=True)
+
+
 def summarize_counters(d, last_fraction=0.5):
     """Markdown table per kernel of a rocprofv3 counter run (its later dispatches: the timed steps):
     dispatches, mean duration, mean of each counter (rocprofv3 sums over XCDs, shader engines and
@@ -359,15 +391,14 @@ def headline(args):
     log(f"timing {args.steps} steps (warmup {args.warmup} steps and >= {args.settle_ms} ms, {R} rotating sets), "
         f"plan {plan}")
     info = {}
-    ms, tq, tg = time_loop(step, sets, args.steps, args.warmup, args.settle_ms, info)
+    ms, tq, tg = time_loop(step, sets, args.steps, args.warmup, args.settle_ms, info, clock_grid=plan["grid"])
     log(f"wall {ms:.4f} ms/step; quantize {stats(tq)['mean']:.4f} ms + linear {stats(tg)['mean']:.4f} ms (HIP events)")
+    clk = info["clock"]
     if args.profile_run:
         dist, flushed, acc = [ms], [ms], None
-        clk = {"clock_mhz": float("nan")}
     else:
         dist = step_distribution(step, sets)
         flushed = flushed_steps(step, sets)
-        clk = clock_during(step, sets, qdt, grid=plan["grid"])
         log(f"step blocks median {np.median(dist):.4f} ms; flushed median {np.median(flushed):.4f} ms; "
             f"GEMM clock {clk['clock_mhz']:.0f} MHz")
         acc = accuracy_info(d, sets[0]["Y"], W0, b, qdt)
@@ -546,8 +577,9 @@ def extra_workloads(args, only=None):
             if ev is not None:
                 ev[2].record()
         steps, warm = counts(step)
-        ms, tq, tg = time_loop_best(step, steps, warm)
-        clk = clock_during(step, [None], qdt, launches=30, grid=plan["grid"])["clock_mhz"]
+        info = {}
+        ms, tq, tg = time_loop_best(step, steps, warm, clock_grid=plan["grid"], info=info)
+        clk = info["clock"]["clock_mhz"]
         ops = 2.0 * M * N * K
         g = stats(tg)["mean"]
         r = {"M": M, "N": N, "K": K, "epilogue": epi, "plan": plan, "steps": steps, "warmup": warm,
@@ -727,8 +759,9 @@ def mxfp4_workload(src, epi, counts):
         if ev is not None:
             ev[2].record()
     steps, warm = counts(step)
-    ms, tq, tg = time_loop_best(step, steps, warm)
-    clk = clock_during(step, [None], qdt, launches=30, grid=plan["grid"])["clock_mhz"]
+    info = {}
+    ms, tq, tg = time_loop_best(step, steps, warm, clock_grid=plan["grid"], info=info)
+    clk = info["clock"]["clock_mhz"]
     ops = 2.0 * M * N * K
     g = stats(tg)["mean"]
     qb = 2 * M * K + M * K // 2 + M * K // 32
@@ -793,6 +826,9 @@ def main():
     args = parse()
     if args.counters_from:
         summarize_counters(args.counters_from)
+        return
+    if args.trace_from:
+        summarize_trace(args.trace_from)
         return
     if args.traffic_from:
         write_traffic(args.traffic_from)

@@ -27,7 +27,7 @@ _lib = C.CDLL(LIB_PATH)
 # ------------------------------------------------------------------------------- C types
 QDT_OK, QDT_EINVAL, QDT_ESHAPE, QDT_EALIGN, QDT_EWORKSPACE, QDT_EALIAS, QDT_EHIP, QDT_EUNSUPPORTED = range(8)
 QDT_EPI_BIAS, QDT_EPI_SILU_GATE, QDT_EPI_HEAD_RMSNORM, QDT_EPI_ACC_I32, QDT_EPI_ACC_F32 = range(5)
-QDT_TILE_AUTO, QDT_TILE_256, QDT_TILE_288, QDT_TILE_288x256 = -1, 0, 1, 2
+QDT_TILE_AUTO, QDT_TILE_256, QDT_TILE_288, QDT_TILE_288x256, QDT_TILE_224x256 = -1, 0, 1, 2, 3
 QDT_MAX_K = 131072
 QDT_MAX_ADALN_K = 8192
 

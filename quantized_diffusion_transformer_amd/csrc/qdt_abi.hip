@@ -69,14 +69,16 @@ qdt_status make_plan(int64_t M, int64_t N, int64_t K, int epi, int esize, int ti
     const bool silu = epi == EPI_SILU, rms = epi == EPI_RMSNORM;
     Plan best{};
     double best_cost = -1.0;
-    for (int tile = QDT_TILE_256; tile <= QDT_TILE_288x256; ++tile) {
+    for (int tile = QDT_TILE_256; tile <= QDT_TILE_224x256; ++tile) {
         if (tile_req != QDT_TILE_AUTO && tile != tile_req) continue;
         if (tile == QDT_TILE_288 && (silu || rms)) continue;  // heads / gate-up halves need 256-wide tiles
         // 288 x 256 only on request: its weight and token waves issue unequal LDS-DMA counts and it
         // measured ~5% slower per FFN gate/up step than 256 x 256 despite fewer tile rounds
         if (tile == QDT_TILE_288x256 && tile_req == QDT_TILE_AUTO) continue;
-        const int bm = tile == QDT_TILE_256 ? 256 : 288;       // token rows
-        const int bn = tile == QDT_TILE_288 ? 288 : 256;       // weight rows
+        // 224 x 256 is an int8 tile
+        if (tile == QDT_TILE_224x256 && esize != 1) continue;
+        const int bm = tile == QDT_TILE_256 ? 256 : tile == QDT_TILE_224x256 ? 224 : 288;  // token rows
+        const int bn = tile == QDT_TILE_288 ? 288 : 256;                                   // weight rows
         const int64_t kstage = 128;  // bytes of K per main-loop stage (whole cache lines)
         const int64_t kt_total = cdiv(K * esize, kstage);
         const int64_t tiles_m = cdiv(M > 0 ? M : 1, bm);
@@ -97,6 +99,8 @@ qdt_status make_plan(int64_t M, int64_t N, int64_t K, int epi, int esize, int ti
         const int64_t grid = tiles * split;
         const int64_t rounds = cdiv(grid, kNumCU);
         double cost = (double)rounds * bm * bn * kps * kstage / 8192.0;  // ~cycles of MFMA per CU
+        // a 224-row tile moves 480 operand rows per stage for 7/8 of the MFMAs of a 256-row one
+        if (tile == QDT_TILE_224x256) cost *= (480.0 / 512.0) / (224.0 / 256.0);
         if (split > 1) cost += (double)split * M * N * 4 * 2 / (8e12 / 2.4e9 / kNumCU) / kNumCU;
         if (best_cost < 0 || cost < best_cost) {
             best_cost = cost;
@@ -307,7 +311,7 @@ qdt_status qdt_w8a8_linear_plan_for(int64_t M, int64_t N, int64_t K, qdt_epilogu
     if (!plan) return QDT_EINVAL;
     qdt_status r = check_shape(M, N, K, epi);
     if (r != QDT_OK) return r;
-    if (tile != QDT_TILE_AUTO && (tile < QDT_TILE_256 || tile > QDT_TILE_288x256)) return QDT_EINVAL;
+    if (tile != QDT_TILE_AUTO && (tile < QDT_TILE_256 || tile > QDT_TILE_224x256)) return QDT_EINVAL;
     if (split_k < 0) return QDT_EINVAL;
     Plan p;
     if ((r = make_plan(M, N, K, epi_kind(epi), 1, tile, split_k, &p)) != QDT_OK) return r;
@@ -331,7 +335,7 @@ static qdt_status linear_impl(const int8_t* Xq, const float* x_scale, const int8
                               bool static_scratch = false) {
     qdt_status r = check_shape(M, N, K, epi);
     if (r != QDT_OK) return r;
-    if (tile_req != QDT_TILE_AUTO && (tile_req < QDT_TILE_256 || tile_req > QDT_TILE_288x256)) return QDT_EINVAL;
+    if (tile_req != QDT_TILE_AUTO && (tile_req < QDT_TILE_256 || tile_req > QDT_TILE_224x256)) return QDT_EINVAL;
     if (split_req < 0) return QDT_EINVAL;
     const int kind = epi_kind(epi);
     const qdt_rmsnorm_params* rp = reinterpret_cast<const qdt_rmsnorm_params*>(epi_params);

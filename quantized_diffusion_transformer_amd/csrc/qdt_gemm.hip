@@ -129,7 +129,8 @@ gemm_kernel(KArgs p) {
     constexpr bool RMS = EPI == EPI_RMSNORM || EPI == EPI_F32RMSNORM;
     static_assert(WM == 2 && WN == 2 && NBW % 2 == 0 && NBX % 2 == 0, "two waves per operand region");
     static_assert(!SILU || (NIW * 8 == BN / 2 && FN % 2 == 0), "one weight wave per gate / up half");
-    constexpr int SP = 4;                  // MFMA slots between consecutive reads of sub-step 0
+    // MFMA slots between consecutive reads of sub-step 0 (3 for the 7 x 8 fragments of 224 x 256)
+    constexpr int SP = (FN + FM) * 4 <= FN * FM ? 4 : 3;
     static_assert((FN + FM) * SP <= FN * FM, "sub-step 0 reads fit between its MFMAs");
     // sub-step 1 puts LDS-DMA q at slot floor(q FN FM / NI) and read q two slots later: distinct
     // slots inside the sub-step when the DMA slots are at least 3 apart and reads <= DMAs
@@ -909,6 +910,16 @@ hipError_t launch_gemm_i8(const GemmArgs& a, const Plan& pl, hipStream_t st) {
             case EPI_BIAS: return go<9, 9, false, EPI_BIAS>(k, pl.grid, st);
             case EPI_ACC: return go<9, 9, false, EPI_ACC>(k, pl.grid, st);
             case EPI_PARTIAL: return go<9, 9, false, EPI_PARTIAL>(k, pl.grid, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (pl.tile == QDT_TILE_224x256) {
+        switch (epi) {
+            case EPI_BIAS: return go<7, 8, false, EPI_BIAS>(k, pl.grid, st);
+            case EPI_SILU: return go<7, 8, false, EPI_SILU>(k, pl.grid, st);
+            case EPI_RMSNORM: return go<7, 8, false, EPI_RMSNORM>(k, pl.grid, st);
+            case EPI_ACC: return go<7, 8, false, EPI_ACC>(k, pl.grid, st);
+            case EPI_PARTIAL: return go<7, 8, false, EPI_PARTIAL>(k, pl.grid, st);
             default: return hipErrorInvalidValue;
         }
     }

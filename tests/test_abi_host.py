@@ -231,9 +231,9 @@ def test_bf16_linear_validation():
     (512, 4608, 53248, "bias", 256, 256, 7),          # deep-K text projection: split K over 7 slices
     (4608, 4608, 53248, "bias", 288, 288, 1),         # its zero-padded variant fills the GPU without a split
     (16896, 4608, 4608, "head_rmsnorm", 256, 256, 1),  # heads need 256-wide tiles
-    (6037, 4608, 4608, "head_rmsnorm", 256, 256, 1),
+    (6037, 4608, 4608, "head_rmsnorm", 224, 256, 1),  # 486 tiles of 224 x 256: two full rounds
     (4608, 24576, 4608, "silu_gate", 256, 256, 1),
-    (64, 128, 256, "bias", 256, 256, 1),
+    (64, 128, 256, "bias", 224, 256, 1),            # one partial tile: the smallest that holds it
 ])
 def test_planner_choices(M, N, K, epi, tm, tn, split):
     p = qdt.linear_plan(M, N, K, epi)
@@ -254,8 +254,10 @@ def test_plan_for_honours_requests():
         qdt.linear_plan(600, 1024, 4096, "head_rmsnorm", tile=qdt.QDT_TILE_288)
     p = qdt.linear_plan(600, 1024, 4096, "head_rmsnorm", tile=qdt.QDT_TILE_288x256)
     assert p["tile_m"] == 288 and p["tile_n"] == 256
+    p = qdt.linear_plan(600, 1024, 4096, "silu_gate", tile=qdt.QDT_TILE_224x256)
+    assert p["tile_m"] == 224 and p["tile_n"] == 256
     with pytest.raises(qdt.QdtError):
-        qdt.linear_plan(600, 1024, 4096, "bias", tile=3)
+        qdt.linear_plan(600, 1024, 4096, "bias", tile=4)
 
 
 def test_noalloc_linear_validation():

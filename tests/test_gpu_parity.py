@@ -160,7 +160,8 @@ SHAPES = [
 @pytest.mark.parametrize("M,N,K", SHAPES)
 @pytest.mark.parametrize("tile,split", [(None, None), (qdt.QDT_TILE_256, 1), (qdt.QDT_TILE_288, 1),
                                         (qdt.QDT_TILE_288x256, 1), (qdt.QDT_TILE_256, 3),
-                                        (qdt.QDT_TILE_288x256, 2)])
+                                        (qdt.QDT_TILE_288x256, 2), (qdt.QDT_TILE_224x256, 1),
+                                        (qdt.QDT_TILE_224x256, 3)])
 def test_int32_accumulators_bit_exact(M, N, K, tile, split):
     announce(f"acc M={M} N={N} K={K} tile={tile} split={split}")
     d = W.make_linear(M, N, K, seed=M + N + K, x_kind="pct1")
@@ -202,7 +203,7 @@ def run_linear(d, epi, tile=None, split=None, bias=True):
 
 @pytest.mark.parametrize("M,N,K", SHAPES + [(700, 4608, 4608)])
 @pytest.mark.parametrize("tile,split", [(None, None), (qdt.QDT_TILE_288, 1), (qdt.QDT_TILE_256, 4),
-                                        (qdt.QDT_TILE_288x256, 1)])
+                                        (qdt.QDT_TILE_288x256, 1), (qdt.QDT_TILE_224x256, 1)])
 def test_bias_epilogue_exact(M, N, K, tile, split):
     announce(f"bias M={M} N={N} K={K} tile={tile} split={split}")
     d = W.make_linear(M, N, K, seed=11 + M, x_kind="pct1")
@@ -214,7 +215,8 @@ def test_bias_epilogue_exact(M, N, K, tile, split):
 
 
 @pytest.mark.parametrize("M,F,K", [(64, 64, 256), (300, 640, 1024), (513, 1152, 512)])
-@pytest.mark.parametrize("tile,split", [(None, None), (None, 3), (qdt.QDT_TILE_288x256, 1)])
+@pytest.mark.parametrize("tile,split", [(None, None), (None, 3), (qdt.QDT_TILE_288x256, 1),
+                                        (qdt.QDT_TILE_224x256, 1)])
 def test_silu_gate_epilogue(M, F, K, tile, split):
     announce(f"silu M={M} F={F} K={K} tile={tile} split={split}")
     d = W.make_linear(M, 2 * F, K, seed=21 + M, x_kind="pct1", bias=True)
@@ -241,7 +243,8 @@ def test_silu_gate_large_gates(split):
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 256, 256), (300, 1024, 1024), (257, 512, 4608)])
-@pytest.mark.parametrize("tile,split", [(None, None), (None, 3), (qdt.QDT_TILE_288x256, 1)])
+@pytest.mark.parametrize("tile,split", [(None, None), (None, 3), (qdt.QDT_TILE_288x256, 1),
+                                        (qdt.QDT_TILE_224x256, 1), (qdt.QDT_TILE_224x256, 2)])
 def test_head_rmsnorm_epilogue(M, N, K, tile, split):
     announce(f"rmsnorm M={M} N={N} K={K} tile={tile} split={split}")
     d = W.make_linear(M, N, K, seed=31 + M, x_kind="pct1", epi="head_rmsnorm")
@@ -281,7 +284,8 @@ def test_results_do_not_depend_on_plan():
     d = W.make_linear(600, 1152, 2048, seed=41, x_kind="pct1")
     outs = [run_linear(d, "bias", t, s)[0] for t, s in ((None, None), (qdt.QDT_TILE_288, 1), (qdt.QDT_TILE_256, 1),
                                                          (qdt.QDT_TILE_256, 5), (qdt.QDT_TILE_288, 2),
-                                                         (qdt.QDT_TILE_288x256, 1), (qdt.QDT_TILE_288x256, 3))]
+                                                         (qdt.QDT_TILE_288x256, 1), (qdt.QDT_TILE_288x256, 3),
+                                                         (qdt.QDT_TILE_224x256, 1))]
     for o in outs[1:]:
         assert bits_equal(o, outs[0])
     ref, dev = prepared(d)
@@ -299,7 +303,8 @@ def test_fused_epilogues_do_not_depend_on_plan(epi):
     d = W.make_linear(600, 1024, 2048, seed=43, x_kind="pct1", epi=epi)
     outs = [run_linear(d, epi, t, s)[0] for t, s in ((None, None), (qdt.QDT_TILE_256, 1), (qdt.QDT_TILE_256, 3),
                                                      (qdt.QDT_TILE_256, 7), (qdt.QDT_TILE_288x256, 1),
-                                                     (qdt.QDT_TILE_288x256, 2))]
+                                                     (qdt.QDT_TILE_288x256, 2), (qdt.QDT_TILE_224x256, 1),
+                                                     (qdt.QDT_TILE_224x256, 3))]
     for o in outs[1:]:
         assert bits_equal(o, outs[0]), f"{np.sum(o != outs[0])} elements differ between plans"
 

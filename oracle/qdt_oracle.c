@@ -17,8 +17,8 @@
  *          fused epilogues: each large matmul is followed by a small op (RMSNorm or
  *          a gated SiLU), and attention heads are 256 wide.
  *   [ZC]   "Faster Ideogram 4 with Less Prompt Compute" -- section "Most of the Tensor
- *          Was Zero": the projection has a bias, so a zero row projects to the bias,
- *          and rows are projected independently.
+ *          Was Zero": each row goes through the linear on its own, and with the bias
+ *          added an all-zero input row comes out as exactly the bias vector.
  *
  * Readings where the pages are silent (each is also listed with the design notes):
  *   - alpha = 0.5 is evaluated as sqrtf(s)/sqrtf(w); lambda = 1 where s or w is 0;

@@ -226,8 +226,24 @@ qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t*
                             const void* epi_params, void* Y, int64_t ldy, void* workspace, size_t workspace_bytes,
                             void* stream);
 
-/* The plan qdt_mxfp4_linear uses (tile, K split, workspace bytes).  Pure host computation. */
+/* The plan qdt_mxfp4_linear uses (tile, K split, workspace bytes).  Pure host computation.  FP4
+ * takes the tiles QDT_TILE_256, QDT_TILE_288 (not with SILU_GATE or HEAD_RMSNORM) and, on request,
+ * QDT_TILE_288x256; the planner chooses as for qdt_w8a8_linear. */
 qdt_status qdt_mxfp4_linear_plan(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, qdt_linear_plan* plan);
+
+/* The plan qdt_mxfp4_linear_planned uses for a requested tile (QDT_TILE_AUTO, QDT_TILE_256, _288 or
+ * _288x256; QDT_EINVAL for another) and K split (0 = planner's choice).  Pure host computation. */
+qdt_status qdt_mxfp4_linear_plan_for(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, int32_t tile,
+                                     int32_t split_k, qdt_linear_plan* plan);
+
+/* As qdt_mxfp4_linear with an explicit tile and K split (plan->tile, plan->split_k; the other fields
+ * are recomputed and written back).  Without a K split the result does not depend on the tile: every
+ * output's K reduction runs through the same MFMA sequence.  A K split changes the fp32 summation
+ * order (within the same bound). */
+qdt_status qdt_mxfp4_linear_planned(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                                    const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi,
+                                    const void* epi_params, void* Y, int64_t ldy, void* workspace,
+                                    size_t workspace_bytes, qdt_linear_plan* plan, void* stream);
 
 /*
  * Weight-only block formats ([PTQ] GGUF paragraph: an 8-bit round-to-nearest format at 8.5 bits

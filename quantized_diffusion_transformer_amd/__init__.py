@@ -59,6 +59,9 @@ _SIGS = {
     "qdt_mxfp4_quantize": ([_P, _P, _I64, _I64, _I64, _P, _P, _P], _I),
     "qdt_mxfp4_linear": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P, _SZ, _P], _I),
     "qdt_mxfp4_linear_plan": ([_I64, _I64, _I64, _I, C.POINTER(qdt_linear_plan)], _I),
+    "qdt_mxfp4_linear_plan_for": ([_I64, _I64, _I64, _I, C.c_int32, C.c_int32, C.POINTER(qdt_linear_plan)], _I),
+    "qdt_mxfp4_linear_planned": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _I64, _P, _SZ,
+                                  C.POINTER(qdt_linear_plan), _P], _I),
     "qdt_wo_quantize": ([_P, _I64, _I64, _I64, _I, _P, _P, _P], _I),
     "qdt_wo_linear": ([_P, _I64, _P, _P, _I, _P, _I64, _I64, _I64, _I, _P, _I64, _P, _SZ, _P], _I),
     "qdt_wo_linear_plan": ([_I64, _I64, _I64, C.POINTER(qdt_linear_plan)], _I),
@@ -242,20 +245,25 @@ _MX_EPI = {"bias": QDT_EPI_BIAS, "silu_gate": QDT_EPI_SILU_GATE, "head_rmsnorm":
            "acc_f32": QDT_EPI_ACC_F32}
 
 
-def mxfp4_linear_plan(M: int, N: int, K: int, epilogue: str = "bias") -> dict:
+def mxfp4_linear_plan(M: int, N: int, K: int, epilogue: str = "bias", tile: int | None = None,
+                      split_k: int | None = None) -> dict:
     p = qdt_linear_plan()
-    _check(qdt_mxfp4_linear_plan(M, N, K, _MX_EPI[epilogue], C.byref(p)), "qdt_mxfp4_linear_plan")
+    if tile is None and split_k is None:
+        _check(qdt_mxfp4_linear_plan(M, N, K, _MX_EPI[epilogue], C.byref(p)), "qdt_mxfp4_linear_plan")
+    else:
+        _check(qdt_mxfp4_linear_plan_for(M, N, K, _MX_EPI[epilogue], QDT_TILE_AUTO if tile is None else tile,
+                                         0 if split_k is None else split_k, C.byref(p)), "qdt_mxfp4_linear_plan_for")
     return p.as_dict()
 
 
 def mxfp4_linear(Xq: torch.Tensor, Xs: torch.Tensor, Wq: torch.Tensor, Ws: torch.Tensor,
                  bias: torch.Tensor | None = None, epilogue: str = "bias", gamma=None, eps: float = 1e-6, out=None,
-                 workspace=None, stream=None) -> torch.Tensor:
+                 workspace=None, tile: int | None = None, split_k: int | None = None, stream=None) -> torch.Tensor:
     """Block-scaled FP4 linear: bf16 [M, N] = acc + bias ("bias"), bf16 [M, N/2] = silu(gate) * up
     ("silu_gate", W rows [gate; up]), RMSNorm of acc + bias over 256-wide heads with gamma
     ("head_rmsnorm"), or the fp32 accumulators ("acc_f32").
     Xq uint8 [M, K/2] and Xs uint8 [K/256, M, 8] from mxfp4_quantize of the activations; Wq, Ws the
-    same of the weights."""
+    same of the weights.  ``tile`` / ``split_k`` force a plan (by default the library plans)."""
     for t, n in ((Xq, "Xq"), (Xs, "Xs"), (Wq, "Wq"), (Ws, "Ws")):
         _dev(t, torch.uint8, n)
     if bias is not None:
@@ -275,13 +283,20 @@ def mxfp4_linear(Xq: torch.Tensor, Xs: torch.Tensor, Wq: torch.Tensor, Ws: torch
         out = torch.empty((M, nout), dtype=torch.float32 if epi == QDT_EPI_ACC_F32 else torch.bfloat16,
                           device=Xq.device)
     out, ldy = _rows(out, "out")
-    need = mxfp4_linear_plan(M, N, K, epilogue)["workspace_bytes"]
+    planned = tile is not None or split_k is not None
+    need = mxfp4_linear_plan(M, N, K, epilogue, tile, split_k)["workspace_bytes"]
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=Xq.device)
-    _check(qdt_mxfp4_linear(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(bias), M, N, K, epi,
-                            None if params is None else C.cast(C.byref(params), C.c_void_p), _ptr(out), ldy,
-                            _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
-                            _stream(stream)), "qdt_mxfp4_linear")
+    args = [_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(bias), M, N, K, epi,
+            None if params is None else C.cast(C.byref(params), C.c_void_p), _ptr(out), ldy,
+            _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size()]
+    if planned:
+        plan = qdt_linear_plan()
+        plan.tile = QDT_TILE_AUTO if tile is None else tile
+        plan.split_k = 0 if split_k is None else split_k
+        _check(qdt_mxfp4_linear_planned(*args, C.byref(plan), _stream(stream)), "qdt_mxfp4_linear_planned")
+    else:
+        _check(qdt_mxfp4_linear(*args, _stream(stream)), "qdt_mxfp4_linear")
     return out
 
 

@@ -65,7 +65,8 @@ static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // the split-K partial sums.  QDT_TILE_288 exists for the hidden width 4608 = 16 x 288: 256
 // tiles at 4608 x 4608, exactly one per compute unit, where 256 x 256 tiles leave a second
 // round that is only 68/256 full.
-qdt_status make_plan(int64_t M, int64_t N, int64_t K, int epi, int esize, int tile_req, int split_req, Plan* p) {
+qdt_status make_plan(int64_t M, int64_t N, int64_t K, int epi, int esize, int tile_req, int split_req, Plan* p,
+                     bool fp4) {
     const bool silu = epi == EPI_SILU, rms = epi == EPI_RMSNORM;
     Plan best{};
     double best_cost = -1.0;
@@ -75,8 +76,9 @@ qdt_status make_plan(int64_t M, int64_t N, int64_t K, int epi, int esize, int ti
         // 288 x 256 only on request: its weight and token waves issue unequal LDS-DMA counts and it
         // measured ~5% slower per FFN gate/up step than 256 x 256 despite fewer tile rounds
         if (tile == QDT_TILE_288x256 && tile_req == QDT_TILE_AUTO) continue;
-        // 224 x 256 is an int8 tile
-        if (tile == QDT_TILE_224x256 && esize != 1) continue;
+        // 224 x 256 is an int8 tile (its 56 MFMA slots per K step hold too few for FP4's exponent
+        // LDS-DMAs)
+        if (tile == QDT_TILE_224x256 && (esize != 1 || fp4)) continue;
         const int bm = tile == QDT_TILE_256 ? 256 : tile == QDT_TILE_224x256 ? 224 : 288;  // token rows
         const int bn = tile == QDT_TILE_288 ? 288 : 256;                                   // weight rows
         const int64_t kstage = 128;  // bytes of K per main-loop stage (whole cache lines)
@@ -447,34 +449,47 @@ qdt_status qdt_bf16_linear(const uint16_t* X, const uint16_t* W, const uint16_t*
     return hip_status(launch_gemm_bf16(a, p, reinterpret_cast<hipStream_t>(stream)));
 }
 
-// The planner's view of an FP4 problem: K/2 code bytes per row, 256 x 256 tiles (the only FP4
-// tile), the epilogue's tile constraints, K split chosen by the planner.
-static qdt_status mx_plan(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, Plan* p) {
+// The planner's view of an FP4 problem: K/2 code bytes per row, the int8 planner's tiles other
+// than 224 x 256 and its K split rule (or the requested tile and split).
+static qdt_status mx_plan(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, int tile_req, int split_req, Plan* p) {
     if (epi != QDT_EPI_BIAS && epi != QDT_EPI_SILU_GATE && epi != QDT_EPI_HEAD_RMSNORM && epi != QDT_EPI_ACC_F32)
         return QDT_EINVAL;
     if (M < 0 || M > INT32_MAX / 2 || N <= 0 || N > INT32_MAX / 2 || N % 16 != 0) return QDT_ESHAPE;
     if (epi == QDT_EPI_SILU_GATE && N % 32 != 0) return QDT_ESHAPE;
     if (epi == QDT_EPI_HEAD_RMSNORM && N % 256 != 0) return QDT_ESHAPE;
     if (K <= 0 || K % 256 != 0 || K > QDT_MAX_K) return QDT_ESHAPE;
+    if (tile_req != QDT_TILE_AUTO && (tile_req < QDT_TILE_256 || tile_req > QDT_TILE_288x256)) return QDT_EINVAL;
+    if (split_req < 0) return QDT_EINVAL;
     const int pk = epi == QDT_EPI_SILU_GATE ? EPI_SILU : epi == QDT_EPI_HEAD_RMSNORM ? EPI_RMSNORM : EPI_BIAS;
-    return make_plan(M, N, K / 2, pk, 1, QDT_TILE_256, 0, p);
+    return make_plan(M, N, K / 2, pk, 1, tile_req, split_req, p, true);
 }
 
 qdt_status qdt_mxfp4_linear_plan(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, qdt_linear_plan* plan) {
     if (!plan) return QDT_EINVAL;
     Plan p;
-    qdt_status r = mx_plan(M, N, K, epi, &p);
+    qdt_status r = mx_plan(M, N, K, epi, QDT_TILE_AUTO, 0, &p);
     if (r == QDT_OK) export_plan(p, plan);
     return r;
 }
 
-qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
-                            const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi,
-                            const void* epi_params, void* Y, int64_t ldy, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+qdt_status qdt_mxfp4_linear_plan_for(int64_t M, int64_t N, int64_t K, qdt_epilogue epi, int32_t tile, int32_t split_k,
+                                     qdt_linear_plan* plan) {
+    if (!plan) return QDT_EINVAL;
     Plan p;
-    qdt_status r = mx_plan(M, N, K, epi, &p);
+    qdt_status r = mx_plan(M, N, K, epi, tile, split_k, &p);
+    if (r == QDT_OK) export_plan(p, plan);
+    return r;
+}
+
+static qdt_status mx_linear_impl(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                                 const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi,
+                                 const void* epi_params, void* Y, int64_t ldy, void* workspace,
+                                 size_t workspace_bytes, int tile_req, int split_req, qdt_linear_plan* plan_out,
+                                 void* stream) {
+    Plan p;
+    qdt_status r = mx_plan(M, N, K, epi, tile_req, split_req, &p);
     if (r != QDT_OK) return r;
+    if (plan_out) export_plan(p, plan_out);
     const qdt_rmsnorm_params* rp = reinterpret_cast<const qdt_rmsnorm_params*>(epi_params);
     if (epi == QDT_EPI_HEAD_RMSNORM) {
         if (!rp || !rp->gamma) return QDT_EINVAL;
@@ -524,6 +539,23 @@ qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t*
     if ((r = hip_status(launch_gemm_mx(a, Xs, Ws, p, st))) != QDT_OK) return r;
     if (p.split_k > 1) return hip_status(launch_splitk_f32_epilogue(a, p.split_k, a.epi, st));
     return QDT_OK;
+}
+
+qdt_status qdt_mxfp4_linear(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                            const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi,
+                            const void* epi_params, void* Y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    return mx_linear_impl(Xq, Xs, Wq, Ws, bias, M, N, K, epi, epi_params, Y, ldy, workspace, workspace_bytes,
+                          QDT_TILE_AUTO, 0, nullptr, stream);
+}
+
+qdt_status qdt_mxfp4_linear_planned(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                                    const uint16_t* bias, int64_t M, int64_t N, int64_t K, qdt_epilogue epi,
+                                    const void* epi_params, void* Y, int64_t ldy, void* workspace,
+                                    size_t workspace_bytes, qdt_linear_plan* plan, void* stream) {
+    if (!plan) return QDT_EINVAL;
+    return mx_linear_impl(Xq, Xs, Wq, Ws, bias, M, N, K, epi, epi_params, Y, ldy, workspace, workspace_bytes,
+                          plan->tile, plan->split_k, plan, stream);
 }
 
 // The weight-only linear's plan: 256 x 256 tiles and K slices of QDT_WO_KSLICE elements,

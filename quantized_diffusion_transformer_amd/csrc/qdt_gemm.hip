@@ -87,16 +87,25 @@ __device__ __forceinline__ void mfma(typename AccT<BF16>::type& c, const v4u& a,
 }
 
 // Block-scaled FP4 MFMA, accumulator tied in place: A and B are 32 FP4 codes per lane (16 bytes,
-// the int8 fragment layout), sa / sb the biased block exponents of the lane's A and B blocks in
-// byte 0 (cbsz / blgp 4 select FP4 for both operands).
-template <bool ACC_AGPR>
+// the int8 fragment layout), sa / sb hold the biased block exponents of the lane's A and B blocks
+// in byte BYTE (0 or 1, chosen by op_sel; cbsz / blgp 4 select FP4 for both operands).
+template <bool ACC_AGPR, int BYTE>
 __device__ __forceinline__ void mfma_mx(v4f& c, const v4u& a, const v4u& b, uint32_t sa, uint32_t sb) {
-    if constexpr (ACC_AGPR)
-        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
-                     : "+a"(c) : "v"(a), "v"(b), "v"(sa), "v"(sb));
-    else
-        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
-                     : "+v"(c) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    if constexpr (BYTE == 0) {
+        if constexpr (ACC_AGPR)
+            asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                         : "+a"(c) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+        else
+            asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                         : "+v"(c) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    } else {
+        if constexpr (ACC_AGPR)
+            asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[1,1,0] op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                         : "+a"(c) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+        else
+            asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[1,1,0] op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                         : "+v"(c) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    }
 }
 
 // WM x WN waves, FM x FN fragments of 16x16 per wave.  BF16: bf16 operands; MX: block-scaled FP4
@@ -116,14 +125,22 @@ gemm_kernel(KArgs p) {
     constexpr int NBW = BN / 8, NBX = BM / 8;
     constexpr int NIW = NBW / 2, NIX = NBX / 2;
     constexpr int NI = NIW > NIX ? NIW : NIX;  // LDS-DMA slots per wave per stage
-    // FP4: 4 dword LDS-DMAs per wave and stage carry the block exponents of its 128 rows
-    // (8 bytes per row: the stage's 256 elements are 8 blocks)
-    constexpr int NSC = MX ? 4 : 0;
+    // FP4: dword LDS-DMAs carry the block exponents, 8 bytes per row and stage (the stage's 256
+    // elements are 8 blocks), 32 rows per instruction.  A region of R rows (weight or token rows)
+    // takes R / 32 of them, the first of its two waves ceil(R / 64), the second the rest; a wave
+    // with fewer than NSC repeats its last one (the same bytes to the same place).  The gate and
+    // up halves of SILU tiles are copied by their own waves.
+    constexpr int NDW = BN / 32, NDX = BM / 32;
+    constexpr int NSC = !MX ? 0 : ((NDW + 1) / 2 > (NDX + 1) / 2 ? (NDW + 1) / 2 : (NDX + 1) / 2);
     constexpr int NDMA = NI + NSC;
-    static_assert(!MX || (BM == 256 && BN == 256 && !BF16 &&
+    static_assert(!MX || (BM % 32 == 0 && BN % 32 == 0 && !BF16 &&
                           (EPI == EPI_F32BIAS || EPI == EPI_F32SILU || EPI == EPI_F32RMSNORM || EPI == EPI_ACC ||
                            EPI == EPI_PARTIAL)),
-                  "FP4: 256 x 256 tiles, fp32-accumulator epilogues");
+                  "FP4: tiles of whole 32-row exponent blocks, fp32-accumulator epilogues");
+    // The per-lane LDS-DMA offsets are held in registers, except for FP4 tiles of more than 256
+    // rows, where the registers go to the block exponents and the offsets are recomputed per
+    // instruction (a min and a multiply-add).
+    constexpr bool VOFF_REGS = !(MX && NI > 16);
     constexpr int NACC_A = 64;             // accumulator tuples held in AGPRs (the rest in VGPRs)
     constexpr bool SILU = EPI == EPI_SILU || EPI == EPI_F32SILU;
     constexpr bool RMS = EPI == EPI_RMSNORM || EPI == EPI_F32RMSNORM;
@@ -216,10 +233,19 @@ gemm_kernel(KArgs p) {
     }
     wbase = uniform_ptr(wbase + (int64_t)kta * BK);
     // lane offset of LDS-DMA i: row rlocal0 + 8 i + lane / 8, clamped to the region's last row
-    uint32_t voffs[NI];
+    uint32_t voffs[VOFF_REGS ? NI : 1];
+    int vrow = rlocal0 + (lane >> 3);  // recomputed offsets: lane row of instruction 0, chunk byte
+    const uint32_t vch = lchunk * 16;
+    if constexpr (VOFF_REGS) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) voffs[i] = (uint32_t)(min(rlocal0 + i * 8 + (lane >> 3), rlast) * Kb) + lchunk * 16;
-    auto voff = [&](int i) __attribute__((always_inline)) { return voffs[i]; };
+        for (int i = 0; i < NI; ++i) voffs[i] = (uint32_t)(min(vrow + i * 8, rlast) * Kb) + vch;
+    }
+    auto voff = [&](int i) __attribute__((always_inline)) {
+        if constexpr (VOFF_REGS)
+            return voffs[i];
+        else
+            return __umul24((uint32_t)min(vrow + i * 8, rlast), (uint32_t)Kb) + vch;
+    };
     const int blk0 = wwave ? wave * NIW : NBW + (wave - 2) * NIX;  // first LDS block of the wave
     const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds_offset(smem) + blk0 * 1024);
     // whether LDS-DMA slot i is used by this wave (all are when both regions have equal rows)
@@ -230,25 +256,49 @@ gemm_kernel(KArgs p) {
     };
     // FP4 block exponents, stored stage-major: for each 256-element stage, every row's 8 exponent
     // bytes are consecutive and rows follow each other (a stage's exponents of R rows are 8 R
-    // contiguous bytes).  Dword LDS-DMA i of a wave copies rows rlocal0 + 32 i .. + 31 of its region
+    // contiguous bytes).  Dword LDS-DMA i of a wave copies rows erow0 + 32 i .. + 31 of its region
     // (lane l: row + l / 2, dword l % 2, i.e. 256 contiguous bytes) to LDS [row][8 bytes] of the
-    // stage.
-    uint32_t scvoffs[NSC > 0 ? NSC : 1];
+    // stage; instructions past the wave's ecnt repeat its last one.
+    uint32_t scvoffs[NSC > 0 && VOFF_REGS ? NSC : 1];
     const uint8_t* scbase = nullptr;
     uint32_t ldss = 0;
     int64_t sstride = 0;  // exponent bytes per stage of the wave's operand (8 x its row count)
+    int ecnt = 1, erow0 = 0;
     if constexpr (MX) {
         const int wrow0 = (SILU && wave == 1 ? p.F : 0) + n0;  // the up half's rows for SILU
         sstride = __builtin_amdgcn_readfirstlane(wwave ? p.N : p.M) * (int64_t)8;
         scbase = uniform_ptr((wwave ? p.wsc + (int64_t)wrow0 * 8 : p.xsc + (int64_t)m0 * 8) + (int64_t)kta * sstride);
-#pragma unroll
-        for (int i = 0; i < NSC; ++i)
-            scvoffs[i] = (uint32_t)(min(rlocal0 + i * 32 + (lane >> 1), rlast) * 8) + (lane & 1) * 4;
-        const int row0 = wwave ? wave * NIW * 8 : BN + (wave - 2) * NIX * 8;
+        const bool first = (wave & 1) == 0;
+        if (wwave && SILU) {
+            ecnt = NDW / 2;
+            erow0 = 0;
+        } else {
+            const int nd = wwave ? NDW : NDX;
+            ecnt = first ? (nd + 1) / 2 : nd / 2;
+            erow0 = first ? 0 : 32 * ((nd + 1) / 2);
+        }
+        const int row0 = wwave ? (SILU ? wave * (BN / 2) : erow0) : BN + erow0;
         ldss = __builtin_amdgcn_readfirstlane(lds_offset(smem_sc) + row0 * 8);
     }
+    int erow = erow0 + (lane >> 1);  // lane row of exponent instruction 0
+    const uint32_t edw = (lane & 1) * 4;
+    auto scv = [&](int i) __attribute__((always_inline)) {
+        return (uint32_t)(min(erow + i * 32, rlast) * 8) + edw;
+    };
+    if constexpr (MX && VOFF_REGS) {
+#pragma unroll
+        for (int i = 0; i < NSC; ++i) scvoffs[i] = scv(min(i, ecnt - 1));
+    }
+    // lane offset of exponent instruction i (already limited to ecnt - 1)
+    auto scoff = [&](int i, int ie) __attribute__((always_inline)) {
+        if constexpr (VOFF_REGS)
+            return scvoffs[i];
+        else
+            return scv(ie);
+    };
     auto sdma = [&](int buf, int stage, int i) __attribute__((always_inline)) {
-        lds_dma4_s(ldss + (uint32_t)(buf * SCST + i * 256), scvoffs[i], scbase + (int64_t)stage * sstride);
+        const int ie = min(i, ecnt - 1);
+        lds_dma4_s(ldss + (uint32_t)(buf * SCST + ie * 256), scoff(i, ie), scbase + (int64_t)stage * sstride);
     };
 
     // Global weight row of tile weight row r (clamped like the operand rows).
@@ -313,9 +363,11 @@ gemm_kernel(KArgs p) {
     // FP4: the block exponent of this lane's row (lane & 15) of a fragment starting at tile row
     // `row`, K step ks of the stage: lane group q = lane >> 4 covers block 4 ks + q, stored at byte
     // 2 q + ks of the row's 8 bytes
+    // (both K steps' bytes of a block pair side by side: one 16-bit read gives the exponents of
+    // K step 0 in byte 0 and of K step 1 in byte 1)
     const int sclane = (lane & 15) * 8 + 2 * (lane >> 4);
-    auto sc = [&](int buf, int row, int ks) __attribute__((always_inline)) {
-        return (uint32_t)smem_sc[buf * SCST + row * 8 + ks + sclane];
+    auto sc16 = [&](int buf, int row) __attribute__((always_inline)) {
+        return (uint32_t)*reinterpret_cast<const uint16_t*>(&smem_sc[buf * SCST + row * 8 + sclane]);
     };
     auto frag = [&](const uint8_t* s, int row, int lck) __attribute__((always_inline)) {
         return *reinterpret_cast<const v4u*>(s + row * BK + lck);
@@ -337,14 +389,18 @@ gemm_kernel(KArgs p) {
     // the bias is converted to fp32 right after the first barrier.
     const int nkc = max(nk, 1);
     v4u a0[FN], b0[FM], a1[FN], b1[FM];
-    // FP4 block exponents of the fragments (one byte per lane in byte 0), per K step
-    uint32_t sa0[MX ? FN : 1], sb0[MX ? FM : 1], sa1[MX ? FN : 1], sb1[MX ? FM : 1];
-    auto mmx = [&](int g, int fm, const v4u& a, const v4u& b, uint32_t sa, uint32_t sb) __attribute__((always_inline)) {
+    // FP4 block exponents of the fragments for both K steps of a stage (byte 0: K step 0, byte 1:
+    // K step 1).  ea[g] (weight fragment g) is used by row g of both sub-steps, so the next stage's
+    // value is read into it right after row g of sub-step 1.  eb[fm] (token fragment fm) is used by
+    // every row: sub-step 1 works from a copy, eb1, while the next stage's values are read into eb.
+    uint32_t ea[MX ? FN : 1], eb[MX ? FM : 1], eb1[MX ? FM : 1];
+    auto mmx = [&](int g, int fm, const v4u& a, const v4u& b, uint32_t sa, uint32_t sb, auto byte) __attribute__((always_inline)) {
+        constexpr int BY = decltype(byte)::value;
         if constexpr (MX) {
             if (g * FM + fm < NACC_A)
-                mfma_mx<true>(acc[g][fm], a, b, sa, sb);
+                mfma_mx<true, BY>(acc[g][fm], a, b, sa, sb);
             else
-                mfma_mx<false>(acc[g][fm], a, b, sa, sb);
+                mfma_mx<false, BY>(acc[g][fm], a, b, sa, sb);
         } else {
             mma(g, fm, a, b);
         }
@@ -398,9 +454,9 @@ gemm_kernel(KArgs p) {
         for (int fm = 0; fm < FM; ++fm) b0[fm] = frag(s, xrow0 + fm * 16, lck0);
         if constexpr (MX) {
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) sa0[fn] = sc(0, wrow[fn], 0);
+            for (int fn = 0; fn < FN; ++fn) ea[fn] = sc16(0, wrow[fn]);
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) sb0[fm] = sc(0, xrow0 + fm * 16, 0);
+            for (int fm = 0; fm < FM; ++fm) eb[fm] = sc16(0, xrow0 + fm * 16);
         }
     }
     // one main-loop stage; DMA: issue the LDS-DMAs of stage j + 2, NEXT: read the first fragments
@@ -410,24 +466,25 @@ gemm_kernel(KArgs p) {
         const uint8_t* s = smem + (j % NB) * STAGE + lrow;
         const uint8_t* sn = smem + ((j + 1) % NB) * STAGE + lrow;
         const int jd = j + 2;
+        if constexpr (!VOFF_REGS) {
+            // the recomputed LDS-DMA offsets stay inside the loop (hoisted, they would hold the
+            // registers they are meant to free)
+            asm volatile("" : "+v"(vrow));
+            asm volatile("" : "+v"(erow));
+        }
+        using B0 = std::integral_constant<int, 0>;
+        using B1 = std::integral_constant<int, 1>;
         // sub-step 0: every SP-th slot reads b1[0..FM-1], then a1[0..FN-1]
 #pragma unroll
         for (int g = 0; g < FN; ++g) {
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
-                mmx(g, fm, a0[g], b0[fm], sa0[MX ? g : 0], sb0[MX ? fm : 0]);
+                mmx(g, fm, a0[g], b0[fm], ea[MX ? g : 0], eb[MX ? fm : 0], B0{});
                 const int k = g * FM + fm, q = k / SP;
                 if (k % SP == 0 && q < FM)
                     b1[q] = frag(s, xrow0 + q * 16, lck1);
                 else if (k % SP == 0 && q < FM + FN)
                     a1[q - FM] = frag(s, wrow[q - FM], lck1);
-                if constexpr (MX) {
-                    // block exponents of K step 1, between the fragment reads
-                    if (k % SP == SP / 2 && q < FM)
-                        sb1[q] = sc(j % NB, xrow0 + q * 16, 1);
-                    else if (k % SP == SP / 2 && q < FM + FN)
-                        sa1[q - FM] = sc(j % NB, wrow[q - FM], 1);
-                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -442,15 +499,20 @@ gemm_kernel(KArgs p) {
         const uint8_t* scbased = MX ? scbase + (int64_t)jd * sstride : nullptr;
         (void)ldssd;
         (void)scbased;
+        if constexpr (MX) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) eb1[fm] = eb[fm];
+        }
         if constexpr (DMA) set_m0(ldsd);
 #pragma unroll
         for (int g = 0; g < FN; ++g) {
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
-                mmx(g, fm, a1[g], b1[fm], sa1[MX ? g : 0], sb1[MX ? fm : 0]);
+                mmx(g, fm, a1[g], b1[fm], ea[MX ? g : 0], eb1[MX ? fm : 0], B1{});
                 const int k = g * FM + fm;
-                // LDS-DMA q at slot floor(q * S / NDMA), read q two slots later (FP4: its block
-                // exponents one slot later); the FP4 exponent LDS-DMAs follow the operand ones
+                // LDS-DMA q at slot floor(q * S / NDMA), read q two slots later (FP4: the next
+                // stage's token-fragment exponents one slot later); the FP4 exponent LDS-DMAs
+                // follow the operand ones
                 constexpr int S = FN * FM;
                 int qd = -1, qr = -1, qs = -1;
 #pragma unroll
@@ -458,22 +520,26 @@ gemm_kernel(KArgs p) {
 #pragma unroll
                 for (int t = 0; t < FM + FN; ++t) if ((t * S) / NDMA + 2 == k) qr = t;
 #pragma unroll
-                for (int t = 0; t < FM + FN; ++t) if ((t * S) / NDMA + 1 == k) qs = t;
+                for (int t = 0; t < FM; ++t) if ((t * S) / NDMA + 1 == k) qs = t;
                 if (qd >= 0 && qd < NI) {
-                    const uint32_t next = qd + 1 < NI || !MX ? ldsd + (uint32_t)((qd + 1) * 1024) : ldssd;
+                    // the wave's last operand LDS-DMA points M0 at its first exponent LDS-DMA
+                    const uint32_t next = MX && qd + 1 >= niw ? ldssd : ldsd + (uint32_t)((qd + 1) * 1024);
                     if (DMA && dma_used(qd)) lds_dma16_next(voff(qd), sbase, next);
                 } else if (qd >= NI) {
-                    if constexpr (MX && DMA)
-                        lds_dma4_next(scvoffs[qd - NI], scbased, ldssd + (uint32_t)((qd - NI + 1) * 256));
+                    if constexpr (MX && DMA) {
+                        const int i = qd - NI, ie = min(i, ecnt - 1), inext = min(i + 1, ecnt - 1);
+                        lds_dma4_next(scoff(i, ie), scbased, ldssd + (uint32_t)(inext * 256));
+                    }
                 } else if (NEXT && qr >= 0 && qr < FM)
                     b0[qr] = frag(sn, xrow0 + qr * 16, lck0);
                 else if (NEXT && qr >= FM)
                     a0[qr - FM] = frag(sn, wrow[qr - FM], lck0);
                 if constexpr (MX && NEXT) {
-                    if (qs >= 0 && qs < FM)
-                        sb0[qs] = sc((j + 1) % NB, xrow0 + qs * 16, 0);
-                    else if (qs >= FM)
-                        sa0[qs - FM] = sc((j + 1) % NB, wrow[qs - FM], 0);
+                    if (qs >= 0) eb[qs] = sc16((j + 1) % NB, xrow0 + qs * 16);
+                    // weight fragment g's exponents once row g is done: after the second MFMA of
+                    // row g + 1, and the last row's after the sub-step's last MFMA
+                    if (g >= 1 && fm == 1) ea[g - 1] = sc16((j + 1) % NB, wrow[g - 1]);
+                    if (g == FN - 1 && fm == FM - 1) ea[FN - 1] = sc16((j + 1) % NB, wrow[FN - 1]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -955,13 +1021,34 @@ hipError_t launch_gemm_mx(const GemmArgs& a, const uint8_t* xsc, const uint8_t* 
     k.Kb = a.K / 2;  // two FP4 codes per byte
     k.xsc = xsc;
     k.wsc = wsc;
+    const int epi = pl.split_k > 1 ? EPI_PARTIAL : a.epi;
+    if (pl.tile == QDT_TILE_288) {
+        switch (epi) {
+            case EPI_F32BIAS: return go<9, 9, false, EPI_F32BIAS, true>(k, pl.grid, st);
+            case EPI_ACC: return go<9, 9, false, EPI_ACC, true>(k, pl.grid, st);
+            case EPI_PARTIAL: return go<9, 9, false, EPI_PARTIAL, true>(k, pl.grid, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (pl.tile == QDT_TILE_288x256) {
+        switch (epi) {
+            case EPI_F32BIAS: return go<9, 8, false, EPI_F32BIAS, true>(k, pl.grid, st);
+            case EPI_F32SILU: return go<9, 8, false, EPI_F32SILU, true>(k, pl.grid, st);
+            case EPI_F32RMSNORM: return go<9, 8, false, EPI_F32RMSNORM, true>(k, pl.grid, st);
+            case EPI_ACC: return go<9, 8, false, EPI_ACC, true>(k, pl.grid, st);
+            case EPI_PARTIAL: return go<9, 8, false, EPI_PARTIAL, true>(k, pl.grid, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
     if (pl.tile != QDT_TILE_256) return hipErrorInvalidValue;
-    if (pl.split_k > 1) return go<8, 8, false, EPI_PARTIAL, true>(k, pl.grid, st);
-    if (a.epi == EPI_F32BIAS) return go<8, 8, false, EPI_F32BIAS, true>(k, pl.grid, st);
-    if (a.epi == EPI_F32SILU) return go<8, 8, false, EPI_F32SILU, true>(k, pl.grid, st);
-    if (a.epi == EPI_F32RMSNORM) return go<8, 8, false, EPI_F32RMSNORM, true>(k, pl.grid, st);
-    if (a.epi == EPI_ACC) return go<8, 8, false, EPI_ACC, true>(k, pl.grid, st);
-    return hipErrorInvalidValue;
+    switch (epi) {
+        case EPI_F32BIAS: return go<8, 8, false, EPI_F32BIAS, true>(k, pl.grid, st);
+        case EPI_F32SILU: return go<8, 8, false, EPI_F32SILU, true>(k, pl.grid, st);
+        case EPI_F32RMSNORM: return go<8, 8, false, EPI_F32RMSNORM, true>(k, pl.grid, st);
+        case EPI_ACC: return go<8, 8, false, EPI_ACC, true>(k, pl.grid, st);
+        case EPI_PARTIAL: return go<8, 8, false, EPI_PARTIAL, true>(k, pl.grid, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 // Block-scaled FP4 split-K: sums the S fp32 partial slices in slice order and applies the

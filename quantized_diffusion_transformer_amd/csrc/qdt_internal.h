@@ -41,7 +41,8 @@ struct Plan {
 
 // Planner: pure host computation.  esize = operand bytes (1 int8, 2 bf16).
 // tile_req / split_req: QDT_TILE_AUTO / 0 for automatic.
-qdt_status make_plan(int64_t M, int64_t N, int64_t K, int epi, int esize, int tile_req, int split_req, Plan* p);
+qdt_status make_plan(int64_t M, int64_t N, int64_t K, int epi, int esize, int tile_req, int split_req, Plan* p,
+                     bool fp4 = false);
 
 struct GemmArgs {
     const void* X;       // token operand [M][K] (int8 or bf16)

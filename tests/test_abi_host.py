@@ -112,6 +112,25 @@ def test_mxfp4_validation():
     assert qdt.mxfp4_linear_plan(4608, 4608, 4608)["split_k"] == 1
 
 
+def test_mxfp4_planner():
+    # 4608^3: 256 tiles of 288 x 288, one round on 256 compute units (324 tiles of 256 x 256 need two)
+    p = qdt.mxfp4_linear_plan(4608, 4608, 4608)
+    assert (p["tile_m"], p["tile_n"], p["grid"], p["split_k"]) == (288, 288, 256, 1)
+    # gated SiLU and head RMSNorm need 256 weight rows per tile; 288 x 256 only on request
+    assert qdt.mxfp4_linear_plan(4608, 24576, 4608, "silu_gate")["tile_n"] == 256
+    p = qdt.mxfp4_linear_plan(4608, 24576, 4608, "silu_gate", tile=qdt.QDT_TILE_288x256)
+    assert (p["tile_m"], p["tile_n"], p["tiles_n"]) == (288, 256, 96)
+    p = qdt.mxfp4_linear_plan(16896, 4608, 4608, "head_rmsnorm", tile=qdt.QDT_TILE_288x256)
+    assert (p["tile_m"], p["tile_n"], p["tiles_m"]) == (288, 256, 59)
+    with pytest.raises(qdt.QdtError):   # 288 x 288 has no 256-column head
+        qdt.mxfp4_linear_plan(4608, 4608, 4608, "head_rmsnorm", tile=qdt.QDT_TILE_288)
+    with pytest.raises(qdt.QdtError):   # 224 x 256 is an int8 tile
+        qdt.mxfp4_linear_plan(4608, 4608, 4608, tile=qdt.QDT_TILE_224x256)
+    # a forced K split
+    p = qdt.mxfp4_linear_plan(600, 1024, 8192, tile=qdt.QDT_TILE_288, split_k=4)
+    assert p["tile_m"] == 288 and p["split_k"] == 4 and p["workspace_bytes"] == 4 * 600 * 1024 * 4
+
+
 def test_weight_only_validation():
     q = qdt.qdt_wo_quantize
     assert q(A(), 16, 64, 64, 3, A(0x200000), A(0x300000), None) == qdt.QDT_EINVAL       # bits 4 or 8

@@ -275,3 +275,77 @@ def test_mxfp4_text_projection_shape():
     Wq, Ws = qdt.mxfp4_quantize(to_dev(d["W"]))
     Y = to_host(qdt.mxfp4_linear(Xq, Xs, Wq, Ws, to_dev(d["bias"]), "bias"))
     within_bound(Y, to_host(Xq), ex_host(Xs), to_host(Wq), ex_host(Ws), d["bias"], sample_rows(512, 4, 11))
+
+
+MX_TILES = [(qdt.QDT_TILE_256, "256x256"), (qdt.QDT_TILE_288, "288x288"), (qdt.QDT_TILE_288x256, "288x256")]
+
+
+@pytest.mark.parametrize("tile,tname", MX_TILES, ids=[t[1] for t in MX_TILES])
+@pytest.mark.parametrize("M,N,K", [(16, 16, 256), (170, 288, 256), (300, 272, 512), (600, 592, 1024)])
+def test_mxfp4_tiles_exact_accumulators(tile, tname, M, N, K):
+    """Every FP4 tile on exact-sum inputs, M and N ragged against it (170 rows end inside the
+    second exponent block copy of a 288-row region): the fp32 accumulators bit for bit."""
+    announce(f"mxfp4_linear exact tile {tname} M={M} N={N} K={K}")
+    Xq, Xs = exact_operands(M, K, 130 + M)
+    Wq, Ws = exact_operands(N, K, 140 + N)
+    _, acc = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, want_acc=True)
+    Y = to_host(qdt.mxfp4_linear(to_dev(Xq), ex_dev(Xs), to_dev(Wq), ex_dev(Ws), None, "acc_f32", tile=tile))
+    assert np.array_equal(Y.astype(np.float64), acc), f"{np.sum(Y != acc)} accumulators differ"
+
+
+@pytest.mark.parametrize("M,F,K", [(300, 272, 512), (600, 384, 1024)])
+def test_mxfp4_288x256_epilogues_exact_sums(M, F, K):
+    """The 288 x 256 tile's fused epilogues on exact-sum inputs: bias bit for bit, gated SiLU and
+    head RMSNorm within 1 ulp of the oracle."""
+    announce(f"mxfp4_linear 288x256 epilogues M={M} F={F} K={K}")
+    t = qdt.QDT_TILE_288x256
+    Xq, Xs = exact_operands(M, K, 150 + M)
+    Wq, Ws = exact_operands(2 * F, K, 160 + F)
+    rng = np.random.default_rng(F)
+    bias = W.f32_to_bf16_bits(rng.standard_normal(2 * F).astype(np.float32) * 4)
+    dX, dXs, dW, dWs, db = to_dev(Xq), ex_dev(Xs), to_dev(Wq), ex_dev(Ws), to_dev(bias)
+    Yb = to_host(qdt.mxfp4_linear(dX, dXs, dW, dWs, db, "bias", tile=t))
+    assert bits_equal(Yb, oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias))
+    Ys = to_host(qdt.mxfp4_linear(dX, dXs, dW, dWs, db, "silu_gate", tile=t))
+    assert ulp_bf16(Ys, oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, epi="silu_gate")).max() <= 1
+    N = 512
+    gamma = W.f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(256)).astype(np.float32))
+    Yr = to_host(qdt.mxfp4_linear(dX, dXs, to_dev(Wq[:N]), ex_dev(Ws[:N]), to_dev(bias[:N]), "head_rmsnorm",
+                                  gamma=to_dev(gamma), eps=1e-6, tile=t))
+    Yr_ref = oracle.mxfp4_gemm_rows(Xq, Xs, Wq[:N], Ws[:N], bias[:N], epi="head_rmsnorm", gamma=gamma, eps=1e-6)
+    assert ulp_bf16(Yr, Yr_ref).max() <= 1
+
+
+def test_mxfp4_results_do_not_depend_on_tile():
+    """General inputs, no K split: every output's K reduction runs through the same MFMA sequence
+    whatever the tile, so the outputs of all FP4 tiles are identical bit for bit."""
+    M, N, K = 600, 1024, 4608
+    announce(f"mxfp4_linear tile independence M={M} N={N} K={K}")
+    d = W.make_linear(M, N, K, seed=4400, x_kind="pct1", w_sigma=0.015, bias=True, epi="head_rmsnorm")
+    Xq, Xs = qdt.mxfp4_quantize(to_dev(d["X"]))
+    Wq, Ws = qdt.mxfp4_quantize(to_dev(d["W"]))
+    b, g = to_dev(d["bias"]), to_dev(d["gamma"])
+    for epi, tiles in (("bias", [t for t, _ in MX_TILES]), ("acc_f32", [t for t, _ in MX_TILES]),
+                       ("silu_gate", [qdt.QDT_TILE_256, qdt.QDT_TILE_288x256]),
+                       ("head_rmsnorm", [qdt.QDT_TILE_256, qdt.QDT_TILE_288x256])):
+        kw = dict(gamma=g, eps=d["eps"]) if epi == "head_rmsnorm" else {}
+        outs = [to_host(qdt.mxfp4_linear(Xq, Xs, Wq, Ws, b, epi, tile=t, split_k=1, **kw)) for t in tiles]
+        for t, o in zip(tiles[1:], outs[1:]):
+            assert bits_equal(o, outs[0]), f"{epi}: tile {t} differs from 256 x 256"
+
+
+@pytest.mark.parametrize("tile,tname", MX_TILES[1:], ids=[t[1] for t in MX_TILES[1:]])
+def test_mxfp4_split_k_exact_tiles(tile, tname):
+    """K split on the 288-row tiles: exact sums, accumulators and bias output bit for bit."""
+    M, N, K = 300, 576, 16384
+    plan = qdt.mxfp4_linear_plan(M, N, K, tile=tile)
+    assert plan["split_k"] > 1 and plan["tile_m"] == 288
+    announce(f"mxfp4_linear split-K {plan['split_k']} tile {tname} M={M} N={N} K={K}")
+    Xq, Xs = small_operands(M, K, 170)
+    Wq, Ws = small_operands(N, K, 180)
+    bias = W.f32_to_bf16_bits(np.random.default_rng(3).standard_normal(N).astype(np.float32))
+    dX, dXs, dW, dWs = to_dev(Xq), ex_dev(Xs), to_dev(Wq), ex_dev(Ws)
+    Y_ref, acc = oracle.mxfp4_gemm_rows(Xq, Xs, Wq, Ws, bias, want_acc=True)
+    Yacc = to_host(qdt.mxfp4_linear(dX, dXs, dW, dWs, None, "acc_f32", tile=tile))
+    assert np.array_equal(Yacc.astype(np.float64), acc), f"{np.sum(Yacc != acc)} accumulators differ"
+    assert bits_equal(to_host(qdt.mxfp4_linear(dX, dXs, dW, dWs, to_dev(bias), "bias", tile=tile)), Y_ref)

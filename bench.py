@@ -78,7 +78,14 @@ def to_dev(a):
 
 
 EVENT_EVERY = 10   # steps between event-bracketed steps (a timing event record costs ~5 us of stream time)
-MIN_EVENT_SAMPLES = 20
+MIN_EVENT_PAIRS = 10
+
+
+class _NoEvent:
+    """Stands in for an event a sampled step does not record."""
+
+    def record(self, *a, **k):
+        pass
 
 
 def warm_up(fn_step, sets, warmup, settle_ms=0.0):
@@ -98,23 +105,38 @@ def warm_up(fn_step, sets, warmup, settle_ms=0.0):
 def time_loop(fn_step, sets, steps, warmup, settle_ms=0.0, stats_out=None, clock_grid=None):
     """Wall time of `steps` steps (sync on both sides) + per-phase HIP event times.
 
-    Every k-th step of the timed region records HIP events (on the stream the library launches
-    on) around its two launches, k = EVENT_EVERY, or less so that there are at least
-    MIN_EVENT_SAMPLES samples; the others run without events.  With `clock_grid` (the GEMM's
-    workgroup count) the library's clock record is armed over the timed steps, and the GEMM's
-    shader clock during them goes to stats_out["clock"]."""
+    A step calls ev[0].record() before its first launch, ev[1].record() between its two launches
+    and ev[2].record() after the second.  Every k-th step of the timed region is sampled
+    (k = EVENT_EVERY, or less so that there are at least MIN_EVENT_PAIRS pairs of samples), and
+    the samples alternate: the first of a pair records ev[0] and ev[1] (phase 1 alone), the second
+    ev[0] and ev[2] only, so that no event sits between the two launches of the step whose second
+    phase is measured (an event record between two kernels delays the second one's start).  Phase
+    2 of a pair is the second sample's interval minus the first's; an event interval's own fixed
+    overhead cancels in that difference.  The other steps run without events.  With `clock_grid`
+    (the GEMM's workgroup count) the library's clock record is armed over the timed steps, and the
+    GEMM's shader clock during them goes to stats_out["clock"]."""
     import torch
-    nw = warm_up(fn_step, sets, warmup, settle_ms)
-    if stats_out is not None:
-        stats_out["warmup_steps_run"] = nw
-    every = max(1, min(EVENT_EVERY, steps // MIN_EVENT_SAMPLES))
+    # Everything the timed region needs is allocated before the warm-up: an allocation between the
+    # warm-up and the timed steps leaves the GPU idle for a few milliseconds, after which its clock
+    # takes ~40 ms of load to come back (measured: the first 400 steps after such a gap ran 7-9%
+    # slower), which is longer than the timed region.
+    every = max(1, min(EVENT_EVERY, steps // (2 * MIN_EVENT_PAIRS)))
     sampled = list(range(0, steps, every))
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+    sampled = sampled[: len(sampled) // 2 * 2]
+    none = _NoEvent()
+    evs = {}
+    for n, i in enumerate(sampled):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        evs[i] = [e[0], e[1], none] if n % 2 == 0 else [e[0], none, e[2]]
     rec = None
     if clock_grid is not None:
         import quantized_diffusion_transformer_amd as qdt
         rec = torch.zeros((steps * clock_grid, 4), dtype=torch.int64, device="cuda")
-        qdt.clock_record(rec)
+    nw = warm_up(fn_step, sets, warmup, settle_ms)
+    if stats_out is not None:
+        stats_out["warmup_steps_run"] = nw
+    if rec is not None:
+        qdt.clock_record(rec)  # host-side arming only
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -129,8 +151,10 @@ def time_loop(fn_step, sets, steps, warmup, settle_ms=0.0, stats_out=None, clock
     if stats_out is not None:
         stats_out["event_every"] = every
         stats_out["event_samples"] = len(sampled)
-    ph1 = [evs[i][0].elapsed_time(evs[i][1]) for i in sampled]
-    ph2 = [evs[i][1].elapsed_time(evs[i][2]) for i in sampled]
+        stats_out["event_pairs"] = len(sampled) // 2
+    ph1 = [evs[i][0].elapsed_time(evs[i][1]) for i in sampled[0::2]]
+    both = [evs[i][0].elapsed_time(evs[i][2]) for i in sampled[1::2]]
+    ph2 = [b - a for a, b in zip(ph1, both)]
     return (t1 - t0) * 1e3 / steps, ph1, ph2
 
 
@@ -447,6 +471,9 @@ def headline(args):
                      "algorithmic_ops_per_launch": ops, "avg_launch_ms": round(g["mean"], 5),
                      "launch_ms": {k: round(v, 5) for k, v in g.items()},
                      "event_samples": info["event_samples"],
+                     "timing": "HIP events on the library's stream, in pairs of sampled steps: (quantize + "
+                               "linear, no event between them) minus (quantize alone); the clock record's "
+                               "first-start-to-last-end span of the same launches is clock.kernel_span_us_median",
                      "peak_at_measured_clock": round(peak_clk, 1),
                      "frac_at_measured_clock": round(gemm_tops / peak_clk, 4)},
         "roofline_quantize": {"bound": "hbm", "kernel": "quant_rows_kernel (qdt_quantize_per_token)",

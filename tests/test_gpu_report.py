@@ -91,7 +91,7 @@ def test_workload_report(name, padded):
     for k, r in (("s", s_r), ("Wq", Wq_r), ("sw", sw_r), ("Xq", Xq_r), ("sx", sx_r)):
         assert bits_equal(to_host(g[k]), r), f"{k} differs from the oracle"
     real = 512 if padded else M  # padded: the text rows carry the information; the zero rows give the bias
-    rows = np.arange(real, dtype=np.int64) if real <= ROWS else sample_rows(real, ROWS, 7)
+    rows = np.arange(real, dtype=np.int64) if real <= 2 * ROWS else sample_rows(real, ROWS, 7)
     t0 = time.perf_counter()
     Y_ref = oracle.linear_rows(Xq_r, sx_r, Wq_r, sw_r, d.get("bias"), rows, epi, d.get("gamma"), 256,
                                d.get("eps", 1e-6))

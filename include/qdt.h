@@ -374,10 +374,15 @@ qdt_status qdt_bf16_linear(const uint16_t* X, const uint16_t* W, const uint16_t*
  *   the second product, like any bf16 flash-attention kernel, so the result is within a
  *   first-order error bound of the exact one: 2^-9 (bf16 probabilities) plus the fp32 error of the
  *   scores and of the two sums over S keys, times sum_j p_j |V[j]| / sum_j p_j, plus one bf16 ulp.
- *   Each query row is computed independently of the other rows.
+ *   Each query row is computed independently of the other rows.  The work is 256-query blocks per
+ *   head; when the blocks past a whole number of rounds on the 256 compute units would fill at most
+ *   half of a last round, each of those blocks is computed as floor(256 / count) key ranges whose
+ *   partial outputs, references and row sums are then merged (the same bound; the fp32 summation
+ *   order of those blocks' rows differs from a single pass).
  *   ld, ldo >= 256 H, both % 8 == 0; pointers 16-byte aligned; 1 <= H <= 1024, S <= QDT_ATTN_MAX_S.
  *   `workspace`: caller-owned device memory of qdt_attention_workspace_size bytes (V transposed per
- *   head, 16-byte aligned); no output may overlap an input or the workspace.  S = 0 is a no-op.
+ *   head, the rerun flags and the key-range pieces' partial outputs; 16-byte aligned); no output may
+ *   overlap an input or the workspace.  S = 0 is a no-op.
  */
 #define QDT_ATTN_HEAD_DIM 256
 #define QDT_ATTN_MAX_S (1 << 22)
@@ -385,7 +390,8 @@ qdt_status qdt_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V
                          uint16_t* O, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace qdt_attention needs: H * 256 * roundup(S, 32) * 2 for V transposed, plus one int
- * per 256-query block and head (padded to 16 bytes).  Pure host computation. */
+ * per workgroup (padded to 16 bytes), plus 256 * 258 * 4 bytes per key-range piece when the last
+ * round is split (S = 4608, H = 18: 68 blocks x 3 pieces, 53.9 MB).  Pure host computation. */
 qdt_status qdt_attention_workspace_size(int64_t S, int64_t H, size_t* bytes);
 
 /*

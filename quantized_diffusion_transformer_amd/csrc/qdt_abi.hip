@@ -647,9 +647,13 @@ qdt_status qdt_wo_linear(const uint16_t* X, int64_t ldx, const uint8_t* Wq, cons
     return hip_status(launch_splitk_f32_epilogue(a, p.split_k, e, st));
 }
 
-// Workspace: V^T per head (keys padded to a multiple of 32), then one int per workgroup.
+// Workspace: V^T per head (keys padded to a multiple of 32), then one int per workgroup (padded to
+// 16 bytes), then the fp32 outputs of the key-range pieces (none unless the plan splits).
 static int64_t attn_vt_bytes(int64_t S, int64_t H) { return H * QDT_ATTN_HEAD_DIM * ((S + 31) / 32 * 32) * 2; }
-static int64_t attn_ws_bytes(int64_t S, int64_t H) { return attn_vt_bytes(S, H) + ((S + 255) / 256 * H + 3) / 4 * 16; }
+static int64_t attn_redo_bytes(int64_t S, int64_t H) { return (attention_plan((int)S, (int)H).workgroups + 3) / 4 * 16; }
+static int64_t attn_ws_bytes(int64_t S, int64_t H) {
+    return attn_vt_bytes(S, H) + attn_redo_bytes(S, H) + attention_plan((int)S, (int)H).part_floats * 4;
+}
 
 qdt_status qdt_attention_workspace_size(int64_t S, int64_t H, size_t* bytes) {
     if (!bytes) return QDT_EINVAL;
@@ -677,6 +681,7 @@ qdt_status qdt_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V
     uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
     return hip_status(launch_attention(Q, K, V, (int)S, (int)H, ld, O, ldo, reinterpret_cast<uint16_t*>(ws),
                                        reinterpret_cast<int*>(ws + attn_vt_bytes(S, H)),
+                                       reinterpret_cast<float*>(ws + attn_vt_bytes(S, H) + attn_redo_bytes(S, H)),
                                        reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -85,9 +85,12 @@ struct AttnArgs {
     const uint16_t* K;
     const uint16_t* Vt;
     uint16_t* O;
-    int* redo;  // per workgroup: scores outgrew the reference (cleared by the V^T pass)
+    int* redo;    // per workgroup: scores outgrew the reference (cleared by the V^T pass)
+    float* part;  // key-range pieces: unnormalized O [piece][256 queries][256], then (m C, l) [piece][256][2]
     int64_t ld, ldo;
     int S, Spad, H, tiles_q;
+    int t_full;   // workgroups 0 .. t_full-1 take whole (query block, head) tiles over all keys
+    int split;    // each later tile is split over `split` key ranges (1: no later tiles)
 };
 
 // Output MFMA with the accumulator tuple tied in place in AGPRs (all 256 AGPRs hold accumulators).
@@ -112,7 +115,12 @@ __device__ __forceinline__ int at_ksw(int n) { return n & 15; }
 // V^T rows (64 bytes, 4 chunks): chunk c of row r in slot c ^ (bit 3 of r, moved to bit 1).
 __device__ __forceinline__ int at_vsw(int r) { return (r >> 2) & 2; }
 
-template <bool EXACT>
+// Which workgroups a launch holds: the whole tiles or the key-range pieces.  (One launch holding
+// both measured no faster for the rerun pass, and in the first pass the piece stores pushed the
+// register allocation of a kernel holding both into spills.)
+enum AttnWork { kWhole = 0, kPieces = 1 };
+
+template <bool EXACT, int WORK>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
 attn_fwd_kernel(AttnArgs p) {
     constexpr int KROW = AT_D * 2;           // LDS bytes per key row
@@ -123,14 +131,31 @@ attn_fwd_kernel(AttnArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STG];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int bid = blockIdx.x, nb = gridDim.x;
-    const int xcd = bid % kNumXCD, per = nb / kNumXCD, rem = nb % kNumXCD;
-    const int t = xcd * per + min(xcd, rem) + bid / kNumXCD;  // contiguous per XCD: one head's tiles
+    const int bid = blockIdx.x;
+    const int nkt = p.Spad / AT_BK;
+    // Work item of the workgroup.  Whole tiles (t_full of them, a whole number of rounds on the
+    // compute units) run over all keys, dealt so that each XCD holds a contiguous run (one head's
+    // tiles share K and V in its L2).  The remaining tiles would fill a last round only partly, so
+    // each is split into `split` key ranges, one workgroup each; a range's unnormalized output and
+    // its (reference, row sum) go to `part`, and attn_combine_kernel merges them.
+    int t, kt0 = 0, kt1 = nkt, piece = -1;
+    const int widx = WORK == kPieces ? p.t_full + bid : bid;  // index of the rerun flag
+    if (WORK == kWhole) {
+        const int nb = p.t_full;
+        const int xcd = bid % kNumXCD, per = nb / kNumXCD, rem = nb % kNumXCD;
+        t = xcd * per + min(xcd, rem) + bid / kNumXCD;
+    } else {
+        piece = bid;
+        const int part = piece % p.split;
+        t = p.t_full + piece / p.split;
+        kt0 = part * nkt / p.split;
+        kt1 = (part + 1) * nkt / p.split;
+    }
+    const int kend = min(p.S, kt1 * AT_BK);  // keys at or past kend are masked
     const int h = t / p.tiles_q, qt = t % p.tiles_q;
     const int q0 = qt * AT_BQ + 64 * wave;  // the wave's first query
-    const int nkt = p.Spad / AT_BK;
     if constexpr (EXACT) {
-        if (__builtin_amdgcn_readfirstlane(p.redo[t]) == 0) return;
+        if (__builtin_amdgcn_readfirstlane(p.redo[widx]) == 0) return;
     }
 
     // ---- Q fragments (B operand of S^T = K Q^T): lane holds query 16 qf + (lane & 15) of the wave,
@@ -231,9 +256,9 @@ attn_fwd_kernel(AttnArgs p) {
                 for (int qf = 0; qf < 4; ++qf) keep_after_v(s[kf][qf]);
         }
     };
-    // keys past S get -inf
+    // keys past S, or past the workgroup's key range, get -inf
     auto mask_tail = [&](int jt) __attribute__((always_inline)) {
-        if ((jt + 1) * AT_BK > p.S) {
+        if ((jt + 1) * AT_BK > kend) {
             mfma_drain();
 #pragma unroll
             for (int kf = 0; kf < 2; ++kf)
@@ -243,7 +268,7 @@ attn_fwd_kernel(AttnArgs p) {
             for (int kf = 0; kf < 2; ++kf)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const bool out = jt * AT_BK + 16 * kf + 4 * (lane >> 4) + r >= p.S;
+                    const bool out = jt * AT_BK + 16 * kf + 4 * (lane >> 4) + r >= kend;
 #pragma unroll
                     for (int qf = 0; qf < 4; ++qf)
                         if (out) s[kf][qf][r] = -__builtin_inff();
@@ -269,9 +294,9 @@ attn_fwd_kernel(AttnArgs p) {
     if constexpr (EXACT) {
         // first pass over the keys: the exact row max
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma_k(0, 0, i);
-        for (int jt = 0; jt < nkt; ++jt) {
-            const int buf = jt & 1, jn = min(jt + 1, nkt - 1);
+        for (int i = 0; i < 4; ++i) dma_k(0, kt0, i);
+        for (int jt = kt0; jt < kt1; ++jt) {
+            const int buf = (jt - kt0) & 1, jn = min(jt + 1, kt1 - 1);
             wait_vmcnt<0>();
             __syncthreads();
             scores(
@@ -349,21 +374,21 @@ attn_fwd_kernel(AttnArgs p) {
     // other registers, right before MFMAs that read them.
     v4u pprev[4], pnew[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma_k(0, 0, i);
+    for (int i = 0; i < 4; ++i) dma_k(0, kt0, i);
     {
         wait_vmcnt<0>();
         __syncthreads();
-        const int jn = min(1, nkt - 1);
+        const int jn = min(kt0 + 1, kt1 - 1);
         scores(
             0,
             [&](int g) __attribute__((always_inline)) {
                 if (g < 4)
                     dma_k(1, jn, g);
                 else if (g < 8)
-                    dma_v(0, 0, g - 4);
+                    dma_v(0, kt0, g - 4);
             },
             true);
-        mask_tail(0);
+        mask_tail(kt0);
         if constexpr (!EXACT) {
             // the reference: the first tile's max
 #pragma unroll
@@ -374,10 +399,11 @@ attn_fwd_kernel(AttnArgs p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) softmax_piece(qf, i, pprev);
     }
-    // nkt >= 1.  The loop leaves only through the drain, so the register copies the compiler places
+    // kt1 > kt0.  The loop leaves only through the drain, so the register copies the compiler places
     // on its exit edge read finished accumulators.
-    for (int jt = 1;; ++jt) {
-        const int buf = jt & 1, jn = min(jt + 1, nkt - 1), jv = min(jt, nkt - 1);
+    for (int lj = 1;; ++lj) {
+        const int jt = kt0 + lj;
+        const int buf = lj & 1, jn = min(jt + 1, kt1 - 1), jv = min(jt, kt1 - 1);
         wait_vmcnt<0>();
         __syncthreads();
         scores(
@@ -393,7 +419,7 @@ attn_fwd_kernel(AttnArgs p) {
         pv(buf ^ 1, pprev, true, pnew);
 #pragma unroll
         for (int qf = 0; qf < 4; ++qf) pprev[qf] = pnew[qf];
-        if (jt == nkt) {
+        if (jt == kt1) {
             mfma_drain();
             break;
         }
@@ -405,7 +431,7 @@ attn_fwd_kernel(AttnArgs p) {
         bool bad = false;
 #pragma unroll
         for (int qf = 0; qf < 4; ++qf) bad |= !(lp[qf] <= 0x1p64f);
-        if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) p.redo[t] = 1;
+        if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) p.redo[widx] = 1;
     }
     mfma_drain();
 #pragma unroll
@@ -413,6 +439,29 @@ attn_fwd_kernel(AttnArgs p) {
 #pragma unroll
         for (int qf = 0; qf < 4; ++qf) keep_after_a(oacc[df][qf]);
 
+    if (WORK == kPieces) {
+        // a key-range piece: its unnormalized output, its reference m C and row sum per query
+        float* po = p.part + (int64_t)piece * AT_BQ * AT_D;
+        float* pml = p.part + (int64_t)(p.H * p.tiles_q - p.t_full) * p.split * AT_BQ * AT_D + (int64_t)piece * AT_BQ * 2;
+#pragma unroll
+        for (int qf = 0; qf < 4; ++qf) {
+            float l = lp[qf];
+            l += __shfl_xor(l, 16, 64);
+            l += __shfl_xor(l, 32, 64);
+            const int ql = 64 * wave + 16 * qf + (lane & 15);  // query within the tile
+            float* dst = po + (int64_t)ql * AT_D + 4 * (lane >> 4);
+            // one accumulator tuple at a time: reading all 16 first would need 64 more VGPRs
+#pragma unroll
+            for (int df = 0; df < 16; ++df) {
+                *reinterpret_cast<v4f*>(dst + 16 * df) = oacc[df][qf];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if ((lane >> 4) == 0) {
+                pml[2 * ql] = mu[qf] * C;
+                pml[2 * ql + 1] = l;
+            }
+        }
+    } else {
     // ---- normalize by the full row sums and store 4 consecutive dims per lane
 #pragma unroll
     for (int qf = 0; qf < 4; ++qf) {
@@ -430,14 +479,64 @@ attn_fwd_kernel(AttnArgs p) {
                 make_uint2(pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv));
         }
     }
+    }
+}
+
+// ---------------------------------------------------------------------------- combine
+// Merges the key-range pieces of a split tile: with the pieces' references c_i = m_i C (log2 units)
+// and row sums l_i, M = max c_i, w_i = 2^(c_i - M), O = (sum_i w_i O_i) / (sum_i w_i l_i), summed
+// in piece order.  One thread per 4 dims of a query, 4 queries per block.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs p) {
+    const int64_t npieces = (int64_t)(p.H * p.tiles_q - p.t_full) * p.split;
+    const int per_tile = AT_BQ / 4;
+    const int tt = blockIdx.x / per_tile;
+    const int ql = (blockIdx.x % per_tile) * 4 + (threadIdx.x >> 6);
+    const int d = (threadIdx.x & 63) * 4;
+    const int t = p.t_full + tt;
+    const int h = t / p.tiles_q, q = (t % p.tiles_q) * AT_BQ + ql;
+    if (q >= p.S) return;
+    const float* ml = p.part + npieces * AT_BQ * AT_D;
+    float m = -__builtin_inff();
+    for (int i = 0; i < p.split; ++i) m = fmaxf(m, ml[((int64_t)(tt * p.split + i) * AT_BQ + ql) * 2]);
+    float l = 0.0f;
+    v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < p.split; ++i) {
+        const int64_t pc = (int64_t)tt * p.split + i;
+        const float w = __builtin_amdgcn_exp2f(ml[(pc * AT_BQ + ql) * 2] - m);
+        l += w * ml[(pc * AT_BQ + ql) * 2 + 1];
+        const v4f v = *reinterpret_cast<const v4f*>(p.part + (pc * AT_BQ + ql) * AT_D + d);
+        o += w * v;
+    }
+    const float inv = 1.0f / l;
+    *reinterpret_cast<uint2*>(p.O + (int64_t)q * p.ldo + h * AT_D + d) =
+        make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
+}
+
+// A last round of workgroups that would be less than half full (R tiles past a whole number of
+// rounds, R <= kNumCU / 2) is replaced by R x floor(kNumCU / R) key-range pieces, which fill it.
+AttnPlan attention_plan(int S, int H) {
+    AttnPlan pl;
+    const int tiles_q = (S + AT_BQ - 1) / AT_BQ;
+    const int nkt = (S + AT_BK - 1) / AT_BK;
+    pl.tiles = tiles_q * H;
+    const int r = pl.tiles % kNumCU;
+    int split = r > 0 && pl.tiles > kNumCU ? kNumCU / r : 1;
+    if (split > nkt) split = nkt;  // every piece holds at least one key tile
+    if (split < 2) split = 1;
+    pl.split = split;
+    pl.t_full = split > 1 ? pl.tiles - r : pl.tiles;
+    pl.workgroups = pl.t_full + (pl.tiles - pl.t_full) * split;
+    pl.part_floats = split > 1 ? (int64_t)(pl.tiles - pl.t_full) * split * AT_BQ * (AT_D + 2) : 0;
+    return pl;
 }
 
 hipError_t launch_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int S, int H, int64_t ld,
-                            uint16_t* O, int64_t ldo, uint16_t* Vt, int* redo, hipStream_t st) {
+                            uint16_t* O, int64_t ldo, uint16_t* Vt, int* redo, float* part, hipStream_t st) {
     const int Spad = (S + AT_BK - 1) / AT_BK * AT_BK;
     const int tiles_q = (S + AT_BQ - 1) / AT_BQ;
+    const AttnPlan pl = attention_plan(S, H);
     hipLaunchKernelGGL(attn_vt_kernel, dim3((Spad + 63) / 64, H), dim3(256), 0, st, V, ld, S, Spad, Vt, redo,
-                       tiles_q * H);
+                       pl.workgroups);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     AttnArgs a;
@@ -452,9 +551,23 @@ hipError_t launch_attention(const uint16_t* Q, const uint16_t* K, const uint16_t
     a.H = H;
     a.tiles_q = tiles_q;
     a.redo = redo;
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(tiles_q * H), dim3(256), 0, st, a);
+    a.part = part;
+    a.t_full = pl.t_full;
+    a.split = pl.split;
+    const int npieces = (pl.tiles - pl.t_full) * pl.split;
+    hipLaunchKernelGGL((attn_fwd_kernel<false, kWhole>), dim3(pl.t_full), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(tiles_q * H), dim3(256), 0, st, a);
+    if (npieces > 0) {
+        hipLaunchKernelGGL((attn_fwd_kernel<false, kPieces>), dim3(npieces), dim3(256), 0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((attn_fwd_kernel<true, kWhole>), dim3(pl.t_full), dim3(256), 0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((attn_fwd_kernel<true, kPieces>), dim3(npieces), dim3(256), 0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_combine_kernel, dim3((pl.tiles - pl.t_full) * (AT_BQ / 4)), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((attn_fwd_kernel<true, kWhole>), dim3(pl.t_full), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -174,6 +174,14 @@ def test_attention_validation():
     f = qdt.qdt_attention
     n = qdt.attention_workspace_size(100, 2)
     assert n == 2 * 256 * 128 * 2 + 16 and qdt.attention_workspace_size(256, 1) == 256 * 512 + 16
+    # 4608 tokens x 18 heads: 324 (query block, head) tiles, 68 past one round of 256, each split
+    # into 3 key ranges: 460 workgroups' rerun flags and 204 pieces' fp32 outputs
+    vt = 18 * 256 * 4608 * 2
+    assert qdt.attention_workspace_size(4608, 18) == vt + (460 + 3) // 4 * 16 + 204 * 256 * 258 * 4
+    # 16896 x 18: 1188 tiles, 164 past four rounds, more than half a round: no split
+    assert qdt.attention_workspace_size(16896, 18) == 18 * 256 * 16896 * 2 + (1188 + 3) // 4 * 16
+    # 2048 x 40: 320 tiles, 64 past one round, 4 key ranges each
+    assert qdt.attention_workspace_size(2048, 40) == 40 * 256 * 2048 * 2 + 512 // 4 * 16 + 256 * 256 * 258 * 4
 
     def att(S=100, H=2, ld=512, ldo=512, O=0x900000, ws=0x2000000, wsb=None, q=0x100000):
         return f(A(q), A(0x300000), A(0x500000), S, H, ld, A(O), ldo, A(ws), n if wsb is None else wsb, None)

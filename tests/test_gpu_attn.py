@@ -170,3 +170,56 @@ def test_attention_ragged_full_heads_sampled_rows():
     rows = np.array([0, 255, 256, 5887, 5888, 6000, 6036])
     for h in (0, 9, 17):
         within_bound(O, d["Q"], d["K"], d["V"], h, rows)
+
+
+# Shapes whose last round of workgroups is split into key ranges (qdt.h, qdt_attention): 2048 tokens
+# x 40 heads has 320 (query block, head) tiles; the 64 past one round of 256 (heads 32-39) run as 4
+# key ranges of 512 keys each, merged afterwards.  4608 x 18 (the attention after the 4608-token
+# projection) splits its last 68 tiles (head 14 from query 1024 on, heads 15-17) into 3 ranges.
+
+
+def test_attention_split_uniform_scores_exact():
+    """Zero queries with key-range pieces: every piece's probabilities are exactly 1 against the same
+    reference, so the merged output is the exact mean of V, bit for bit, in whole and split heads."""
+    S, H = 2048, 40
+    announce(f"attention split uniform S={S} H={H}")
+    rng = np.random.default_rng(940)
+    Q = np.zeros((S, 256 * H), np.uint16)
+    K = bf(rng.standard_normal((S, 256 * H)))
+    V = bf(rng.integers(-8, 9, (S, 256 * H)) * 0.25)
+    O = run(Q, K, V, H)
+    rows = np.array([0, 1000, S - 1])
+    for h in (0, 31, 32, 39):
+        assert bits_equal(O[rows][:, 256 * h:256 * h + 256], oracle.attention_rows(Q, K, V, h, rows)), f"head {h}"
+
+
+def test_attention_split_dominant_key_rerun_exact():
+    """A key 4000 raw points above the rest, inside the second key range of the split heads and past
+    that range's first tile: that piece is recomputed with its exact max, the other pieces' weights
+    2^(c_i - M) underflow to zero, and every output row is the key's V row, bit for bit."""
+    S, H, key = 2048, 40, 1000
+    announce(f"attention split dominant key S={S} H={H}")
+    rng = np.random.default_rng(950)
+    Q = np.zeros((S, 256 * H), np.float32)
+    K = np.zeros((S, 256 * H), np.float32)
+    for h in range(H):
+        Q[:, 256 * h] = 1.0
+        K[:, 256 * h] = rng.integers(-4, 5, S)
+        K[key, 256 * h] = 4000.0
+    V = bf(rng.standard_normal((S, 256 * H)))
+    O = run(bf(Q), bf(K), V, H)
+    for h in (0, 39):
+        c = slice(256 * h, 256 * h + 256)
+        assert np.array_equal(O[:, c], np.broadcast_to(V[key, c], (S, 256))), f"head {h}"
+
+
+def test_attention_split_full_size_sampled_rows():
+    """4608 tokens x 18 heads, the split layout: sampled rows of a whole head (0), a head that is
+    whole up to query 1023 and split after (14) and a split head (17), within the same bound."""
+    d = W.make_attention(4608, 18, seed=W.BASE_SEED + 1)
+    announce("attention 4608 x 18 heads (split last round)")
+    O = to_host(qdt.attention(to_dev(d["Q"]), to_dev(d["K"]), to_dev(d["V"]), 18))
+    rows = np.array([0, 255, 1023, 1024, 2500, 4607])
+    for h in (0, 14, 17):
+        exact = within_bound(O, d["Q"], d["K"], d["V"], h, rows)
+        print(f"head {h}: {exact:.3f} of the sampled outputs equal the correctly rounded result", flush=True)

@@ -503,7 +503,7 @@ gemm_kernel(KArgs p) {
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) eb1[fm] = eb[fm];
         }
-        if constexpr (DMA) set_m0(ldsd);
+        if constexpr (DMA) set_m0(MX ? ldssd : ldsd);
 #pragma unroll
         for (int g = 0; g < FN; ++g) {
 #pragma unroll
@@ -521,14 +521,16 @@ gemm_kernel(KArgs p) {
                 for (int t = 0; t < FM + FN; ++t) if ((t * S) / NDMA + 2 == k) qr = t;
 #pragma unroll
                 for (int t = 0; t < FM; ++t) if ((t * S) / NDMA + 1 == k) qs = t;
-                if (qd >= 0 && qd < NI) {
-                    // the wave's last operand LDS-DMA points M0 at its first exponent LDS-DMA
-                    const uint32_t next = MX && qd + 1 >= niw ? ldssd : ldsd + (uint32_t)((qd + 1) * 1024);
-                    if (DMA && dma_used(qd)) lds_dma16_next(voff(qd), sbase, next);
-                } else if (qd >= NI) {
+                // FP4: the exponent LDS-DMAs go first (they and the operand ones land before the next
+                // barrier; the earliest slots leave them the most time)
+                const int qop = MX ? qd - NSC : qd;  // operand LDS-DMA of this slot, if any
+                if (qd >= 0 && qop >= 0) {
+                    const uint32_t next = ldsd + (uint32_t)((qop + 1) * 1024);
+                    if (DMA && dma_used(qop)) lds_dma16_next(voff(qop), sbase, next);
+                } else if (qd >= 0) {
                     if constexpr (MX && DMA) {
-                        const int i = qd - NI, ie = min(i, ecnt - 1), inext = min(i + 1, ecnt - 1);
-                        lds_dma4_next(scoff(i, ie), scbased, ldssd + (uint32_t)(inext * 256));
+                        const int i = qd, ie = min(i, ecnt - 1), inext = min(i + 1, ecnt - 1);
+                        lds_dma4_next(scoff(i, ie), scbased, i + 1 < NSC ? ldssd + (uint32_t)(inext * 256) : ldsd);
                     }
                 } else if (NEXT && qr >= 0 && qr < FM)
                     b0[qr] = frag(sn, xrow0 + qr * 16, lck0);

@@ -312,18 +312,22 @@ hipError_t launch_quant_rows(const uint16_t* X, int64_t ldx, const float* colmul
 // mean and var: sum x and sum x^2 in fp64 (one pass), var = sum x^2 / K - mean^2, both rounded
 // to fp32.  The fp64 rounding errors stay far below the fp32 rounding of the results, so these
 // are the correctly rounded fp32 statistics except on rare near-ties, whatever the order.
-// One wave per row (K <= 8192), 8 waves per block.  The block stages inv_lambda (1 when absent),
-// 1 + scale and shift (0 when absent) as fp32 in LDS, 12 K bytes; 1 + scale is rounded exactly
-// as in the definition.  The row stays in registers from the load to the last store: X is read
-// once, Xq (and H on request) written once.  The kernel is bound by VALU issue more than by HBM
-// (about 20 operations per element).
-constexpr int kAdalnWaves = 8;
+// One wave per row (K <= 8192).  The block stages inv_lambda (1 when absent), 1 + scale and
+// shift (0 when absent) as fp32 in LDS, 12 K bytes; 1 + scale is rounded exactly as in the
+// definition.  The row stays in registers from the load to the last store: X is read once, Xq
+// (and H on request) written once.  The kernel is bound by VALU issue more than by HBM (about 25
+// operations per element), so the launch balances rows per SIMD: at most one block per compute
+// unit (16 waves, 4 per SIMD; 8 waves where the row needs more registers), each block a
+// contiguous run of floor or ceil(M / blocks) rows, taken by its waves in turn.  At 4608 rows
+// that is 18 rows per block and at most 5 per SIMD (a grid-stride launch of 8-wave blocks left
+// 6 on some SIMDs).
+constexpr int adaln_waves(int C) { return C <= 9 ? 16 : 8; }
 
 template <int C, bool QUANT>
-__global__ __launch_bounds__(kAdalnWaves * 64) void adaln_quant_kernel(
+__global__ __launch_bounds__(adaln_waves(C) * 64) void adaln_quant_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ shift,
     const uint16_t* __restrict__ scale, float eps, const float* __restrict__ colmul, int64_t M, int64_t K,
-    int8_t* __restrict__ Q, float* __restrict__ xscale, uint16_t* __restrict__ H) {
+    int8_t* __restrict__ Q, float* __restrict__ xscale, uint16_t* __restrict__ H, int64_t rq, int64_t rr) {
     extern __shared__ __attribute__((aligned(16))) float smem_f[];
     float* smul = smem_f;      // K: inv_lambda
     float* sg = smem_f + K;    // K: 1 + scale
@@ -355,9 +359,11 @@ __global__ __launch_bounds__(kAdalnWaves * 64) void adaln_quant_kernel(
         const float4 b = *reinterpret_cast<const float4*>(base + j * 8 + 4);
         o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
     };
-    const int64_t row0 = (int64_t)blockIdx.x * kAdalnWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t rstep = (int64_t)gridDim.x * kAdalnWaves;
-    for (int64_t row = row0; row < M; row += rstep) {
+    // rows [rb0, rb1) of this block: rq each, one more for the first rr blocks
+    constexpr int W = adaln_waves(C);
+    const int64_t rb0 = (int64_t)blockIdx.x * rq + min((int64_t)blockIdx.x, rr);
+    const int64_t rb1 = rb0 + rq + ((int64_t)blockIdx.x < rr ? 1 : 0);
+    for (int64_t row = rb0 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); row < rb1; row += W) {
         const uint16_t* x = X + row * ldx;
         uint4 raw[C];
 #pragma unroll
@@ -436,17 +442,18 @@ __global__ __launch_bounds__(kAdalnWaves * 64) void adaln_quant_kernel(
             lds8(smul, j, mm);
 #pragma unroll
             for (int e = 0; e < 8; ++e) vc[e] = elem(c, e) * mm[e];
+            // the largest distance to the nearest integer decides the chunk's path (one max per
+            // element instead of a compare and a flag)
             uint32_t b[8];
-            bool near = !fast;
+            float dmax = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float tq = vc[e] * rcp;
                 const float m = tq + kRoundMagic;
-                const float rr = m - kRoundMagic;
-                near |= fabsf(tq - rr) >= kNearTie;
+                dmax = fmaxf(dmax, fabsf(tq - (m - kRoundMagic)));
                 b[e] = __float_as_uint(m);
             }
-            if (near) {
+            if (!fast || dmax >= kNearTie) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) b[e] = (uint32_t)quant_exact(vc[e], sc);
             }
@@ -460,7 +467,7 @@ template <int C, bool QUANT>
 static hipError_t launch_adaln_cfg(const uint16_t* X, int64_t ldx, const uint16_t* shift, const uint16_t* scale,
                                    float eps, const float* colmul, int64_t M, int64_t K, int8_t* Q, float* xscale,
                                    uint16_t* H, hipStream_t st) {
-    const int threads = kAdalnWaves * 64;
+    const int threads = adaln_waves(C) * 64;
     const size_t lds = (size_t)K * 12;
     // cached like launch_quant_cfg's, for the largest LDS request of the configuration (K = 512 C)
     static std::atomic<int> per_cu_cache{0};
@@ -473,10 +480,10 @@ static hipError_t launch_adaln_cfg(const uint16_t* X, int64_t ldx, const uint16_
         per_cu = max(v, 1);
         per_cu_cache.store(per_cu, std::memory_order_relaxed);
     }
-    const int64_t units = (M + kAdalnWaves - 1) / kAdalnWaves;
+    const int64_t units = (M + adaln_waves(C) - 1) / adaln_waves(C);
     const int64_t blocks = min(units, (int64_t)per_cu * kNumCU);
     hipLaunchKernelGGL((adaln_quant_kernel<C, QUANT>), dim3((unsigned)blocks), dim3(threads), lds, st, X, ldx, shift,
-                       scale, eps, colmul, M, K, Q, xscale, H);
+                       scale, eps, colmul, M, K, Q, xscale, H, M / blocks, M % blocks);
     return hipGetLastError();
 }
 

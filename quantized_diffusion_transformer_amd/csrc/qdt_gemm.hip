@@ -20,7 +20,8 @@
 //     one ds_read_b128 fall in distinct banks.
 //   * Tile order is XCD-aware: workgroup ids are dealt round-robin to the 8 XCDs, so ids are
 //     remapped to give each XCD a contiguous run of tiles, walked in groups of `group_m` tile
-//     rows, which keeps the operands of neighbouring tiles in that XCD's L2.
+//     rows, which keeps the operands of neighbouring tiles in that XCD's L2 (with split-K, the
+//     K slice is the slowest index of the run).
 //   * Epilogue parameters are staged in LDS during the prologue; outputs go through LDS strips
 //     so that each store writes 16 contiguous bytes per lane.
 //   * Rows beyond M (or N) are clamped loads whose outputs are not stored; the integer sum is
@@ -185,8 +186,13 @@ gemm_kernel(KArgs p) {
     const int bid = blockIdx.x, nb = gridDim.x;
     const int xcd = bid % kNumXCD, per = nb / kNumXCD, rem = nb % kNumXCD;
     const int t = xcd * per + min(xcd, rem) + bid / kNumXCD;
-    const int split = t % p.split_k;
-    const int tt = t / p.split_k;
+    // K slice slowest: an XCD's run of workgroups covers one or two K slices of every tile, so
+    // its L2 fetches the token rows of those slices only (with the slice fastest, every XCD
+    // fetched every slice of X: 518 MB of L2 fills per 512 x 4608 x 53248 split-K-7 launch
+    // instead of 304 MB)
+    const int ntiles = p.tiles_m * p.tiles_n;
+    const int split = t / ntiles;
+    const int tt = t % ntiles;
     const int gsz = p.group_m * p.tiles_n;
     const int first_m = (tt / gsz) * p.group_m;
     const int gm = min(p.tiles_m - first_m, p.group_m);

@@ -122,6 +122,17 @@ __device__ __forceinline__ int quant_exact(float v, float sc) {
     return (int)q;
 }
 
+// A 16-byte load of activations, which these kernels read exactly once: non-temporal, so the
+// stream does not displace what the next kernel reads (the weights and the quantized X, from L2
+// and the Infinity Cache).  Measured on the 4608 x 4608 quantize pass: 17.0 -> 14.3 us, and the
+// quantize + linear step 92.7 -> 91.1 us; the fused adaLN 25.1 -> 25.0 us (4608 rows) and 60.5 -> 59.8 us
+// (16896 rows).  The FP4 quantizer keeps plain loads (its 4608 x 4608 step measured 1 us slower).
+__device__ __forceinline__ uint4 load_once16(const uint16_t* p) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // bytes 0 of a, b, c, d -> one dword (a in byte 0)
 __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
@@ -171,7 +182,7 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : WPR * 64) void quant_rows_kernel(
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const int64_t j = t + (int64_t)c * NT;
-            raw[c] = j < nch ? *reinterpret_cast<const uint4*>(x + j * 8) : make_uint4(0u, 0u, 0u, 0u);
+            raw[c] = j < nch ? load_once16(x + j * 8) : make_uint4(0u, 0u, 0u, 0u);
         }
         // v = bf16 element * multiplier; chunk c, computed again in the second pass when the
         // row does not fit in registers as fp32 (C > 12)
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(adaln_waves(C) * 64) void adaln_quant_kernel(
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const int64_t j = lane + (int64_t)c * 64;
-            raw[c] = j < nch ? *reinterpret_cast<const uint4*>(x + j * 8) : make_uint4(0u, 0u, 0u, 0u);
+            raw[c] = j < nch ? load_once16(x + j * 8) : make_uint4(0u, 0u, 0u, 0u);
         }
         // element e of chunk c (bf16 pairs, low half first)
         auto elem = [&](int c, int e) __attribute__((always_inline)) {

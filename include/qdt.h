@@ -380,18 +380,21 @@ qdt_status qdt_bf16_linear(const uint16_t* X, const uint16_t* W, const uint16_t*
  *   partial outputs, references and row sums are then merged (the same bound; the fp32 summation
  *   order of those blocks' rows differs from a single pass).
  *   ld, ldo >= 256 H, both % 8 == 0; pointers 16-byte aligned; 1 <= H <= 1024, S <= QDT_ATTN_MAX_S.
- *   `workspace`: caller-owned device memory of qdt_attention_workspace_size bytes (V transposed per
- *   head, the rerun flags and the key-range pieces' partial outputs; 16-byte aligned); no output may
- *   overlap an input or the workspace.  S = 0 is a no-op.
+ *   `workspace`: caller-owned device memory of qdt_attention_workspace_size bytes (past 8192 tokens
+ *   V transposed per head, written by a first pass; the waves' rerun flags; the key-range pieces'
+ *   partial outputs; 16-byte aligned); no output may overlap an input or the workspace.  Up to 8192
+ *   tokens the kernel reads V's rows transposed from LDS instead of a transposed copy (the same
+ *   results bit for bit).  S = 0 is a no-op.
  */
 #define QDT_ATTN_HEAD_DIM 256
 #define QDT_ATTN_MAX_S (1 << 22)
 qdt_status qdt_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int64_t S, int64_t H, int64_t ld,
                          uint16_t* O, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace qdt_attention needs: H * 256 * roundup(S, 32) * 2 for V transposed, plus one int
- * per workgroup (padded to 16 bytes), plus 256 * 258 * 4 bytes per key-range piece when the last
- * round is split (S = 4608, H = 18: 68 blocks x 3 pieces, 53.9 MB).  Pure host computation. */
+/* Bytes of workspace qdt_attention needs: H * 256 * roundup(S, 32) * 2 for V transposed when
+ * S > 8192 (0 otherwise), plus 16 bytes per workgroup (one int per wave), plus 256 * 258 * 4 bytes
+ * per key-range piece when the last round is split (S = 4608, H = 18: 68 blocks x 3 pieces, 53.9 MB).
+ * Pure host computation. */
 qdt_status qdt_attention_workspace_size(int64_t S, int64_t H, size_t* bytes);
 
 /*

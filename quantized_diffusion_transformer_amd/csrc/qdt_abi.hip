@@ -647,10 +647,13 @@ qdt_status qdt_wo_linear(const uint16_t* X, int64_t ldx, const uint8_t* Wq, cons
     return hip_status(launch_splitk_f32_epilogue(a, p.split_k, e, st));
 }
 
-// Workspace: V^T per head (keys padded to a multiple of 32), then one int per workgroup (padded to
-// 16 bytes), then the fp32 outputs of the key-range pieces (none unless the plan splits).
-static int64_t attn_vt_bytes(int64_t S, int64_t H) { return H * QDT_ATTN_HEAD_DIM * ((S + 31) / 32 * 32) * 2; }
-static int64_t attn_redo_bytes(int64_t S, int64_t H) { return (attention_plan((int)S, (int)H).workgroups + 3) / 4 * 16; }
+// Workspace: V^T per head (keys padded to a multiple of 32; only past kAttnVtrMaxS tokens, shorter
+// sequences read V transposed in LDS), then 4 ints per workgroup (the waves' rerun flags), then the
+// fp32 outputs of the key-range pieces (none unless the plan splits).
+static int64_t attn_vt_bytes(int64_t S, int64_t H) {
+    return attention_plan((int)S, (int)H).vtr ? 0 : H * QDT_ATTN_HEAD_DIM * ((S + 31) / 32 * 32) * 2;
+}
+static int64_t attn_redo_bytes(int64_t S, int64_t H) { return (int64_t)attention_plan((int)S, (int)H).workgroups * 16; }
 static int64_t attn_ws_bytes(int64_t S, int64_t H) {
     return attn_vt_bytes(S, H) + attn_redo_bytes(S, H) + attention_plan((int)S, (int)H).part_floats * 4;
 }

@@ -45,13 +45,12 @@ __device__ __forceinline__ int vt_key_of_pos(int p) {
 
 // ---------------------------------------------------------------------------- V -> V^T
 // Block (64-key block kb, head h): V rows kb*64 .. +63 of head h into LDS, then each thread writes
-// one dim row of V^T: 64 keys in the permuted order, zeros past S.
+// one dim row of V^T: 64 keys in the permuted order, zeros past S.  (Only for S past
+// kAttnVtrMaxS; shorter sequences read V transposed from LDS instead.)
 __global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* __restrict__ V, int64_t ld, int S, int Spad,
-                                                      uint16_t* __restrict__ Vt, int* __restrict__ redo, int nredo) {
+                                                      uint16_t* __restrict__ Vt) {
     __shared__ __attribute__((aligned(16))) uint16_t tile[64][AT_D];
     const int kb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-    if (kb == 0 && h == 0)
-        for (int i = tid; i < nredo; i += 256) redo[i] = 0;
     const int k0 = kb * 64;
     for (int c = tid; c < 64 * (AT_D / 8); c += 256) {
         const int r = c / (AT_D / 8), ch = c % (AT_D / 8);
@@ -83,9 +82,10 @@ __global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* __restrict
 struct AttnArgs {
     const uint16_t* Q;
     const uint16_t* K;
-    const uint16_t* Vt;
+    const uint16_t* Vt;  // V^T from attn_vt_kernel (VTR false)
+    const uint16_t* V;   // V itself (VTR true)
     uint16_t* O;
-    int* redo;    // per workgroup: scores outgrew the reference (cleared by the V^T pass)
+    int* redo;    // per wave (4 per workgroup): scores outgrew the reference; written on every call
     float* part;  // key-range pieces: unnormalized O [piece][256 queries][256], then (m C, l) [piece][256][2]
     int64_t ld, ldo;
     int S, Spad, H, tiles_q;
@@ -114,13 +114,23 @@ __device__ __forceinline__ void mfma_s0(v4f& c, const v4u& a, const v4u& b) {
 __device__ __forceinline__ int at_ksw(int n) { return n & 15; }
 // V^T rows (64 bytes, 4 chunks): chunk c of row r in slot c ^ (bit 3 of r, moved to bit 1).
 __device__ __forceinline__ int at_vsw(int r) { return (r >> 2) & 2; }
+// V rows, read transposed (512 bytes, 32 chunks; key r of the tile): chunk c in slot c ^ 2 (r mod 8).
+// A transposing fragment read touches 16 key rows, 8 per half-wave, at chunks 2 df and 2 df + 1:
+// each half-wave covers the 64 banks once (SQ_LDS_BANK_CONFLICT reads 0).
+__device__ __forceinline__ int at_vsw2(int r) { return 2 * (r & 7); }
+typedef short at_v4s __attribute__((ext_vector_type(4)));
+typedef uint32_t at_u2 __attribute__((ext_vector_type(2)));
 
 // Which workgroups a launch holds: the whole tiles or the key-range pieces.  (One launch holding
 // both measured no faster for the rerun pass, and in the first pass the piece stores pushed the
 // register allocation of a kernel holding both into spills.)
 enum AttnWork { kWhole = 0, kPieces = 1 };
 
-template <bool EXACT, int WORK>
+// VTR: the PV product reads V's rows transposed from LDS (ds_read_b64_tr_b16) instead of a V^T
+// written by a separate pass.  Per tile that is two LDS reads per fragment instead of one and a few
+// more VALU instructions (the main loop measured ~3% slower), against the V^T pass (~5.2 ns per
+// token and head block of 18: 24 us of a 0.36 ms call at 4608 tokens, 88 us of 4.1 ms at 16896).
+template <bool EXACT, int WORK, bool VTR>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
 attn_fwd_kernel(AttnArgs p) {
     constexpr int KROW = AT_D * 2;           // LDS bytes per key row
@@ -155,7 +165,8 @@ attn_fwd_kernel(AttnArgs p) {
     const int h = t / p.tiles_q, qt = t % p.tiles_q;
     const int q0 = qt * AT_BQ + 64 * wave;  // the wave's first query
     if constexpr (EXACT) {
-        if (__builtin_amdgcn_readfirstlane(p.redo[widx]) == 0) return;
+        const int4 f = *reinterpret_cast<const int4*>(p.redo + 4 * widx);
+        if (__builtin_amdgcn_readfirstlane(f.x | f.y | f.z | f.w) == 0) return;
     }
 
     // ---- Q fragments (B operand of S^T = K Q^T): lane holds query 16 qf + (lane & 15) of the wave,
@@ -181,7 +192,8 @@ attn_fwd_kernel(AttnArgs p) {
     // its LDS slot under the swizzles above.  Keys past S are clamped to the last key (their
     // scores are masked).
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.K + h * AT_D);
-    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.Vt + (int64_t)h * AT_D * p.Spad);
+    const uint8_t* vbase = VTR ? reinterpret_cast<const uint8_t*>(p.V + h * AT_D)
+                               : reinterpret_cast<const uint8_t*>(p.Vt + (int64_t)h * AT_D * p.Spad);
     const uint32_t ldsk = __builtin_amdgcn_readfirstlane(lds_offset(smem) + wave * 4 * 1024);
     const uint32_t ldsv = ldsk + KT;
     // Per-lane offsets, computed once: K instruction i of this wave moves key rows
@@ -195,8 +207,11 @@ attn_fwd_kernel(AttnArgs p) {
         const int row = 2 * (4 * wave + i) + (lane >> 5);
         koff[i] = (uint32_t)(row * p.ld * 2) + (uint32_t)(((lane & 31) ^ at_ksw(row & 15)) * 16);
     }
-    const uint32_t voff = (uint32_t)((64 * wave + (lane >> 2)) * p.Spad * 2) +
-                          (uint32_t)(((lane & 3) ^ at_vsw(lane >> 2)) * 16);
+    const uint32_t voff = VTR ? 0u : (uint32_t)((64 * wave + (lane >> 2)) * p.Spad * 2) +
+                                     (uint32_t)(((lane & 3) ^ at_vsw(lane >> 2)) * 16);
+    // VTR: V instruction i of this wave moves key rows 2 (4 w + i) + (lane >> 5), as for K, under
+    // the V swizzle, its offset computed per instruction (an array of them would not fit)
+    int vdrow = 8 * wave + (lane >> 5);
     auto dma_k = [&](int buf, int jt, int i) __attribute__((always_inline)) {
         const int key0 = jt * AT_BK;
         uint32_t off = koff[i];
@@ -207,8 +222,18 @@ attn_fwd_kernel(AttnArgs p) {
         lds_dma16_s(ldsk + (uint32_t)(buf * STG + i * 1024), off, kbase + (int64_t)key0 * p.ld * 2);
     };
     auto dma_v = [&](int buf, int jt, int i) __attribute__((always_inline)) {
-        lds_dma16_s(ldsv + (uint32_t)(buf * STG + i * 1024), voff,
-                    vbase + (int64_t)jt * AT_BK * 2 + (int64_t)16 * i * p.Spad * 2);
+        if constexpr (VTR) {
+            const int key0 = jt * AT_BK;
+            asm volatile("" : "+v"(vdrow));
+            const int row = vdrow + 2 * i;
+            // rows past S read the last key: their probabilities are 0
+            const uint32_t off = (uint32_t)(min(row, p.S - 1 - key0) * p.ld * 2) +
+                                 (uint32_t)(((lane & 31) ^ at_vsw2(row)) * 16);
+            lds_dma16_s(ldsv + (uint32_t)(buf * STG + i * 1024), off, vbase + (int64_t)key0 * p.ld * 2);
+        } else {
+            lds_dma16_s(ldsv + (uint32_t)(buf * STG + i * 1024), voff,
+                        vbase + (int64_t)jt * AT_BK * 2 + (int64_t)16 * i * p.Spad * 2);
+        }
     };
     // K fragment (A operand): key 16 kf + (lane & 15) of the tile, dims 32 kk + 8 (lane >> 4) .. + 7
     auto kfrag = [&](int buf, int kf, int kk) __attribute__((always_inline)) {
@@ -221,6 +246,30 @@ attn_fwd_kernel(AttnArgs p) {
         const int row = 16 * df + (lane & 15);
         return *reinterpret_cast<const v4u*>(smem + buf * STG + KT + row * VROW +
                                              (((lane >> 4) ^ at_vsw(lane & 15)) * 16));
+    };
+    // VTR: the same fragment from the V rows, with two transposing reads.  In each 16-lane group g,
+    // lane j points at dims 16 df + 4 (j & 3) .. + 3 of the key at position 8 g + 4 h + (j >> 2),
+    // and lane i receives dim 16 df + i of the 4 keys at positions 8 g + 4 h .. + 3 (measured lane
+    // layout: lane i gets element i & 3 of the chunks of lanes 4 k + (i >> 2), k = 0..3).  Position
+    // 8 g + k (k < 4) holds key 4 g + k = lane >> 2 of the pointing lane, position 8 g + 4 + k key
+    // 16 + (lane >> 2): the same row modulo 8, 16 rows (8 KiB) further.  The row offset has bits 5-7
+    // clear, so the slot xor acts on the address: vrx = row offset | 32 (key mod 8), and dims
+    // 16 df .. lie at (vrx ^ 32 (df mod 8)) + 256 (df / 8).
+    uint32_t vrx = ((uint32_t)(KT + (lane >> 2) * KROW) + ((lane & 2) >> 1) * 16 + 8 * (lane & 1)) |
+                   (32u * ((lane >> 2) & 7));
+    auto vfrag_tr = [&](int buf, int df, uint32_t xa) __attribute__((always_inline)) {
+        auto tr = [&](int hk) __attribute__((always_inline)) {
+            const uint8_t* a = smem + buf * STG + hk * 16 * KROW + 256 * (df >> 3) + xa;
+            return __builtin_bit_cast(at_u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                 (__attribute__((address_space(3))) at_v4s*)(const_cast<uint8_t*>(a))));
+        };
+        const at_u2 lo = tr(0), hi = tr(1);
+        v4u r;
+        r[0] = lo.x;
+        r[1] = lo.y;
+        r[2] = hi.x;
+        r[3] = hi.y;
+        return r;
     };
 
     // ---- scores of the key tile in K buffer buf: S^T = K Q^T, lane holds keys
@@ -350,16 +399,32 @@ attn_fwd_kernel(AttnArgs p) {
     // of query 16 qf + (lane & 15)), each MFMA followed by one softmax piece of the current scores
     auto pv = [&](int vbuf, const v4u (&pp)[4], bool with_softmax, v4u (&pn)[4]) __attribute__((always_inline)) {
         asm volatile("s_nop 1");  // VALU-written P -> MFMA source
+        // VTR: the fragments go in the order 0, 8, 1, 9, .., so that a pair shares its address
+        // (each fragment has its own accumulators, so any order gives the same sums; the softmax
+        // pieces keep their slots).  The address base is pinned here: hoisted out of the loop, the
+        // per-read addresses would take registers the kernel does not have.
+        if constexpr (VTR) asm volatile("" : "+v"(vrx));
+        auto fdf = [](int n) { return VTR ? (n >> 1) + 8 * (n & 1) : n; };
         v4u va[16];
+        uint32_t xa[VTR ? 8 : 1];
+        auto load = [&](int n) __attribute__((always_inline)) {
+            if constexpr (VTR) {
+                if ((n & 1) == 0) xa[n >> 1] = vrx ^ (32u * (n >> 1));
+                va[n] = vfrag_tr(vbuf, fdf(n), xa[n >> 1]);
+            } else {
+                va[n] = vfrag(vbuf, n);
+            }
+        };
 #pragma unroll
-        for (int df = 0; df < AT_LA; ++df) va[df] = vfrag(vbuf, df);
+        for (int n = 0; n < AT_LA; ++n) load(n);
 #pragma unroll
-        for (int df = 0; df < 16; ++df) {
-            if (df + AT_LA < 16) va[df + AT_LA] = vfrag(vbuf, df + AT_LA);
+        for (int n = 0; n < 16; ++n) {
+            if (n + AT_LA < 16) load(n + AT_LA);
+            const int df = fdf(n);
 #pragma unroll
             for (int qf = 0; qf < 4; ++qf) {
-                mfma_o(oacc[df][qf], va[df], pp[qf]);
-                if (with_softmax) softmax_piece(df / 4, 4 * (df % 4) + qf, pn);
+                mfma_o(oacc[df][qf], va[n], pp[qf]);
+                if (with_softmax) softmax_piece(n / 4, 4 * (n % 4) + qf, pn);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -427,11 +492,13 @@ attn_fwd_kernel(AttnArgs p) {
     wait_vmcnt<0>();  // the last iteration's LDS-DMAs land before the workgroup ends
     if constexpr (!EXACT) {
         // a probability past 2^64 (a score more than 64 log2 units above the reference) leaves a
-        // lane's partial row sum past 2^64: flag the workgroup for the exact-max rerun
+        // lane's partial row sum past 2^64: flag the wave for the exact-max rerun (each wave writes
+        // its flag on every call, so no pass has to clear them)
         bool bad = false;
 #pragma unroll
         for (int qf = 0; qf < 4; ++qf) bad |= !(lp[qf] <= 0x1p64f);
-        if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) p.redo[widx] = 1;
+        const bool any = __builtin_amdgcn_ballot_w64(bad) != 0;
+        if (lane == 0) p.redo[4 * widx + wave] = any ? 1 : 0;
     }
     mfma_drain();
 #pragma unroll
@@ -527,7 +594,28 @@ AttnPlan attention_plan(int S, int H) {
     pl.t_full = split > 1 ? pl.tiles - r : pl.tiles;
     pl.workgroups = pl.t_full + (pl.tiles - pl.t_full) * split;
     pl.part_floats = split > 1 ? (int64_t)(pl.tiles - pl.t_full) * split * AT_BQ * (AT_D + 2) : 0;
+    pl.vtr = S <= kAttnVtrMaxS;
     return pl;
+}
+
+template <bool VTR>
+static hipError_t launch_attention_as(const AttnPlan& pl, const AttnArgs& a, hipStream_t st) {
+    hipError_t e;
+    const int npieces = (pl.tiles - pl.t_full) * pl.split;
+    hipLaunchKernelGGL((attn_fwd_kernel<false, kWhole, VTR>), dim3(pl.t_full), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (npieces > 0) {
+        hipLaunchKernelGGL((attn_fwd_kernel<false, kPieces, VTR>), dim3(npieces), dim3(256), 0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((attn_fwd_kernel<true, kWhole, VTR>), dim3(pl.t_full), dim3(256), 0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((attn_fwd_kernel<true, kPieces, VTR>), dim3(npieces), dim3(256), 0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_combine_kernel, dim3((pl.tiles - pl.t_full) * (AT_BQ / 4)), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((attn_fwd_kernel<true, kWhole, VTR>), dim3(pl.t_full), dim3(256), 0, st, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int S, int H, int64_t ld,
@@ -535,14 +623,16 @@ hipError_t launch_attention(const uint16_t* Q, const uint16_t* K, const uint16_t
     const int Spad = (S + AT_BK - 1) / AT_BK * AT_BK;
     const int tiles_q = (S + AT_BQ - 1) / AT_BQ;
     const AttnPlan pl = attention_plan(S, H);
-    hipLaunchKernelGGL(attn_vt_kernel, dim3((Spad + 63) / 64, H), dim3(256), 0, st, V, ld, S, Spad, Vt, redo,
-                       pl.workgroups);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (!pl.vtr) {
+        hipLaunchKernelGGL(attn_vt_kernel, dim3((Spad + 63) / 64, H), dim3(256), 0, st, V, ld, S, Spad, Vt);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     AttnArgs a;
     a.Q = Q;
     a.K = K;
     a.Vt = Vt;
+    a.V = V;
     a.O = O;
     a.ld = ld;
     a.ldo = ldo;
@@ -554,21 +644,7 @@ hipError_t launch_attention(const uint16_t* Q, const uint16_t* K, const uint16_t
     a.part = part;
     a.t_full = pl.t_full;
     a.split = pl.split;
-    const int npieces = (pl.tiles - pl.t_full) * pl.split;
-    hipLaunchKernelGGL((attn_fwd_kernel<false, kWhole>), dim3(pl.t_full), dim3(256), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (npieces > 0) {
-        hipLaunchKernelGGL((attn_fwd_kernel<false, kPieces>), dim3(npieces), dim3(256), 0, st, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((attn_fwd_kernel<true, kWhole>), dim3(pl.t_full), dim3(256), 0, st, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((attn_fwd_kernel<true, kPieces>), dim3(npieces), dim3(256), 0, st, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(attn_combine_kernel, dim3((pl.tiles - pl.t_full) * (AT_BQ / 4)), dim3(256), 0, st, a);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((attn_fwd_kernel<true, kWhole>), dim3(pl.t_full), dim3(256), 0, st, a);
-    return hipGetLastError();
+    return pl.vtr ? launch_attention_as<true>(pl, a, st) : launch_attention_as<false>(pl, a, st);
 }
 
 }  // namespace qdt

@@ -79,16 +79,20 @@ hipError_t launch_wo_gemm(const uint16_t* X, int64_t ldx, const uint8_t* Wq, con
                           const Plan& pl, hipStream_t st);
 // Work layout of the attention: `tiles` (query block, head) tiles; the first t_full go to one
 // workgroup each over all keys, each later one to `split` workgroups over key ranges (split 1 when
-// there are none); `workgroups` in all; `part_floats` fp32 values of piece outputs.
+// there are none); `workgroups` in all; `part_floats` fp32 values of piece outputs; `vtr`: the PV
+// product reads V transposed from LDS (S <= kAttnVtrMaxS), otherwise a V^T pass runs first.
+constexpr int kAttnVtrMaxS = 8192;
 struct AttnPlan {
     int tiles, t_full, split, workgroups;
     int64_t part_floats;
+    bool vtr;
 };
 AttnPlan attention_plan(int S, int H);
-// Softmax attention per 256-wide head: V^T (keys permuted within 32-key groups, zero-padded to a
-// multiple of 32 keys) into Vt, then O = softmax(Q K^T / 16) V for every head.
-// redo: one int per workgroup (cleared here) for the exact-max rerun; part: the pieces' partial
-// outputs (plan.part_floats floats, unused when the plan splits nothing).
+// Softmax attention per 256-wide head: O = softmax(Q K^T / 16) V for every head; past
+// kAttnVtrMaxS tokens V^T (keys permuted within 32-key groups, zero-padded to a multiple of 32
+// keys) is written to Vt first (Vt unused otherwise).  redo: 4 ints per workgroup (one per wave,
+// written on every call) for the exact-max rerun; part: the pieces' partial outputs
+// (plan.part_floats floats, unused when the plan splits nothing).
 hipError_t launch_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int S, int H, int64_t ld,
                             uint16_t* O, int64_t ldo, uint16_t* Vt, int* redo, float* part, hipStream_t st);
 // Sum of the S int32 partial slices followed by epilogue `epi` (BIAS, SILU, RMSNORM, ACC).

@@ -172,16 +172,20 @@ def test_weight_only_validation():
 
 def test_attention_validation():
     f = qdt.qdt_attention
+    # up to 8192 tokens V is read transposed in LDS (no V^T region): 16 bytes of rerun flags per
+    # workgroup (one int per wave), plus the pieces' fp32 outputs when the last round is split
     n = qdt.attention_workspace_size(100, 2)
-    assert n == 2 * 256 * 128 * 2 + 16 and qdt.attention_workspace_size(256, 1) == 256 * 512 + 16
+    assert n == 2 * 16 and qdt.attention_workspace_size(256, 1) == 16
     # 4608 tokens x 18 heads: 324 (query block, head) tiles, 68 past one round of 256, each split
     # into 3 key ranges: 460 workgroups' rerun flags and 204 pieces' fp32 outputs
-    vt = 18 * 256 * 4608 * 2
-    assert qdt.attention_workspace_size(4608, 18) == vt + (460 + 3) // 4 * 16 + 204 * 256 * 258 * 4
+    assert qdt.attention_workspace_size(4608, 18) == 460 * 16 + 204 * 256 * 258 * 4
+    # 8192 tokens still reads V transposed; 8193 writes V^T first (keys padded to 8224)
+    assert qdt.attention_workspace_size(8192, 1) == 32 * 16
+    assert qdt.attention_workspace_size(8193, 1) == 256 * 8224 * 2 + 33 * 16
     # 16896 x 18: 1188 tiles, 164 past four rounds, more than half a round: no split
-    assert qdt.attention_workspace_size(16896, 18) == 18 * 256 * 16896 * 2 + (1188 + 3) // 4 * 16
+    assert qdt.attention_workspace_size(16896, 18) == 18 * 256 * 16896 * 2 + 1188 * 16
     # 2048 x 40: 320 tiles, 64 past one round, 4 key ranges each
-    assert qdt.attention_workspace_size(2048, 40) == 40 * 256 * 2048 * 2 + 512 // 4 * 16 + 256 * 256 * 258 * 4
+    assert qdt.attention_workspace_size(2048, 40) == 512 * 16 + 256 * 256 * 258 * 4
 
     def att(S=100, H=2, ld=512, ldo=512, O=0x900000, ws=0x2000000, wsb=None, q=0x100000):
         return f(A(q), A(0x300000), A(0x500000), S, H, ld, A(O), ldo, A(ws), n if wsb is None else wsb, None)

@@ -77,10 +77,11 @@ def within_bound(O, Q, K, V, h, rows):
     return float(np.mean(O[rows][:, c] == O_ref))
 
 
-@pytest.mark.parametrize("S,H", [(64, 1), (128, 2), (4096, 1)])
+@pytest.mark.parametrize("S,H", [(64, 1), (128, 2), (4096, 1), (16384, 1)])
 def test_attention_uniform_scores_exact(S, H):
     """Zero queries: every probability is exactly 1, the output is the mean of V (exact in fp32 for
-    power-of-two key counts), bit for bit."""
+    power-of-two key counts), bit for bit.  Up to 8192 tokens the kernel reads V transposed in LDS,
+    past it from a V^T written first (16384): both paths."""
     announce(f"attention uniform S={S} H={H}")
     rng = np.random.default_rng(900 + S)
     Q = np.zeros((S, 256 * H), np.uint16)
@@ -118,6 +119,25 @@ def test_attention_dominant_key_exact(gap, key, exact):
         assert np.array_equal(O, want)
     else:
         assert ulp_bf16(O, want).max() <= 1
+
+
+@pytest.mark.parametrize("S", [8192, 8200])
+def test_attention_dominant_key_rerun_exact_at_the_path_boundary(S):
+    """The exact-max rerun on both sides of the 8192-token switch between V read transposed in LDS
+    and the V^T pass: key S - 3 (in the partial last key tile of 8200) scores 4000 above the rest,
+    past the 64 log2-unit limit, so every workgroup is recomputed with the exact max and its output
+    is that key's V row bit for bit."""
+    announce(f"attention dominant key rerun S={S}")
+    rng = np.random.default_rng(920 + S)
+    key = S - 3
+    Q = np.zeros((S, 256), np.float32)
+    K = np.zeros((S, 256), np.float32)
+    Q[:, 0] = 1.0
+    K[:, 0] = rng.integers(-4, 5, S)
+    K[key, 0] = 4000.0
+    V = bf(rng.standard_normal((S, 256)))
+    O = run(bf(Q), bf(K), V, 1)
+    assert np.array_equal(O, np.broadcast_to(V[key], O.shape))
 
 
 @pytest.mark.parametrize("S,H,pad", [(300, 2, 24), (1, 1, 0), (33, 3, 8)])

@@ -144,6 +144,8 @@ qdt_status qdt_smooth_prepare(const uint16_t* W, const float* s, int64_t N, int6
  *   with a correctly rounded fp32 division and round-half-to-even; an all-zero row gets
  *   x_scale 0 and Xq 0.
  *   X: bf16 [M, ldx] (first K columns).  Xq: int8 [M, K].  x_scale: fp32 [M].
+ *   K % 64 == 0 and K <= QDT_MAX_K; ldx >= K, ldx % 8 == 0; pointers 16-byte aligned; no
+ *   output may overlap an input or the other output.
  *   Bit-exact.  M = 0 is a no-op.
  */
 qdt_status qdt_quantize_per_token(const uint16_t* X, const float* inv_lambda, int64_t M, int64_t K,

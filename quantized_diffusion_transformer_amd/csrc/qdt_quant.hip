@@ -213,6 +213,13 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : WPR * 64) void quant_rows_kernel(
                 amax = fmaxf(amax, fabsf(vc[e]));
                 if constexpr (KEEP) v[c][e] = vc[e];
             }
+            // without these empty asm statements the compiler keeps every chunk's values live
+            // into the second pass (295 VGPRs at C = 16, 315 spills with 16 waves per row)
+            if constexpr (!KEEP) asm volatile("" : "+v"(amax));
+        }
+        if constexpr (!KEEP) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) asm volatile("" : "+v"(raw[c].x), "+v"(raw[c].y), "+v"(raw[c].z), "+v"(raw[c].w));
         }
         amax = wave_max(amax);
         if (WPR > 1) {

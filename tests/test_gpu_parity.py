@@ -51,9 +51,15 @@ def assert_stages_exact(ref, dev):
 # ------------------------------------------------------------------------------ quantize
 @pytest.mark.parametrize("M,K,kind,zero_after", [
     (64, 256, "four20", None),
-    (600, 4608, "pct1", 590),       # one wave per row, ragged row count, 10 zero rows
+    (9, 1984, "pct1", None),        # one wave per row: 4, 6, 9, 12 and 16 chunks per lane
+    (7, 2560, "four20", None),
+    (600, 4608, "pct1", 590),       # ragged row count, 10 zero rows
+    (13, 6080, "pareto", 11),
+    (21, 8128, "pct1", None),       # 16 chunks per lane, the last lanes' last chunk absent
     (37, 12288, "pct1", None),      # 4 waves per row
-    (19, 53248, "pareto", 17),      # 16 waves per row (deep K)
+    (19, 53248, "pareto", 17),      # 16 waves per row (deep K), 7 chunks per lane
+    (3, 57344, "pct1", None),       # the largest K with 7 chunks per lane
+    (3, 57408, "pareto", None),     # the smallest with 16
     (3, 131072, "pct1", None),      # largest K
     (5, 64, "none", None),
 ])

@@ -57,6 +57,8 @@ def assert_stages_exact(ref, dev):
     (13, 6080, "pareto", 11),
     (21, 8128, "pct1", None),       # 16 chunks per lane, the last lanes' last chunk absent
     (37, 12288, "pct1", None),      # 4 waves per row
+    (1600, 12288, "pct1", 1500),    # 4 waves per row, blocks taking several rows (next row prefetched), zero rows
+    (1000, 8256, "pareto", None),   # the same, ragged chunks
     (19, 53248, "pareto", 17),      # 16 waves per row (deep K), 7 chunks per lane
     (3, 57344, "pct1", None),       # the largest K with 7 chunks per lane
     (3, 57408, "pareto", None),     # the smallest with 16

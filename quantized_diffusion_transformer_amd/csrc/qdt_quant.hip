@@ -133,6 +133,15 @@ __device__ __forceinline__ uint4 load_once16(const uint16_t* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Chunk j of a row (8 elements), zero past the row's end (j >= nch).  The load is issued for every
+// lane (lanes past the end re-read the row's last chunk) and the zero is a select: with the load
+// under a branch, the compiler copied each loaded value inside its branch and so waited for every
+// load before issuing the next, serializing a row's C loads.
+__device__ __forceinline__ uint4 load_row_chunk(const uint16_t* row, int64_t j, int64_t nch) {
+    const uint4 v = load_once16(row + min(j, nch - 1) * 8);
+    return j < nch ? v : make_uint4(0u, 0u, 0u, 0u);
+}
+
 // bytes 0 of a, b, c, d -> one dword (a in byte 0)
 __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
@@ -180,13 +189,26 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : WPR * 64) void quant_rows_kernel(
     // overlap it (4608 x 12288: 38.2 -> 35.9 us).  With 16 waves per row the extra registers spill
     // at the 128-register cap, and the 512 x 53248 step measured no faster.
     constexpr bool PF = WPR == 4 && C <= 12;
+    // Loads of chunks past the row's end: under a branch (zero without a load) or clamped into the
+    // row (load_row_chunk).  With 16 chunks per lane the branch form made the compiler serialize the
+    // row's loads (a copy of each loaded value inside its branch waits for it): clamped, 4608 x 8192
+    // measured 34.3 -> 26.7 us with identical outputs.  Elsewhere the branch form keeps the loads back
+    // to back with fewer registers (9 chunks: 107 against 123 VGPRs), or measured faster anyway (four
+    // waves per row, which serializes 4 of its loads: 36.0 against 38.7 us at 4608 x 12288).
+    constexpr bool CLAMP = WPR == 1 && C == 16;
+    auto chunk_load = [&](const uint16_t* rowp, int64_t j) __attribute__((always_inline)) {
+        if constexpr (CLAMP)
+            return load_row_chunk(rowp, j, nch);
+        else
+            return j < nch ? load_once16(rowp + j * 8) : make_uint4(0u, 0u, 0u, 0u);
+    };
     uint4 nxt[PF ? C : 1];
     if constexpr (PF) {
         if (row0 < M) {
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 const int64_t j = t + (int64_t)c * NT;
-                nxt[c] = j < nch ? load_once16(X + row0 * ldx + j * 8) : make_uint4(0u, 0u, 0u, 0u);
+                nxt[c] = chunk_load(X + row0 * ldx, j);
             }
         }
     }
@@ -201,7 +223,7 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : WPR * 64) void quant_rows_kernel(
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 const int64_t j = t + (int64_t)c * NT;
-                raw[c] = j < nch ? load_once16(x + j * 8) : make_uint4(0u, 0u, 0u, 0u);
+                raw[c] = chunk_load(x, j);
             }
         }
         // v = bf16 element * multiplier; chunk c, computed again in the second pass when the
@@ -257,7 +279,7 @@ __global__ __launch_bounds__(WPR == 1 ? 256 : WPR * 64) void quant_rows_kernel(
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
                     const int64_t j = t + (int64_t)c * NT;
-                    nxt[c] = j < nch ? load_once16(X + rn * ldx + j * 8) : make_uint4(0u, 0u, 0u, 0u);
+                    nxt[c] = chunk_load(X + rn * ldx, j);
                 }
             }
         }
@@ -427,23 +449,28 @@ __global__ __launch_bounds__(adaln_waves(C) * 64) void adaln_quant_kernel(
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const int64_t j = lane + (int64_t)c * 64;
-            raw[c] = j < nch ? load_once16(x + j * 8) : make_uint4(0u, 0u, 0u, 0u);
+            // every chunk is loaded (lanes past the row re-read its last chunk, skipped below), so
+            // the row's loads go out back to back: under a branch, or with the zero as a select
+            // right after each load, the compiler waited for each load before issuing the next
+            raw[c] = load_once16(x + min(j, nch - 1) * 8);
         }
         // element e of chunk c (bf16 pairs, low half first)
         auto elem = [&](int c, int e) __attribute__((always_inline)) {
             const uint32_t ww[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
             return (e & 1) ? __uint_as_float(ww[e >> 1] & 0xFFFF0000u) : bf16_to_f32(ww[e >> 1] & 0xFFFFu);
         };
-        // statistics; padding chunks hold zeros and add nothing
+        // statistics over the row's chunks
         double s1 = 0.0, s2 = 0.0;
 #pragma unroll
-        for (int c = 0; c < C; ++c)
+        for (int c = 0; c < C; ++c) {
+            if (lane + (int64_t)c * 64 >= nch) continue;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const double v = (double)elem(c, e);
                 s1 += v;
                 s2 = __builtin_fma(v, v, s2);
             }
+        }
         s1 = wave_sum64(s1);
         s2 = wave_sum64(s2);
         const double mean64 = s1 / (double)K;

@@ -62,7 +62,10 @@ def run_and_check(d, use_shift=True, use_scale=True, use_inv=True, eps=1e-6, ldx
     return Hg, Xqg, sxg, inv
 
 
-@pytest.mark.parametrize("M,K", [(1, 64), (37, 256), (129, 512), (67, 4608), (40, 8192), (300, 1088)])
+# (the last four: rows whose last chunks cover only some lanes, with 6, 9, 12 and 16 chunks per lane;
+# such lanes load the row's last chunk again and skip it)
+@pytest.mark.parametrize("M,K", [(1, 64), (37, 256), (129, 512), (67, 4608), (40, 8192), (300, 1088),
+                                 (61, 3008), (50, 4160), (33, 5696), (45, 7744)])
 def test_adaln_quantize_parity(M, K):
     announce(f"adaln_quantize M={M} K={K}")
     run_and_check(W.make_adaln(M, K, seed=3000 + K))
@@ -80,6 +83,8 @@ def test_adaln_row_stride_and_eps():
     d = W.make_adaln(33, 2048, seed=3200)
     d["X"][5] = W.f32_to_bf16_bits(W.bf16_bits_to_f32(d["X"][5]) * np.float32(1e-2))  # variance ~ eps
     run_and_check(d, ldx=2048 + 72, eps=1e-2)
+    # a row whose last chunk covers only some lanes, in a wider buffer
+    run_and_check(W.make_adaln(29, 4160, seed=3201), ldx=4160 + 200)
 
 
 def test_adaln_constant_and_zero_rows_give_shift():

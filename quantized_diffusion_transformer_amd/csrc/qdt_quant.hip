@@ -390,7 +390,10 @@ hipError_t launch_quant_rows(const uint16_t* X, int64_t ldx, const float* colmul
 // unit (16 waves, 4 per SIMD; 8 waves where the row needs more registers), each block a
 // contiguous run of floor or ceil(M / blocks) rows, taken by its waves in turn.  At 4608 rows
 // that is 18 rows per block and at most 5 per SIMD (a grid-stride launch of 8-wave blocks left
-// 6 on some SIMDs).
+// 6 on some SIMDs).  Every wave issues its first row's loads at once: a stagger of the one-row
+// waves' first loads (so that the two-row waves' rows arrive first) helped while each wave's loads
+// ran one after another, and measured slower once they went out back to back (4608 rows 21.5 ->
+// 20.8 us without it).
 constexpr int adaln_waves(int C) { return C <= 9 ? 16 : 8; }
 
 template <int C, bool QUANT>
@@ -433,16 +436,6 @@ __global__ __launch_bounds__(adaln_waves(C) * 64) void adaln_quant_kernel(
     constexpr int W = adaln_waves(C);
     const int64_t rb0 = (int64_t)blockIdx.x * rq + min((int64_t)blockIdx.x, rr);
     const int64_t rb1 = rb0 + rq + ((int64_t)blockIdx.x < rr ? 1 : 0);
-    // When only a few waves own a second row (W < rq <= W + W / 4, e.g. 18 rows per 16 waves), the
-    // block's time is those waves' two rows in sequence, and every other wave has a row of slack.
-    // Their first loads then go out one group of four waves (one per SIMD) at a time, about one
-    // group's loads at full bandwidth apart (64 x 64 cycles), so the memory system serves the
-    // critical waves first.  Measured at 4608 rows: 25.0 -> 23.5 us; slower where every wave owns
-    // the same number of rows or most own two.
-    if (rq > W && rq <= W + W / 4) {
-        const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >> 2;
-        for (int i = 0; i < grp; ++i) __builtin_amdgcn_s_sleep(64);
-    }
     for (int64_t row = rb0 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); row < rb1; row += W) {
         const uint16_t* x = X + row * ldx;
         uint4 raw[C];
